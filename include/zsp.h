@@ -1,0 +1,202 @@
+/*
+ * zsp.h -- C ABI of libzsp, the per-rank hot path of ZeRO-3 intra-layer
+ * partitioning on one MI355X (gfx950): N_d data-parallel ranks live as
+ * "virtual ranks" in one GPU's memory and every exchange between them is a
+ * local HIP kernel.
+ *
+ * Pages the operations follow (cited by title and section):
+ *   [ZD]  "The ZeRO-3 Diagram Most People Remember Is Wrong"
+ *         section 2 (flatten, pad, contiguous slice per rank) and section 3
+ *         (AllGather before compute, ReduceScatter of gradients, optimizer
+ *         updates the local shard)
+ *   [ZS3] "ZeRO Stage 3: Parameter Partitioning" (on-demand fetch steps,
+ *         equation M_Stage3 and its 7B / 64-GPU example)
+ *   [ZST] "ZeRO Stages: Sharding Optimizer State, Gradients, and Parameters"
+ *         ("What stage 1 partitions": rank i owns [i*N/P, (i+1)*N/P);
+ *          "Stage 2 also partitions gradients": reduce-scatter, shard-sized
+ *          gradient buffer, reduce per micro-batch and accumulate)
+ * The Adam update is the textbook one (Kingma & Ba, Algorithm 1), which the
+ * pages name without printing.
+ *
+ * Terms
+ *   nd            number of data-parallel ranks (N_d), 1..ZSP_MAX_RANKS
+ *   numel[t]      element count of parameter t, flattened row-major
+ *   pad[t]        (nd - numel[t] % nd) % nd
+ *   shard_len[t]  (numel[t] + pad[t]) / nd   -- s_t
+ *   S             sum of shard_len over all parameters: elements one rank owns
+ *   full_off[t]   sum_{u<t} (numel[u] + pad[u])   (full padded layout)
+ *   shard_off[t]  sum_{u<t} shard_len[u]          (a rank's shard layout)
+ *   flat_off[t]   sum_{u<t} numel[u]              (unpadded concatenation)
+ *   Rank r owns elements [r*s_t, (r+1)*s_t) of padded parameter t and stores
+ *   them at shard_off[t] of its shard; positions >= numel[t] are pad.
+ *
+ * Memory and ownership
+ *   The caller allocates and owns every device buffer (parameters, gradients,
+ *   optimizer state, accumulator, gather outputs). A plan owns only its host
+ *   tables and the device copies of its offset tables, which it allocates in
+ *   zsp_bind_state and frees in zsp_destroy. No call after zsp_bind_state
+ *   allocates memory.
+ *   Every device pointer must be 16-byte aligned (torch allocations are).
+ *   State arrays bound for all ranks hold nd*S elements, rank r at
+ *   [r*S, (r+1)*S); bound for one rank j they hold that rank's S elements.
+ *
+ * Streams
+ *   Every call that touches the device enqueues its kernels on `stream` (a
+ *   hipStream_t; NULL is the default stream) and returns without waiting.
+ *   The caller keeps buffers alive until the stream has run them. The plan is
+ *   tied to the device that was current at zsp_bind_state; calls made with
+ *   another device current fail with ZSP_ESTATE.
+ *
+ * Errors
+ *   Arguments are checked before anything is enqueued; a bad argument returns
+ *   a negative zsp_status and enqueues nothing. A failed kernel launch returns
+ *   ZSP_EHIP. zsp_last_error() gives a message for the calling thread's most
+ *   recent failure. Values are not checked: NaN and Inf propagate.
+ *
+ * Threads
+ *   Calls on one plan must not overlap in time (they share its binding).
+ *   Different plans are independent.
+ */
+#ifndef ZSP_H
+#define ZSP_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct zsp_plan zsp_plan;
+
+typedef enum {
+    ZSP_OK = 0,
+    ZSP_EINVAL = -1, /* bad argument: null/misaligned pointer, bad rank, dtype, ... */
+    ZSP_ERANGE = -2, /* index or size out of the supported range */
+    ZSP_ENOMEM = -3, /* host or device allocation for the plan's tables failed */
+    ZSP_EHIP = -4,   /* a HIP runtime call or kernel launch failed */
+    ZSP_ESTATE = -5  /* call not valid in the plan's current binding/device */
+} zsp_status;
+
+typedef enum { ZSP_F32 = 0, ZSP_BF16 = 1 } zsp_dtype;
+
+typedef enum {
+    ZSP_GRADS_FULL = 0,  /* grads[r]: rank r's full padded gradient, tensor t at full_off[t] */
+    ZSP_GRADS_SHARD = 1  /* grads[r]: indexed like the bound state arrays (see below) */
+} zsp_grad_layout;
+
+typedef enum { ZSP_SRC_WORK = 0, ZSP_SRC_MASTER = 1 } zsp_source;
+
+#define ZSP_ALL_RANKS (-1)
+#define ZSP_MAX_RANKS 256
+
+/* partition(param list, N_d) -- [ZD] section 2; [ZST] "What stage 1
+ * partitions". Builds the per-parameter layout tables for n_params
+ * parameters of numel[0..n_params) elements split over n_d ranks. Host only:
+ * touches no device. n_params >= 1, numel[t] >= 0, 1 <= n_d <= ZSP_MAX_RANKS.
+ * On success *out receives a new plan (free with zsp_destroy). */
+zsp_status zsp_partition(const int64_t* numel, int32_t n_params, int32_t n_d,
+                         zsp_plan** out);
+
+/* Release the plan, its host tables and its device tables. NULL is ignored.
+ * The caller must make sure no enqueued work still reads the tables. */
+void zsp_destroy(zsp_plan* plan);
+
+/* Sizes of the plan. Any output pointer may be NULL.
+ *   shard_elems  S
+ *   total_padded sum of numel+pad (elements of one full-layout gradient)
+ *   total_numel  sum of numel
+ *   model_state_bytes_per_rank  16*S: 16-bit param + 16-bit grad + fp32
+ *     master + fp32 m + fp32 v per owned element ([ZS3] equation M_Stage3). */
+zsp_status zsp_plan_info(const zsp_plan* plan, int64_t* shard_elems, int64_t* total_padded,
+                         int64_t* total_numel, int64_t* model_state_bytes_per_rank);
+
+/* Layout of parameter t (0 <= t < n_params). Any output pointer may be NULL. */
+zsp_status zsp_plan_tensor(const zsp_plan* plan, int32_t t, int64_t* numel, int64_t* pad,
+                           int64_t* shard_len, int64_t* full_off, int64_t* shard_off,
+                           int64_t* flat_off);
+
+/* Bind the caller-owned optimizer state and build the device tables.
+ *   rank_or_all = ZSP_ALL_RANKS: every array holds n_d*S elements (all ranks
+ *     resident on this GPU); every rank-taking call may name any rank or all.
+ *   rank_or_all = j: every array holds rank j's S elements only; calls must
+ *     name rank j, and gathers are not possible (ZSP_ESTATE).
+ *   master, m, v: fp32; work: bf16 bit patterns; grad_acc: fp32 accumulator
+ *     or NULL (then accumulate/use_acc calls fail with ZSP_ESTATE).
+ * Allocates the device tables (setup path; the only device allocation the
+ * library makes). Rebinding replaces the previous binding. */
+zsp_status zsp_bind_state(zsp_plan* plan, int32_t rank_or_all, float* master, float* m,
+                          float* v, uint16_t* work, float* grad_acc);
+
+/* Copy-in ([ZD] section 2, steps 1-4): split the unpadded parameters into the
+ * bound ranks' shards. flat_params holds total_numel elements of `dtype`,
+ * parameter t at flat_off[t]. Writes master = fp32(x), work = x (bf16 input)
+ * or its round-to-nearest-even bf16 (fp32 input), m = v = 0, and +0 at every
+ * pad position of all four arrays. */
+zsp_status zsp_load_params(zsp_plan* plan, const void* flat_params, zsp_dtype dtype,
+                           void* stream);
+
+/* reduce_shard(rank, grads[N_d]) -- ReduceScatter restricted to the owned
+ * slice ([ZD] section 3; [ZST] "Stage 2 also partitions gradients").
+ * For each owned non-pad element: red = sum over r = 0..n_d-1, in rank
+ * order, of fp32(grads[r][...]), one fp32 addition at a time starting from
+ * rank 0's value. Writes grad_acc = red (accumulate = 0) or
+ * grad_acc = grad_acc + red (accumulate = 1); pad positions of grad_acc are
+ * set to +0. grads: n_d device pointers (host array) of `dtype`.
+ *   ZSP_GRADS_FULL : grads[r] holds total_padded elements; the element of
+ *                    parameter t at padded index k is at full_off[t] + k.
+ *   ZSP_GRADS_SHARD: grads[r] is the chunk rank r sends to the owners, in the
+ *                    bound arrays' indexing: S elements for a one-rank
+ *                    binding, n_d*S (owner j at j*S) for an all-rank one.
+ * Pad positions of grads are never read. rank_or_all: a rank or
+ * ZSP_ALL_RANKS (all-rank binding only). */
+zsp_status zsp_reduce_shard(zsp_plan* plan, int32_t rank_or_all, const void* const* grads,
+                            zsp_dtype dtype, zsp_grad_layout layout, int32_t accumulate,
+                            void* stream);
+
+/* adam_step(shard, lr, beta1, beta2, eps, step) -- the optimizer updates the
+ * local shard ([ZD] section 3; [ZS3] on-demand fetch, last step; [ZST]).
+ * Uses grad_acc as the gradient. For each owned non-pad element, in fp32 with
+ * one rounding per operation, in this order:
+ *   m = beta1*m + (1-beta1)*g ;  v = beta2*v + (1-beta2)*(g*g)
+ *   mh = m/(1-beta1^step) ;  vh = v/(1-beta2^step)
+ *   master = master - (lr*mh)/(sqrt(vh) + eps) ;  work = bf16_rne(master)
+ * 1-beta is computed in fp32; 1-beta^step in double and rounded once to
+ * fp32. Pad positions are not touched. step >= 1. */
+zsp_status zsp_adam_step(zsp_plan* plan, int32_t rank_or_all, float lr, float beta1,
+                         float beta2, float eps, int64_t step, void* stream);
+
+/* The hot path: reduce_shard and adam_step fused in one pass. g = red
+ * (use_acc = 0) or g = grad_acc + red (use_acc = 1, the last micro-batch of
+ * an accumulation window); the reduced gradient stays in registers and
+ * grad_acc is not written. Same arithmetic, bit for bit, as reduce_shard
+ * followed by adam_step. */
+zsp_status zsp_reduce_adam_step(zsp_plan* plan, int32_t rank_or_all,
+                                const void* const* grads, zsp_dtype dtype,
+                                zsp_grad_layout layout, int32_t use_acc, float lr,
+                                float beta1, float beta2, float eps, int64_t step,
+                                void* stream);
+
+/* gather(param_id) -- AllGather of a full parameter just before compute
+ * ([ZD] section 3; [ZS3] on-demand fetch, step 2; [ZST] "Stage 3
+ * partitions parameters"). Writes numel[param_id] elements to `out`, pad
+ * dropped: out[k] = src_r[shard_off[t] + k - r*s_t] with r = k / s_t.
+ * src = ZSP_SRC_WORK (bf16 out) or ZSP_SRC_MASTER (fp32 out). Needs an
+ * all-rank binding. */
+zsp_status zsp_gather(zsp_plan* plan, int32_t param_id, zsp_source src, void* out,
+                      void* stream);
+
+/* Batched gather of the consecutive parameters [first_param,
+ * first_param + n_params) in one launch, e.g. every parameter of one layer.
+ * `out` receives them back to back, unpadded: parameter t at
+ * flat_off[t] - flat_off[first_param]. */
+zsp_status zsp_gather_many(zsp_plan* plan, int32_t first_param, int32_t n_params,
+                           zsp_source src, void* out, void* stream);
+
+/* Message for the calling thread's most recent failed call ("" if none). */
+const char* zsp_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ZSP_H */

@@ -1,0 +1,255 @@
+"""ctypes binding of libzsp (include/zsp.h), one function per C entry point.
+
+Argument marshalling only: torch tensors become raw device pointers, torch's
+current stream becomes the hipStream_t, Python lists become C arrays. Every
+step of the path runs in libzsp's HIP kernels. There is no fallback: if
+libzsp.so is missing, importing this module raises.
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libzsp.so")
+
+OK, EINVAL, ERANGE, ENOMEM, EHIP, ESTATE = 0, -1, -2, -3, -4, -5
+F32, BF16 = 0, 1
+GRADS_FULL, GRADS_SHARD = 0, 1
+SRC_WORK, SRC_MASTER = 0, 1
+ALL_RANKS = -1
+MAX_RANKS = 256
+
+_STATUS_NAMES = {EINVAL: "ZSP_EINVAL", ERANGE: "ZSP_ERANGE", ENOMEM: "ZSP_ENOMEM",
+                 EHIP: "ZSP_EHIP", ESTATE: "ZSP_ESTATE"}
+
+
+class ZspError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"{_STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is not built; run __graft_entry__.build() (hipcc, gfx950) first")
+    L = ctypes.CDLL(LIB_PATH)
+    i32, i64, vp, f32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_float
+    i64p = ctypes.POINTER(ctypes.c_int64)
+    vpp = ctypes.POINTER(ctypes.c_void_p)
+    sigs = {
+        "zsp_partition": (i32, [i64p, i32, i32, ctypes.POINTER(vp)]),
+        "zsp_destroy": (None, [vp]),
+        "zsp_plan_info": (i32, [vp, i64p, i64p, i64p, i64p]),
+        "zsp_plan_tensor": (i32, [vp, i32, i64p, i64p, i64p, i64p, i64p, i64p]),
+        "zsp_bind_state": (i32, [vp, i32, vp, vp, vp, vp, vp]),
+        "zsp_load_params": (i32, [vp, vp, i32, vp]),
+        "zsp_reduce_shard": (i32, [vp, i32, vpp, i32, i32, i32, vp]),
+        "zsp_adam_step": (i32, [vp, i32, f32, f32, f32, f32, i64, vp]),
+        "zsp_reduce_adam_step": (i32, [vp, i32, vpp, i32, i32, i32, f32, f32, f32, f32, i64,
+                                       vp]),
+        "zsp_gather": (i32, [vp, i32, i32, vp, vp]),
+        "zsp_gather_many": (i32, [vp, i32, i32, i32, vp, vp]),
+        "zsp_last_error": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sigs.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+    return L
+
+
+lib = _load()
+
+
+def last_error():
+    return lib.zsp_last_error().decode(errors="replace")
+
+
+def _check(status):
+    if status != OK:
+        raise ZspError(status, last_error())
+
+
+def _stream(stream):
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _ptr(t, dtype, what):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{what} must be a torch tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{what} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    if not t.is_cuda:
+        raise ValueError(f"{what} must be on the GPU")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype_code(t):
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _grad_array(grads, n_d):
+    if len(grads) != n_d:
+        raise ValueError(f"need {n_d} gradient buffers, got {len(grads)}")
+    dt = grads[0].dtype
+    ptrs = [_ptr(g, dt, f"grads[{i}]").value for i, g in enumerate(grads)]
+    return (ctypes.c_void_p * n_d)(*ptrs), _dtype_code(grads[0])
+
+
+_LAYOUTS = {"full": GRADS_FULL, "shard": GRADS_SHARD, GRADS_FULL: GRADS_FULL,
+            GRADS_SHARD: GRADS_SHARD}
+_SOURCES = {"work": SRC_WORK, "master": SRC_MASTER, SRC_WORK: SRC_WORK,
+            SRC_MASTER: SRC_MASTER}
+
+
+# ---- one function per C entry point ---------------------------------------
+
+def zsp_partition(numel, n_d):
+    arr = (ctypes.c_int64 * len(numel))(*[int(n) for n in numel])
+    h = ctypes.c_void_p()
+    _check(lib.zsp_partition(arr, len(numel), int(n_d), ctypes.byref(h)))
+    return h
+
+
+def zsp_destroy(h):
+    lib.zsp_destroy(h)
+
+
+def zsp_plan_info(h):
+    out = [ctypes.c_int64() for _ in range(4)]
+    _check(lib.zsp_plan_info(h, *[ctypes.byref(o) for o in out]))
+    return dict(zip(("shard_elems", "total_padded", "total_numel",
+                     "model_state_bytes_per_rank"), (o.value for o in out)))
+
+
+def zsp_plan_tensor(h, t):
+    out = [ctypes.c_int64() for _ in range(6)]
+    _check(lib.zsp_plan_tensor(h, int(t), *[ctypes.byref(o) for o in out]))
+    return dict(zip(("numel", "pad", "shard_len", "full_off", "shard_off", "flat_off"),
+                    (o.value for o in out)))
+
+
+def zsp_bind_state(h, rank, master, m, v, work, grad_acc=None):
+    _check(lib.zsp_bind_state(
+        h, int(rank), _ptr(master, torch.float32, "master"), _ptr(m, torch.float32, "m"),
+        _ptr(v, torch.float32, "v"), _ptr(work, torch.bfloat16, "work"),
+        _ptr(grad_acc, torch.float32, "grad_acc")))
+
+
+def zsp_load_params(h, flat, stream=None):
+    _check(lib.zsp_load_params(h, _ptr(flat, flat.dtype, "flat_params"), _dtype_code(flat),
+                               _stream(stream)))
+
+
+def zsp_reduce_shard(h, n_d, rank, grads, layout="full", accumulate=False, stream=None):
+    arr, code = _grad_array(grads, n_d)
+    _check(lib.zsp_reduce_shard(h, int(rank), arr, code, _LAYOUTS[layout], int(bool(accumulate)),
+                                _stream(stream)))
+
+
+def zsp_adam_step(h, rank, lr, beta1, beta2, eps, step, stream=None):
+    _check(lib.zsp_adam_step(h, int(rank), float(lr), float(beta1), float(beta2), float(eps),
+                             int(step), _stream(stream)))
+
+
+def zsp_reduce_adam_step(h, n_d, rank, grads, lr, beta1, beta2, eps, step, layout="full",
+                         use_acc=False, stream=None):
+    arr, code = _grad_array(grads, n_d)
+    _check(lib.zsp_reduce_adam_step(h, int(rank), arr, code, _LAYOUTS[layout],
+                                    int(bool(use_acc)), float(lr), float(beta1), float(beta2),
+                                    float(eps), int(step), _stream(stream)))
+
+
+def zsp_gather(h, param_id, out, source="work", stream=None):
+    src = _SOURCES[source]
+    dt = torch.bfloat16 if src == SRC_WORK else torch.float32
+    _check(lib.zsp_gather(h, int(param_id), src, _ptr(out, dt, "out"), _stream(stream)))
+
+
+def zsp_gather_many(h, first, n, out, source="work", stream=None):
+    src = _SOURCES[source]
+    dt = torch.bfloat16 if src == SRC_WORK else torch.float32
+    _check(lib.zsp_gather_many(h, int(first), int(n), src, _ptr(out, dt, "out"),
+                               _stream(stream)))
+
+
+# ---- a plan object over the same calls -------------------------------------
+
+class Plan:
+    """Owns a zsp_plan handle; methods map one-to-one onto the C calls."""
+
+    def __init__(self, numel, n_d):
+        self.numel = [int(n) for n in numel]
+        self.n_d = int(n_d)
+        self._h = zsp_partition(self.numel, self.n_d)
+        info = zsp_plan_info(self._h)
+        self.S = info["shard_elems"]
+        self.total_padded = info["total_padded"]
+        self.total_numel = info["total_numel"]
+        self.model_state_bytes_per_rank = info["model_state_bytes_per_rank"]
+        self._bound = None
+
+    @property
+    def handle(self):
+        return self._h
+
+    def destroy(self):
+        if self._h is not None and self._h.value:
+            zsp_destroy(self._h)
+        self._h = None
+
+    def __del__(self):
+        try:
+            self.destroy()
+        except Exception:
+            pass
+
+    def info(self):
+        return zsp_plan_info(self._h)
+
+    def tensor(self, t):
+        return zsp_plan_tensor(self._h, t)
+
+    def bind_state(self, rank, master, m, v, work, grad_acc=None):
+        zsp_bind_state(self._h, rank, master, m, v, work, grad_acc)
+        # keep the tensors alive for as long as they are bound
+        self._bound = (master, m, v, work, grad_acc)
+
+    def load_params(self, flat, stream=None):
+        zsp_load_params(self._h, flat, stream)
+
+    def reduce_shard(self, rank, grads, layout="full", accumulate=False, stream=None):
+        zsp_reduce_shard(self._h, self.n_d, rank, grads, layout, accumulate, stream)
+
+    def adam_step(self, rank, lr, beta1, beta2, eps, step, stream=None):
+        zsp_adam_step(self._h, rank, lr, beta1, beta2, eps, step, stream)
+
+    def reduce_adam_step(self, rank, grads, lr, beta1, beta2, eps, step, layout="full",
+                         use_acc=False, stream=None):
+        zsp_reduce_adam_step(self._h, self.n_d, rank, grads, lr, beta1, beta2, eps, step,
+                             layout, use_acc, stream)
+
+    def gather(self, param_id, out, source="work", stream=None):
+        zsp_gather(self._h, param_id, out, source, stream)
+
+    def gather_many(self, first, n, out, source="work", stream=None):
+        zsp_gather_many(self._h, first, n, out, source, stream)
+
+
+def partition(numel, n_d):
+    """partition(param list, N_d) -> Plan."""
+    return Plan(numel, n_d)

@@ -1,0 +1,402 @@
+// zsp_capi.cpp -- the extern "C" entry points of libzsp (declared and
+// documented in include/zsp.h): argument checks, plan bookkeeping, device
+// table upload at bind time, and dispatch to the kernels.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+
+#include "zsp_internal.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+zsp_status fail(zsp_status st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+zsp_status fail_hip(hipError_t e, const char* what) {
+    return fail(ZSP_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+zsp_status check_device(const zsp_plan* P) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
+    if (dev != P->device)
+        return fail(ZSP_ESTATE, "plan is bound on device %d but device %d is current", P->device,
+                    dev);
+    return ZSP_OK;
+}
+
+zsp_status check_bound(const zsp_plan* P) {
+    if (!P) return fail(ZSP_EINVAL, "plan is NULL");
+    if (!P->bound) return fail(ZSP_ESTATE, "no state bound (call zsp_bind_state first)");
+    return check_device(P);
+}
+
+// E-space range of a rank-taking call.
+zsp_status rank_range(const zsp_plan* P, int32_t rank, int64_t* b, int64_t* e) {
+    if (P->bind_rank == ZSP_ALL_RANKS) {
+        if (rank == ZSP_ALL_RANKS) {
+            *b = 0;
+            *e = int64_t(P->nd) * P->S;
+            return ZSP_OK;
+        }
+        if (rank < 0 || rank >= P->nd)
+            return fail(ZSP_EINVAL, "rank %d outside [0, %d) and not ZSP_ALL_RANKS", rank, P->nd);
+        *b = int64_t(rank) * P->S;
+        *e = *b + P->S;
+        return ZSP_OK;
+    }
+    if (rank != P->bind_rank)
+        return fail(ZSP_ESTATE, "state is bound for rank %d only, call named rank %d",
+                    P->bind_rank, rank);
+    *b = 0;
+    *e = P->S;
+    return ZSP_OK;
+}
+
+zsp_status check_grads(const zsp_plan* P, const void* const* grads, zsp_dtype dtype,
+                       zsp_grad_layout layout) {
+    if (dtype != ZSP_F32 && dtype != ZSP_BF16) return fail(ZSP_EINVAL, "bad dtype %d", dtype);
+    if (layout != ZSP_GRADS_FULL && layout != ZSP_GRADS_SHARD)
+        return fail(ZSP_EINVAL, "bad gradient layout %d", layout);
+    if (!grads) return fail(ZSP_EINVAL, "grads array is NULL");
+    for (int r = 0; r < P->nd; ++r) {
+        if (!grads[r]) return fail(ZSP_EINVAL, "grads[%d] is NULL", r);
+        if (!aligned16(grads[r])) return fail(ZSP_EINVAL, "grads[%d] is not 16-byte aligned", r);
+    }
+    return ZSP_OK;
+}
+
+zsp_status adam_scalars(float lr, float b1, float b2, float eps, int64_t step,
+                        zsp::AdamScalars* hp) {
+    if (step < 1) return fail(ZSP_EINVAL, "step must be >= 1 (got %lld)", (long long)step);
+    hp->lr = lr;
+    hp->b1 = b1;
+    hp->b2 = b2;
+    hp->eps = eps;
+    hp->omb1 = 1.0f - b1;
+    hp->omb2 = 1.0f - b2;
+    hp->bc1 = static_cast<float>(1.0 - std::pow(static_cast<double>(b1), static_cast<double>(step)));
+    hp->bc2 = static_cast<float>(1.0 - std::pow(static_cast<double>(b2), static_cast<double>(step)));
+    return ZSP_OK;
+}
+
+zsp::ShardLaunch base_launch(const zsp_plan* P) {
+    zsp::ShardLaunch L;
+    L.tab = P->shard;
+    L.master = P->master;
+    L.m = P->m;
+    L.v = P->v;
+    L.work = P->work;
+    L.acc = P->acc;
+    L.nd = P->nd;
+    return L;
+}
+
+void free_tables(zsp_plan* P) {
+    if (P->dev_blob) (void)hipFree(P->dev_blob);
+    P->dev_blob = nullptr;
+    P->shard = zsp::ShardTable{};
+    P->gather = zsp::GatherTable{};
+}
+
+template <typename T>
+size_t bytes_of(const std::vector<T>& v) {
+    return v.size() * sizeof(T);
+}
+
+size_t round_up(size_t x) { return (x + 255) & ~size_t(255); }
+
+}  // namespace
+
+extern "C" {
+
+zsp_status zsp_partition(const int64_t* numel, int32_t n_params, int32_t n_d, zsp_plan** out) {
+    if (!out) return fail(ZSP_EINVAL, "out is NULL");
+    *out = nullptr;
+    if (!numel) return fail(ZSP_EINVAL, "numel is NULL");
+    if (n_params < 1) return fail(ZSP_EINVAL, "n_params must be >= 1 (got %d)", n_params);
+    if (n_d < 1 || n_d > ZSP_MAX_RANKS)
+        return fail(ZSP_EINVAL, "n_d must be in [1, %d] (got %d)", ZSP_MAX_RANKS, n_d);
+    zsp_plan* P = new (std::nothrow) zsp_plan();
+    if (!P) return fail(ZSP_ENOMEM, "out of host memory");
+    try {
+        P->T = n_params;
+        P->nd = n_d;
+        P->numel.assign(numel, numel + n_params);
+        P->pad.resize(n_params);
+        P->shard_len.resize(n_params);
+        P->full_off.assign(n_params + 1, 0);
+        P->shard_off.assign(n_params + 1, 0);
+        P->flat_off.assign(n_params + 1, 0);
+        const int64_t kMax = int64_t(1) << 60;
+        for (int32_t t = 0; t < n_params; ++t) {
+            const int64_t n = numel[t];
+            if (n < 0) {
+                delete P;
+                return fail(ZSP_EINVAL, "numel[%d] = %lld is negative", t, (long long)n);
+            }
+            if (n > kMax || P->full_off[t] > kMax - n - n_d) {
+                delete P;
+                return fail(ZSP_ERANGE, "total size exceeds 2^60 elements at parameter %d", t);
+            }
+            const int64_t pad = zsp::pad_for(n, n_d);
+            P->pad[t] = pad;
+            P->shard_len[t] = (n + pad) / n_d;
+            P->full_off[t + 1] = P->full_off[t] + n + pad;
+            P->shard_off[t + 1] = P->shard_off[t] + P->shard_len[t];
+            P->flat_off[t + 1] = P->flat_off[t] + n;
+        }
+        P->S = P->shard_off[n_params];
+        P->total_padded = P->full_off[n_params];
+        P->total_numel = P->flat_off[n_params];
+    } catch (const std::bad_alloc&) {
+        delete P;
+        return fail(ZSP_ENOMEM, "out of host memory");
+    }
+    *out = P;
+    return ZSP_OK;
+}
+
+void zsp_destroy(zsp_plan* plan) {
+    if (!plan) return;
+    free_tables(plan);
+    delete plan;
+}
+
+zsp_status zsp_plan_info(const zsp_plan* P, int64_t* shard_elems, int64_t* total_padded,
+                         int64_t* total_numel, int64_t* model_state_bytes_per_rank) {
+    if (!P) return fail(ZSP_EINVAL, "plan is NULL");
+    if (shard_elems) *shard_elems = P->S;
+    if (total_padded) *total_padded = P->total_padded;
+    if (total_numel) *total_numel = P->total_numel;
+    // 2 (16-bit param) + 2 (16-bit grad) + 4 (fp32 master) + 4 (m) + 4 (v)
+    if (model_state_bytes_per_rank) *model_state_bytes_per_rank = 16 * P->S;
+    return ZSP_OK;
+}
+
+zsp_status zsp_plan_tensor(const zsp_plan* P, int32_t t, int64_t* numel, int64_t* pad,
+                           int64_t* shard_len, int64_t* full_off, int64_t* shard_off,
+                           int64_t* flat_off) {
+    if (!P) return fail(ZSP_EINVAL, "plan is NULL");
+    if (t < 0 || t >= P->T) return fail(ZSP_ERANGE, "parameter %d outside [0, %d)", t, P->T);
+    if (numel) *numel = P->numel[t];
+    if (pad) *pad = P->pad[t];
+    if (shard_len) *shard_len = P->shard_len[t];
+    if (full_off) *full_off = P->full_off[t];
+    if (shard_off) *shard_off = P->shard_off[t];
+    if (flat_off) *flat_off = P->flat_off[t];
+    return ZSP_OK;
+}
+
+zsp_status zsp_bind_state(zsp_plan* P, int32_t rank_or_all, float* master, float* m, float* v,
+                          uint16_t* work, float* grad_acc) {
+    if (!P) return fail(ZSP_EINVAL, "plan is NULL");
+    if (rank_or_all != ZSP_ALL_RANKS && (rank_or_all < 0 || rank_or_all >= P->nd))
+        return fail(ZSP_EINVAL, "rank %d outside [0, %d) and not ZSP_ALL_RANKS", rank_or_all,
+                    P->nd);
+    const void* ptrs[4] = {master, m, v, work};
+    const char* names[4] = {"master", "m", "v", "work"};
+    for (int i = 0; i < 4; ++i) {
+        if (!ptrs[i] && P->S > 0) return fail(ZSP_EINVAL, "%s is NULL", names[i]);
+        if (!aligned16(ptrs[i])) return fail(ZSP_EINVAL, "%s is not 16-byte aligned", names[i]);
+    }
+    if (grad_acc && !aligned16(grad_acc))
+        return fail(ZSP_EINVAL, "grad_acc is not 16-byte aligned");
+
+    zsp::HostShardTable hs;
+    zsp::HostGatherTable hg;
+    try {
+        zsp::build_shard_table(P->numel, P->shard_len, P->full_off, P->shard_off, P->flat_off,
+                               P->S, P->nd, rank_or_all, hs);
+        if (rank_or_all == ZSP_ALL_RANKS)
+            zsp::build_gather_table(P->numel, P->shard_len, P->shard_off, P->flat_off, P->S,
+                                    P->nd, hg);
+    } catch (const std::bad_alloc&) {
+        return fail(ZSP_ENOMEM, "out of host memory building tables");
+    }
+    if (hs.e0.size() > size_t(0x7fffffff) || hg.k0.size() > size_t(0x7fffffff))
+        return fail(ZSP_ERANGE, "more than 2^31 pieces");
+
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
+
+    // One allocation: [e0 | info | tile | k0 | delta | gtile], 256-byte aligned parts.
+    const size_t sz[6] = {bytes_of(hs.e0), bytes_of(hs.info), bytes_of(hs.tile),
+                          bytes_of(hg.k0), bytes_of(hg.delta), bytes_of(hg.tile)};
+    const void* src[6] = {hs.e0.data(), hs.info.data(), hs.tile.data(),
+                          hg.k0.data(), hg.delta.data(), hg.tile.data()};
+    size_t off[6], total = 0;
+    for (int i = 0; i < 6; ++i) {
+        off[i] = total;
+        total += round_up(sz[i]);
+    }
+    free_tables(P);
+    P->bound = false;
+    void* blob = nullptr;
+    if (total > 0) {
+        e = hipMalloc(&blob, total);
+        if (e != hipSuccess) return fail(ZSP_ENOMEM, "hipMalloc of %zu table bytes: %s", total,
+                                         hipGetErrorString(e));
+        for (int i = 0; i < 6; ++i) {
+            if (!sz[i]) continue;
+            e = hipMemcpy(static_cast<char*>(blob) + off[i], src[i], sz[i],
+                          hipMemcpyHostToDevice);
+            if (e != hipSuccess) {
+                (void)hipFree(blob);
+                return fail_hip(e, "hipMemcpy of offset tables");
+            }
+        }
+    }
+    char* b = static_cast<char*>(blob);
+    P->dev_blob = blob;
+    P->shard.e0 = reinterpret_cast<const int64_t*>(b + off[0]);
+    P->shard.info = reinterpret_cast<const zsp::PieceInfo*>(b + off[1]);
+    P->shard.tile = reinterpret_cast<const int32_t*>(b + off[2]);
+    P->shard.np = int64_t(hs.info.size());
+    P->shard.ntile = hs.tile.empty() ? 0 : int64_t(hs.tile.size()) - 1;
+    P->shard.total = hs.total;
+    if (rank_or_all == ZSP_ALL_RANKS) {
+        P->gather.k0 = reinterpret_cast<const int64_t*>(b + off[3]);
+        P->gather.delta = reinterpret_cast<const int64_t*>(b + off[4]);
+        P->gather.tile = reinterpret_cast<const int32_t*>(b + off[5]);
+        P->gather.nq = int64_t(hg.delta.size());
+        P->gather.ntile = hg.tile.empty() ? 0 : int64_t(hg.tile.size()) - 1;
+        P->gather.total = hg.total;
+    }
+    P->bind_rank = rank_or_all;
+    P->device = dev;
+    P->master = master;
+    P->m = m;
+    P->v = v;
+    P->work = work;
+    P->acc = grad_acc;
+    P->bound = true;
+    return ZSP_OK;
+}
+
+zsp_status zsp_load_params(zsp_plan* P, const void* flat_params, zsp_dtype dtype, void* stream) {
+    zsp_status st = check_bound(P);
+    if (st != ZSP_OK) return st;
+    if (dtype != ZSP_F32 && dtype != ZSP_BF16) return fail(ZSP_EINVAL, "bad dtype %d", dtype);
+    if (!flat_params && P->total_numel > 0) return fail(ZSP_EINVAL, "flat_params is NULL");
+    if (!aligned16(flat_params)) return fail(ZSP_EINVAL, "flat_params is not 16-byte aligned");
+    zsp::ShardLaunch L = base_launch(P);
+    L.e_begin = 0;
+    L.e_end = P->shard.total;
+    L.src = flat_params;
+    hipError_t e = zsp::launch_shard_op(L, zsp::OP_COPYIN, dtype, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail_hip(e, "copy-in launch");
+    return ZSP_OK;
+}
+
+zsp_status zsp_reduce_shard(zsp_plan* P, int32_t rank_or_all, const void* const* grads,
+                            zsp_dtype dtype, zsp_grad_layout layout, int32_t accumulate,
+                            void* stream) {
+    zsp_status st = check_bound(P);
+    if (st != ZSP_OK) return st;
+    if (!P->acc) return fail(ZSP_ESTATE, "reduce_shard needs a bound grad_acc");
+    int64_t b, en;
+    if ((st = rank_range(P, rank_or_all, &b, &en)) != ZSP_OK) return st;
+    if ((st = check_grads(P, grads, dtype, layout)) != ZSP_OK) return st;
+    zsp::ShardLaunch L = base_launch(P);
+    L.e_begin = b;
+    L.e_end = en;
+    L.grads = grads;
+    L.shard_layout = layout == ZSP_GRADS_SHARD;
+    hipError_t e = zsp::launch_shard_op(L, accumulate ? zsp::OP_REDUCE_ACC : zsp::OP_REDUCE_SET,
+                                        dtype, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail_hip(e, "reduce launch");
+    return ZSP_OK;
+}
+
+zsp_status zsp_adam_step(zsp_plan* P, int32_t rank_or_all, float lr, float beta1, float beta2,
+                         float eps, int64_t step, void* stream) {
+    zsp_status st = check_bound(P);
+    if (st != ZSP_OK) return st;
+    if (!P->acc) return fail(ZSP_ESTATE, "adam_step reads grad_acc, which is not bound");
+    int64_t b, en;
+    if ((st = rank_range(P, rank_or_all, &b, &en)) != ZSP_OK) return st;
+    zsp::ShardLaunch L = base_launch(P);
+    if ((st = adam_scalars(lr, beta1, beta2, eps, step, &L.hp)) != ZSP_OK) return st;
+    L.e_begin = b;
+    L.e_end = en;
+    hipError_t e = zsp::launch_shard_op(L, zsp::OP_ADAM, ZSP_F32, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail_hip(e, "adam launch");
+    return ZSP_OK;
+}
+
+zsp_status zsp_reduce_adam_step(zsp_plan* P, int32_t rank_or_all, const void* const* grads,
+                                zsp_dtype dtype, zsp_grad_layout layout, int32_t use_acc,
+                                float lr, float beta1, float beta2, float eps, int64_t step,
+                                void* stream) {
+    zsp_status st = check_bound(P);
+    if (st != ZSP_OK) return st;
+    if (use_acc && !P->acc) return fail(ZSP_ESTATE, "use_acc needs a bound grad_acc");
+    int64_t b, en;
+    if ((st = rank_range(P, rank_or_all, &b, &en)) != ZSP_OK) return st;
+    if ((st = check_grads(P, grads, dtype, layout)) != ZSP_OK) return st;
+    zsp::ShardLaunch L = base_launch(P);
+    if ((st = adam_scalars(lr, beta1, beta2, eps, step, &L.hp)) != ZSP_OK) return st;
+    L.e_begin = b;
+    L.e_end = en;
+    L.grads = grads;
+    L.shard_layout = layout == ZSP_GRADS_SHARD;
+    hipError_t e = zsp::launch_shard_op(L, use_acc ? zsp::OP_FUSED_ACC : zsp::OP_FUSED, dtype,
+                                        static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail_hip(e, "fused reduce+adam launch");
+    return ZSP_OK;
+}
+
+zsp_status zsp_gather_many(zsp_plan* P, int32_t first_param, int32_t n_params, zsp_source src,
+                           void* out, void* stream) {
+    zsp_status st = check_bound(P);
+    if (st != ZSP_OK) return st;
+    if (P->bind_rank != ZSP_ALL_RANKS)
+        return fail(ZSP_ESTATE, "gather needs every rank's shard (state bound for rank %d only)",
+                    P->bind_rank);
+    if (n_params < 1 || first_param < 0 || first_param > P->T - n_params)
+        return fail(ZSP_ERANGE, "parameters [%d, %d+%d) outside [0, %d)", first_param,
+                    first_param, n_params, P->T);
+    if (src != ZSP_SRC_WORK && src != ZSP_SRC_MASTER) return fail(ZSP_EINVAL, "bad source %d", src);
+    const int64_t k_first = P->flat_off[first_param];
+    const int64_t count = P->flat_off[first_param + n_params] - k_first;
+    if (count > 0 && !out) return fail(ZSP_EINVAL, "out is NULL");
+    if (!aligned16(out)) return fail(ZSP_EINVAL, "out is not 16-byte aligned");
+    zsp::GatherLaunch L;
+    L.tab = P->gather;
+    L.k_first = k_first;
+    L.count = count;
+    L.src = src == ZSP_SRC_WORK ? static_cast<const void*>(P->work)
+                                : static_cast<const void*>(P->master);
+    L.out = out;
+    hipError_t e = zsp::launch_gather(L, src == ZSP_SRC_WORK ? ZSP_BF16 : ZSP_F32,
+                                      static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail_hip(e, "gather launch");
+    return ZSP_OK;
+}
+
+zsp_status zsp_gather(zsp_plan* P, int32_t param_id, zsp_source src, void* out, void* stream) {
+    if (P && (param_id < 0 || param_id >= P->T))
+        return fail(ZSP_ERANGE, "parameter %d outside [0, %d)", param_id, P->T);
+    return zsp_gather_many(P, param_id, 1, src, out, stream);
+}
+
+const char* zsp_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,160 @@
+// zsp_internal.hpp -- plan structure, device-table formats and kernel launch
+// interfaces shared by the host side (zsp_layout.cpp, zsp_capi.cpp) and the
+// HIP kernels (zsp_kernels.hip) of libzsp.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+
+#include <cstdint>
+#include <vector>
+
+#include "zsp.h"
+
+namespace zsp {
+
+// Elements one wavefront handles per tile: 64 lanes x 8 contiguous elements.
+// Offset tables are indexed at this granularity.
+constexpr int64_t kTile = 512;
+constexpr int kWaveLanes = 64;
+constexpr int kElemsPerLane = 8;
+constexpr int kBlockThreads = 256;
+constexpr int kWavesPerBlock = kBlockThreads / kWaveLanes;
+
+// One piece of the shard index space ("E-space"): the run of elements of
+// one rank's slice of one parameter. E-space is the index space of the bound
+// state arrays (n_d*S for an all-rank binding, S for a one-rank binding).
+// The piece covers [e0, end); [e0, vend) are real elements, [vend, end) pad.
+// For an element e of the piece, its gradient in the full padded layout is
+// at e + gdelta and its value in the unpadded flat parameter buffer at
+// e + idelta.
+struct PieceInfo {
+    int64_t vend;
+    int64_t end;
+    int64_t gdelta;
+    int64_t idelta;
+};
+
+// Device copy of a piece table: e0[np+1] (e0[np] = total), info[np], and
+// tile[ntile+1] where tile[g] is the piece holding element
+// min(g*kTile, total-1). Pieces are never empty.
+struct ShardTable {
+    const int64_t* e0 = nullptr;
+    const PieceInfo* info = nullptr;
+    const int32_t* tile = nullptr;
+    int64_t np = 0;
+    int64_t ntile = 0;
+    int64_t total = 0;
+};
+
+// Device copy of the gather table over the unpadded flat index space
+// ("K-space", parameter t at flat_off[t]): piece q is the run of parameter t
+// held by one rank, starting at k0[q] (k0[nq] = total); element K of it
+// reads source element K + delta[q] of the n_d*S shard arrays. tile[] as
+// above.
+struct GatherTable {
+    const int64_t* k0 = nullptr;
+    const int64_t* delta = nullptr;
+    const int32_t* tile = nullptr;
+    int64_t nq = 0;
+    int64_t ntile = 0;
+    int64_t total = 0;
+};
+
+// Host-side tables before upload.
+struct HostShardTable {
+    std::vector<int64_t> e0;
+    std::vector<PieceInfo> info;
+    std::vector<int32_t> tile;
+    int64_t total = 0;
+};
+
+struct HostGatherTable {
+    std::vector<int64_t> k0;
+    std::vector<int64_t> delta;
+    std::vector<int32_t> tile;
+    int64_t total = 0;
+};
+
+// Kernel operations over E-space.
+enum ShardOp : int {
+    OP_COPYIN = 0,      // flat params -> master, work, m = v = 0
+    OP_REDUCE_SET = 1,  // acc = sum_r grads
+    OP_REDUCE_ACC = 2,  // acc = acc + sum_r grads
+    OP_FUSED = 3,       // g = sum_r grads; Adam; cast
+    OP_FUSED_ACC = 4,   // g = acc + sum_r grads; Adam; cast
+    OP_ADAM = 5         // g = acc; Adam; cast
+};
+
+struct AdamScalars {
+    float lr, b1, b2, eps;
+    float omb1, omb2, bc1, bc2;
+};
+
+struct ShardLaunch {
+    ShardTable tab;
+    int64_t e_begin = 0;  // processed range of E-space
+    int64_t e_end = 0;
+    float* master = nullptr;
+    float* m = nullptr;
+    float* v = nullptr;
+    uint16_t* work = nullptr;
+    float* acc = nullptr;
+    const void* src = nullptr;  // flat params (OP_COPYIN)
+    AdamScalars hp{};
+    int32_t nd = 0;
+    int32_t shard_layout = 0;  // 1: grads indexed like E-space
+    const void* const* grads = nullptr;  // host array of nd device pointers
+};
+
+struct GatherLaunch {
+    GatherTable tab;
+    int64_t k_first = 0;  // first global flat index
+    int64_t count = 0;    // elements to write
+    const void* src = nullptr;
+    void* out = nullptr;
+};
+
+// Launch one E-space operation; dtype is the gradient / parameter dtype.
+hipError_t launch_shard_op(const ShardLaunch& L, ShardOp op, zsp_dtype dtype,
+                           hipStream_t stream);
+// Launch a gather; dtype is the element type of src/out.
+hipError_t launch_gather(const GatherLaunch& L, zsp_dtype dtype, hipStream_t stream);
+
+// Host layout helpers (zsp_layout.cpp).
+int64_t pad_for(int64_t numel, int32_t nd);
+void build_shard_table(const std::vector<int64_t>& numel, const std::vector<int64_t>& shard_len,
+                       const std::vector<int64_t>& full_off,
+                       const std::vector<int64_t>& shard_off,
+                       const std::vector<int64_t>& flat_off, int64_t S, int32_t nd,
+                       int32_t rank_or_all, HostShardTable& out);
+void build_gather_table(const std::vector<int64_t>& numel,
+                        const std::vector<int64_t>& shard_len,
+                        const std::vector<int64_t>& shard_off,
+                        const std::vector<int64_t>& flat_off, int64_t S, int32_t nd,
+                        HostGatherTable& out);
+void build_tile_index(const std::vector<int64_t>& starts, int64_t total,
+                      std::vector<int32_t>& tile);
+
+}  // namespace zsp
+
+struct zsp_plan {
+    int32_t T = 0;
+    int32_t nd = 0;
+    std::vector<int64_t> numel, pad, shard_len, full_off, shard_off, flat_off;
+    int64_t S = 0;
+    int64_t total_padded = 0;
+    int64_t total_numel = 0;
+
+    bool bound = false;
+    int32_t bind_rank = ZSP_ALL_RANKS;
+    int device = -1;
+    float* master = nullptr;
+    float* m = nullptr;
+    float* v = nullptr;
+    uint16_t* work = nullptr;
+    float* acc = nullptr;
+
+    void* dev_blob = nullptr;  // one device allocation holding both tables
+    zsp::ShardTable shard;
+    zsp::GatherTable gather;
+};
