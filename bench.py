@@ -1,0 +1,407 @@
+"""Benchmark of the ZeRO-3 per-rank hot path on one MI355X.
+
+One step = the whole hot path over one batch of synthetic input:
+  * the shard reduce of every virtual rank's gradient fused with the Adam
+    step and the bf16 cast (one launch over all N_d ranks; with gradient
+    accumulation, the earlier micro-batches' reduce launches first), then
+  * the parameter gathers before forward and again before backward.
+Inputs are seeded, synthetic and already resident in HBM when timing starts.
+
+Metric: effective GB/s = algorithmic bytes / time, where algorithmic bytes
+count what the method must move per real (non-pad) element:
+  fused reduce+Adam+cast   N_d*g + 12 (read master, m, v) + 14 (write master,
+                           m, v, bf16 work) [+ 4 reading the accumulator]
+  reduce (accumulate)      N_d*g + 4 (write) [+ 4 read when accumulating]
+  gather                   2*w (read shard, write full) per unpadded element
+with g, w the gradient and parameter element sizes in bytes.
+
+Prints one JSON line. `--rocprof-summary DIR` instead turns rocprofv3 output
+into the text summaries kept under profiles/.
+"""
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, AMD's published figure
+DEFAULT_WORKLOAD = "llama7b_layer_nd8"
+METRIC = "effective GB/s (and % HBM peak) of shard reduce+Adam+cast step and param gather"
+KERNEL_SOURCES = ["zero_sharded_mixed_pad_amd/csrc/zsp_kernels.hip",
+                  "zero_sharded_mixed_pad_amd/csrc/zsp_internal.hpp",
+                  "zero_sharded_mixed_pad_amd/_build.py"]
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="target CPU time for the oracle baseline sample")
+    ap.add_argument("--flush", choices=["auto", "on", "off"], default="auto",
+                    help="overwrite a 1 GiB buffer before each step so a small working set "
+                         "is not served from the 256 MB Infinity Cache")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run plain 2 GiB device copies (PMC byte-count calibration)")
+    ap.add_argument("--rocprof-summary", metavar="DIR", default=None)
+    ap.add_argument("--summary-out", default=None)
+    return ap.parse_args()
+
+
+# ---------------------------------------------------------------------------
+# Hot-path runner
+# ---------------------------------------------------------------------------
+
+class Runner:
+    def __init__(self, w, device):
+        import torch
+        import zero_sharded_mixed_pad_amd as zsp
+        from zero_sharded_mixed_pad_amd import synth
+
+        self.torch, self.zsp, self.synth = torch, zsp, synth
+        self.w, self.dev = w, device
+        self.plan = zsp.partition(w.numel, w.n_d)
+        S, nd = self.plan.S, w.n_d
+        self.rank = zsp.ALL_RANKS if w.rank_local < 0 else w.rank_local
+        n_state = S if w.rank_local >= 0 else nd * S
+        f32, bf16 = torch.float32, torch.bfloat16
+        self.master = torch.empty(n_state, dtype=f32, device=device)
+        self.m = torch.empty(n_state, dtype=f32, device=device)
+        self.v = torch.empty(n_state, dtype=f32, device=device)
+        self.work = torch.empty(n_state, dtype=bf16, device=device)
+        self.acc = torch.empty(n_state, dtype=f32, device=device) if w.micro_batches > 1 else None
+        self.plan.bind_state(self.rank, self.master, self.m, self.v, self.work, self.acc)
+        flat = synth.flat_params(w, device=device)
+        self.plan.load_params(flat)
+        torch.cuda.synchronize()
+        del flat
+        self.layout = "shard" if w.rank_local >= 0 else "full"
+        gsize = S if w.rank_local >= 0 else self.plan.total_padded
+        self.grads = [synth.grad_buffer(w, gsize, r, device=device) for r in range(nd)]
+        # valid (non-pad) elements the step updates
+        if w.rank_local >= 0:
+            j = w.rank_local
+            self.valid = 0
+            for t in range(len(w.numel)):
+                s = self.plan.tensor(t)["shard_len"]
+                self.valid += max(0, min(s, w.numel[t] - j * s))
+        else:
+            self.valid = self.plan.total_numel
+        gb = 2 if w.grad_dtype == bf16 else 4
+        acc_read = 4 if w.micro_batches > 1 else 0
+        self.bytes_fused = self.valid * (nd * gb + 26 + acc_read)
+        self.bytes_reduce_first = self.valid * (nd * gb + 4)
+        self.bytes_reduce_acc = self.valid * (nd * gb + 8)
+        # gathers: one per layer-sized group, before forward and before backward
+        self.gather_groups = []
+        if w.rank_local < 0:
+            if w.name.startswith("mlp"):
+                groups = [(t, 1) for t in range(len(w.numel))]
+            else:
+                groups = [(0, len(w.numel))]
+            for first, n in groups:
+                cnt = sum(w.numel[first:first + n])
+                out = torch.empty(cnt, dtype=bf16, device=device)
+                self.gather_groups.append((first, n, out, cnt * 4))
+        self.step_no = 0
+        self.ev = {"fused": [], "reduce": [], "gather": []}
+
+    def _event(self):
+        return self.torch.cuda.Event(enable_timing=True)
+
+    def _timed(self, kind, fn, record):
+        if record:
+            a, b = self._event(), self._event()
+            a.record()
+            fn()
+            b.record()
+            self.ev[kind].append((a, b))
+        else:
+            fn()
+
+    def step(self, record=False):
+        w, p = self.w, self.plan
+        self.step_no += 1
+        hp = dict(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, step=self.step_no)
+        if w.micro_batches > 1:
+            for mb in range(w.micro_batches - 1):
+                self._timed("reduce", lambda mb=mb: p.reduce_shard(
+                    self.rank, self.grads, layout=self.layout, accumulate=mb > 0), record)
+            self._timed("fused", lambda: p.reduce_adam_step(
+                self.rank, self.grads, layout=self.layout, use_acc=True, **hp), record)
+        else:
+            self._timed("fused", lambda: p.reduce_adam_step(
+                self.rank, self.grads, layout=self.layout, **hp), record)
+        for _ in range(2):  # before forward, and again before backward
+            for first, n, out, _b in self.gather_groups:
+                self._timed("gather", lambda first=first, n=n, out=out: p.gather_many(
+                    first, n, out, "work"), record)
+
+    def step_bytes(self):
+        w = self.w
+        b = self.bytes_fused
+        if w.micro_batches > 1:
+            b += self.bytes_reduce_first + (w.micro_batches - 2) * self.bytes_reduce_acc
+        b += 2 * sum(g[3] for g in self.gather_groups)
+        return b
+
+    def kernel_stats(self):
+        out = {}
+        w = self.w
+        for kind, evs in self.ev.items():
+            if not evs:
+                continue
+            ms = [a.elapsed_time(b) for a, b in evs]
+            avg_s = sum(ms) / len(ms) / 1e3
+            if kind == "fused":
+                nbytes = self.bytes_fused
+            elif kind == "reduce":
+                nb = [self.bytes_reduce_first] + [self.bytes_reduce_acc] * (w.micro_batches - 2)
+                nbytes = sum(nb) / len(nb)
+            else:
+                nbytes = sum(g[3] for g in self.gather_groups) / len(self.gather_groups)
+            gbps = nbytes / avg_s / 1e9
+            out[kind] = {"launches": len(ms), "avg_us": round(avg_s * 1e6, 2),
+                         "min_us": round(min(ms) * 1e3, 2), "bytes_per_launch": int(nbytes),
+                         "GBps": round(gbps, 1), "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4)}
+        return out
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle, as it stands, on a bounded sample
+# ---------------------------------------------------------------------------
+
+def cpu_baseline(runner, target_s):
+    import numpy as np
+    import torch
+    import oracle
+
+    w = runner.w
+    nd = w.n_d
+    torch.cuda.synchronize()
+
+    def host(t):
+        t = t.detach().cpu()
+        if t.dtype == torch.bfloat16:
+            return t.view(torch.int16).numpy().view(np.uint16)
+        return t.numpy()
+
+    j = w.rank_local if w.rank_local >= 0 else 0
+    S = runner.plan.S
+    base = 0 if w.rank_local >= 0 else j * S
+    grads = [host(g) for g in runner.grads]
+    master = host(runner.master[base:base + S]).copy()
+    m = host(runner.m[base:base + S]).copy()
+    v = host(runner.v[base:base + S]).copy()
+    work = host(runner.work[base:base + S]).copy()
+    all_work = host(runner.work) if w.rank_local < 0 else None
+    layout = oracle.GRADS_SHARD if w.rank_local >= 0 else oracle.GRADS_FULL
+    L = oracle.Layout(w.numel, nd)
+    valid = int(sum(max(0, min(int(L.shard_len[t]), int(L.numel[t]) - j * int(L.shard_len[t])))
+                    for t in range(L.T)))
+    gb = 2 if w.grad_dtype == torch.bfloat16 else 4
+    fused_bytes = valid * (nd * gb + 26)
+    gather_bytes = L.total_numel * 4 if all_work is not None else 0
+
+    done_bytes, t0, passes = 0, time.perf_counter(), 0
+    while True:
+        red = oracle.reduce(w.numel, nd, j, grads, layout)
+        oracle.adam(w.numel, nd, j, master, m, v, work, red, w.lr, w.beta1, w.beta2, w.eps,
+                    passes + 1)
+        done_bytes += fused_bytes
+        if all_work is not None:
+            for t in range(L.T):
+                oracle.gather(w.numel, nd, t, all_work)
+            done_bytes += gather_bytes
+        passes += 1
+        el = time.perf_counter() - t0
+        if el >= target_s or el * (passes + 1) / passes > 3 * target_s:
+            break
+    el = time.perf_counter() - t0
+    what = (f"rank {j}'s reduce over {nd} gradient buffers + Adam + cast on its "
+            f"{valid:,}-element shard")
+    if all_work is not None:
+        what += f", plus one gather of all {L.T} parameters"
+    return {"value": round(done_bytes / el / 1e9, 3), "unit": "GB/s", "cores": 1,
+            "kind": "oracle", "seconds": round(el, 2),
+            "sample": f"{passes} pass(es) of {what} (single-threaded C oracle)"}
+
+
+# ---------------------------------------------------------------------------
+# rocprofv3 summaries
+# ---------------------------------------------------------------------------
+
+_OPS = {0: "copy_in", 1: "reduce_set", 2: "reduce_acc", 3: "fused_reduce_adam_cast",
+        4: "fused_reduce_adam_cast_acc", 5: "adam_from_acc"}
+
+
+def _short(name):
+    """Readable kernel name from a mangled or demangled rocprofv3 name."""
+    import re
+    m = re.search(r"shard_kernel(?:ILi|<)(\d)", name)
+    if m:
+        dt = "f32" if ("ILi%sEf" % m.group(1)) in name or ", float" in name else "bf16"
+        return f"{_OPS[int(m.group(1))]}[{dt}]"
+    if "gather_kernel" in name:
+        return "gather[f32]" if ("IfE" in name or "<float>" in name) else "gather[bf16]"
+    name = re.sub(r"^void ", "", name)
+    return name[:48]
+
+
+def rocprof_summary(d, out):
+    lines = []
+    stats = sorted(glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True))
+    for path in stats:
+        lines.append(f"kernel stats: {os.path.relpath(path, d)}")
+        lines.append(f"{'kernel':<48} {'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10}")
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                lines.append(f"{_short(row['Name']):<48} {row['Calls']:>6} "
+                             f"{float(row['AverageNs']) / 1e3:>10.2f} "
+                             f"{float(row['MinNs']) / 1e3:>10.2f} "
+                             f"{float(row['MaxNs']) / 1e3:>10.2f}")
+    counters = sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True))
+    for path in counters:
+        agg = {}
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                k = (_short(row["Kernel_Name"]), row["Counter_Name"])
+                agg.setdefault(k, []).append(float(row["Counter_Value"]))
+        lines.append(f"counters: {os.path.relpath(path, d)}")
+        lines.append(f"{'kernel':<48} {'counter':<12} {'dispatches':>10} {'avg_KiB':>14}")
+        for (k, c), vals in sorted(agg.items()):
+            lines.append(f"{k:<48} {c:<12} {len(vals):>10} {sum(vals) / len(vals):>14.1f}")
+    text = "\n".join(lines) + "\n"
+    if out:
+        with open(out, "w") as f:
+            f.write(text)
+    print(text)
+
+
+def load_traffic(workload):
+    """Measured HBM bytes per fused launch from the committed counter summary,
+    if it was taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return d.get("fused_bytes_per_launch")
+
+
+# ---------------------------------------------------------------------------
+
+def main():
+    args = parse()
+    if args.rocprof_summary:
+        rocprof_summary(args.rocprof_summary, args.summary_out)
+        return 0
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}).", file=sys.stderr)
+        return 2
+
+    import __graft_entry__
+    __graft_entry__.ensure_built()
+    import torch
+    from zero_sharded_mixed_pad_amd import synth
+
+    wl = synth.workloads()
+    if args.workload not in wl:
+        print(f"unknown workload {args.workload}; choose from {sorted(wl)}", file=sys.stderr)
+        return 2
+    w = wl[args.workload]
+    device = torch.device("cuda:0")
+    torch.cuda.set_device(device)
+    r = Runner(w, device)
+    flush = args.flush == "on" or (args.flush == "auto" and r.bytes_fused < 2e9)
+    scratch = torch.empty(1 << 30, dtype=torch.uint8, device=device) if flush else None
+
+    for _ in range(args.warmup):
+        if flush:
+            scratch.fill_(1)
+        r.step()
+    torch.cuda.synchronize()
+    step_events = []
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        if flush:
+            scratch.fill_(1)
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        r.step(record=True)
+        b.record()
+        step_events.append((a, b))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    event_ms = sum(a.elapsed_time(b) for a, b in step_events) / args.steps
+    # Without a flush the wall clock around the K steps is the step time; with
+    # one, the per-step events exclude the flush kernel.
+    ms_per_step = event_ms if flush else wall * 1e3 / args.steps
+    step_bytes = r.step_bytes()
+    value = step_bytes / (ms_per_step / 1e3) / 1e9
+    ks = r.kernel_stats()
+
+    if args.calibrate_copy:
+        src = torch.empty(1 << 30, dtype=torch.bfloat16, device=device)
+        dst = torch.empty_like(src)
+        src.fill_(1.0)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    fused = ks["fused"]
+    roof = {"bound": "hbm", "achieved": fused["GBps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(fused["GBps"] / HBM_PEAK_GBPS, 4), "traffic": load_traffic(w.name),
+            "kernel": "fused reduce+Adam+cast (all ranks, one launch)",
+            "bytes_per_launch": fused["bytes_per_launch"], "avg_launch_us": fused["avg_us"]}
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(r, args.cpu_seconds)
+        cpu["value_vs_gpu_ratio"] = round(value / cpu["value"], 1) if cpu["value"] else None
+
+    gdt = "bf16" if w.grad_dtype == torch.bfloat16 else "f32"
+    pdt = "bf16" if w.param_dtype == torch.bfloat16 else "f32"
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic (seeded normal gradients and parameters, resident in HBM)",
+        "config": {"workload": w.name, "n_d": w.n_d, "params": len(w.numel),
+                   "elements": sum(w.numel), "param_dtype": pdt, "grad_dtype": gdt,
+                   "state": "fp32 master, m, v + bf16 working copy",
+                   "micro_batches": w.micro_batches,
+                   "rank_local": w.rank_local if w.rank_local >= 0 else None,
+                   "gathers_per_step": 2 * len(r.gather_groups),
+                   "bytes_per_step": int(step_bytes), "cache_flush": bool(flush),
+                   "wall_ms_per_step": round(wall * 1e3 / args.steps, 4)},
+        "roofline": roof, "cpu_baseline": cpu, "kernels": ks,
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
