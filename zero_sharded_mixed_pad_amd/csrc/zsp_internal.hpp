@@ -12,13 +12,11 @@
 
 namespace zsp {
 
-// Elements one wavefront handles per tile: 64 lanes x 8 contiguous elements.
-// Offset tables are indexed at this granularity.
+// Elements one wavefront handles per tile (64 lanes x 8 elements); the
+// kernels launch one wavefront per workgroup. Offset tables are indexed at
+// this granularity.
 constexpr int64_t kTile = 512;
 constexpr int kWaveLanes = 64;
-constexpr int kElemsPerLane = 8;
-constexpr int kBlockThreads = 256;
-constexpr int kWavesPerBlock = kBlockThreads / kWaveLanes;
 
 // One piece of the shard index space ("E-space"): the run of elements of
 // one rank's slice of one parameter. E-space is the index space of the bound

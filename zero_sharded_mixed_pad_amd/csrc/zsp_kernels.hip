@@ -1,22 +1,33 @@
 // zsp_kernels.hip -- HIP kernels of libzsp for gfx950 (MI355X, CDNA4).
 //
 // Every kernel here is a stream over HBM with a few fp32 operations per
-// byte: no contraction, so no MFMA and no LDS for data. The design points:
+// byte: no contraction, so no MFMA and no LDS for data. Design points, each
+// chosen by measurement on MI355X:
 //
-//  * One wavefront owns one 512-element tile of the index space; lane l
-//    handles 8 contiguous elements, so every state array moves as 16- or
-//    32-byte vectors per lane (global_load/store_dwordx4), fully coalesced.
-//  * The tile's parameter is found from a per-tile table (one or two cached
-//    loads), so a launch can span any number of parameters -- thousands of
-//    small ones as easily as one large one -- with no per-parameter launch.
+//  * One wavefront per workgroup, owning one 512-element tile of the index
+//    space. Small workgroups keep more, shorter-lived waves in flight, which
+//    measured faster than 256-thread groups for these streams.
+//  * Lane l owns two 4-element quads of the tile, at 4*l and 256 + 4*l, so
+//    every load and store instruction of the wave covers one contiguous run
+//    (1 KiB for fp32 state, 512 B for bf16). Giving a lane 8 contiguous
+//    elements instead makes each fp32 instruction touch every other 16 bytes
+//    of a 2 KiB run, which measured ~5% slower.
+//  * Every stream is touched once per launch, so all global loads and stores
+//    carry the non-temporal hint; that measured a further ~5%.
+//  * The optimizer state of both quads is loaded before the gradients so the
+//    state's latency overlaps the rank loop.
+//  * The tile's parameter comes from a per-tile table: wave-uniform, so the
+//    common single-parameter tile costs two scalar loads. A launch can span
+//    any number of parameters -- thousands of small ones as easily as one
+//    large one -- with no per-parameter launch.
 //  * Gradient and parameter sources may sit at any 2-byte offset relative to
-//    the 8-element groups (each parameter is padded on its own, so slices do
-//    not line up). gfx9 global memory serves unaligned dwordx4 loads, so the
-//    fast path stays one vector load per 8 elements; only groups that cross
-//    a parameter or pad boundary take the per-element path.
+//    the quads (each parameter is padded on its own, so slices do not line
+//    up). gfx9 global memory serves unaligned vector loads, so the fast path
+//    stays one vector load per quad; only quads that cross a parameter or pad
+//    boundary take the per-element path.
 //  * The reduce over N_d ranks keeps each lane's 8 sums in registers and adds
 //    rank r's values strictly after rank r-1's (fixed order, bit-exact); the
-//    ranks are loaded 8 at a time so 8 loads are in flight per lane.
+//    ranks are loaded 8 at a time, so 16 loads per lane are in flight.
 //  * Floating point: built with -ffp-contract=off; division and square root
 //    are the default correctly rounded expansions; bf16 narrowing is the
 //    hardware round-to-nearest-even convert (v_cvt_pk_bf16_f32).
@@ -29,17 +40,29 @@
 namespace zsp {
 namespace {
 
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+// Same vectors at the alignment of their element type: sources that start at
+// any element offset.
+typedef uint32_t u32x2_a2 __attribute__((ext_vector_type(2), aligned(2)));
+typedef uint32_t u32x4_a2 __attribute__((ext_vector_type(4), aligned(2)));
+typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-struct __attribute__((packed, aligned(2))) Unaligned16 {
-    u32x4 v;
-};
+constexpr int kQuad = 4;
+constexpr int kHalf = kTile / 2;  // second quad of a lane is this far on
 
-__device__ __forceinline__ u32x4 ld16u(const void* p) {
-    return reinterpret_cast<const Unaligned16*>(p)->v;
-}
+// Non-temporal accesses. One named function per pointer type rather than a
+// template or overloads: both would lose the reduced alignment of the
+// *_a2 / *_a4 typedefs (they are the same type as the aligned vector).
+__device__ __forceinline__ u32x2 ldnt_x2_a2(const u32x2_a2* p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ u32x4 ldnt_x4_a2(const u32x4_a2* p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ u32x4 ldnt_x4_a4(const u32x4_a4* p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ f32x4 ldnt_f32x4(const f32x4* p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ void stnt(f32x4* p, f32x4 v) { __builtin_nontemporal_store(v, p); }
+__device__ __forceinline__ void stnt(u32x2* p, u32x2 v) { __builtin_nontemporal_store(v, p); }
+__device__ __forceinline__ void stnt(u32x4* p, u32x4 v) { __builtin_nontemporal_store(v, p); }
 
 __device__ __forceinline__ float bf_lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
@@ -55,22 +78,17 @@ __device__ __forceinline__ uint16_t to_bf16(float a) {
     return __builtin_bit_cast(uint16_t, static_cast<__bf16>(a));
 }
 
+// 4 consecutive elements of a bf16 or fp32 source at any element offset.
 template <typename GT>
-__device__ __forceinline__ void load8(const void* base, int64_t idx, float (&x)[8]) {
+__device__ __forceinline__ void load4(const void* base, int64_t idx, float (&x)[4]) {
     if constexpr (std::is_same<GT, uint16_t>::value) {
-        const u32x4 u = ld16u(static_cast<const uint16_t*>(base) + idx);
+        const u32x2 u = ldnt_x2_a2(reinterpret_cast<const u32x2_a2*>(static_cast<const uint16_t*>(base) + idx));
         x[0] = bf_lo(u.x); x[1] = bf_hi(u.x);
         x[2] = bf_lo(u.y); x[3] = bf_hi(u.y);
-        x[4] = bf_lo(u.z); x[5] = bf_hi(u.z);
-        x[6] = bf_lo(u.w); x[7] = bf_hi(u.w);
     } else {
-        const float* f = static_cast<const float*>(base) + idx;
-        const u32x4 a = ld16u(f);
-        const u32x4 b = ld16u(f + 4);
-        x[0] = __uint_as_float(a.x); x[1] = __uint_as_float(a.y);
-        x[2] = __uint_as_float(a.z); x[3] = __uint_as_float(a.w);
-        x[4] = __uint_as_float(b.x); x[5] = __uint_as_float(b.y);
-        x[6] = __uint_as_float(b.z); x[7] = __uint_as_float(b.w);
+        const u32x4 u = ldnt_x4_a4(reinterpret_cast<const u32x4_a4*>(static_cast<const float*>(base) + idx));
+        x[0] = __uint_as_float(u.x); x[1] = __uint_as_float(u.y);
+        x[2] = __uint_as_float(u.z); x[3] = __uint_as_float(u.w);
     }
 }
 
@@ -80,6 +98,19 @@ __device__ __forceinline__ float load1(const void* base, int64_t idx) {
         return __uint_as_float(uint32_t(static_cast<const uint16_t*>(base)[idx]) << 16);
     else
         return static_cast<const float*>(base)[idx];
+}
+
+__device__ __forceinline__ void ld_f32x4(const float* p, float (&x)[4]) {
+    const f32x4 v = ldnt_f32x4(reinterpret_cast<const f32x4*>(p));
+    x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
+}
+
+__device__ __forceinline__ void st_f32x4(float* p, const float (&x)[4]) {
+    stnt(reinterpret_cast<f32x4*>(p), f32x4{x[0], x[1], x[2], x[3]});
+}
+
+__device__ __forceinline__ void st_bf16x4(uint16_t* p, const float (&x)[4]) {
+    stnt(reinterpret_cast<u32x2*>(p), u32x2{pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3])});
 }
 
 // Adam (Kingma & Ba, Algorithm 1) on one element, one fp32 rounding per
@@ -102,7 +133,7 @@ struct ShardArgs {
     const int64_t* e0;
     const PieceInfo* info;
     const int32_t* tile;
-    int64_t tile_first, tile_end, e_begin, e_end;
+    int64_t tile_first, e_begin, e_end;
     float* master;
     float* m;
     float* v;
@@ -121,36 +152,45 @@ constexpr bool reads_acc(int op) {
     return op == OP_REDUCE_ACC || op == OP_FUSED_ACC || op == OP_ADAM;
 }
 constexpr bool is_reduce(int op) { return op == OP_REDUCE_SET || op == OP_REDUCE_ACC; }
+constexpr bool is_adam(int op) { return op == OP_FUSED || op == OP_FUSED_ACC || op == OP_ADAM; }
 
-// Sum of the N_d ranks' values for 8 contiguous elements, rank order.
-template <typename GT, int CAP>
-__device__ __forceinline__ void reduce8(const ShardArgs<CAP>& a, int64_t sidx, float (&g)[8]) {
+// Sum over the N_d ranks, in rank order, of NQ quads per lane.
+template <typename GT, int CAP, int NQ>
+__device__ __forceinline__ void reduce_quads(const ShardArgs<CAP>& a, const int64_t (&s)[NQ],
+                                             float (&g)[NQ][kQuad]) {
     const int nd = a.nd;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) g[k] = 0.0f;
     int r0 = 0;
     for (; r0 + 8 <= nd; r0 += 8) {
-        float x[8][8];
+        float x[8][NQ][kQuad];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) load8<GT>(a.grads[r0 + q], sidx, x[q]);
+        for (int q = 0; q < 8; ++q)
+#pragma unroll
+            for (int h = 0; h < NQ; ++h) load4<GT>(a.grads[r0 + q], s[h], x[q][h]);
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
             const bool first = (r0 + q) == 0;
 #pragma unroll
-            for (int k = 0; k < 8; ++k) g[k] = first ? x[q][k] : g[k] + x[q][k];
+            for (int h = 0; h < NQ; ++h)
+#pragma unroll
+                for (int k = 0; k < kQuad; ++k) g[h][k] = first ? x[q][h][k] : g[h][k] + x[q][h][k];
         }
     }
     if (r0 < nd) {
-        float x[8][8];
+        float x[8][NQ][kQuad];
 #pragma unroll
         for (int q = 0; q < 8; ++q)
-            if (r0 + q < nd) load8<GT>(a.grads[r0 + q], sidx, x[q]);
+            if (r0 + q < nd)
+#pragma unroll
+                for (int h = 0; h < NQ; ++h) load4<GT>(a.grads[r0 + q], s[h], x[q][h]);
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
             if (r0 + q < nd) {
                 const bool first = (r0 + q) == 0;
 #pragma unroll
-                for (int k = 0; k < 8; ++k) g[k] = first ? x[q][k] : g[k] + x[q][k];
+                for (int h = 0; h < NQ; ++h)
+#pragma unroll
+                    for (int k = 0; k < kQuad; ++k)
+                        g[h][k] = first ? x[q][h][k] : g[h][k] + x[q][h][k];
             }
         }
     }
@@ -163,82 +203,82 @@ __device__ __forceinline__ float reduce1(const ShardArgs<CAP>& a, int64_t sidx) 
     return g;
 }
 
-__device__ __forceinline__ void st_f32x8(float* p, const float (&x)[8]) {
-    f32x4* q = reinterpret_cast<f32x4*>(p);
-    q[0] = f32x4{x[0], x[1], x[2], x[3]};
-    q[1] = f32x4{x[4], x[5], x[6], x[7]};
-}
-
-__device__ __forceinline__ void ld_f32x8(const float* p, float (&x)[8]) {
-    const f32x4* q = reinterpret_cast<const f32x4*>(p);
-    const f32x4 a = q[0], b = q[1];
-    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
-}
-
-// 8 contiguous, in-range, non-pad elements of one piece starting at E
-// (E is a multiple of 8, so every state access is an aligned vector).
-template <int OP, typename GT, int CAP>
-__device__ __forceinline__ void fast_group(const ShardArgs<CAP>& a, int64_t E,
-                                           const PieceInfo& pi) {
+// NQ quads, each 4 in-range, non-pad elements of one piece. E[h] is a
+// multiple of 4, so every state access is an aligned 16-byte vector;
+// gs[h] / is[h] are the quads' gradient / flat-parameter source indices.
+template <int OP, typename GT, int CAP, int NQ>
+__device__ __forceinline__ void quads_fast(const ShardArgs<CAP>& a, const int64_t (&E)[NQ],
+                                           const int64_t (&gs)[NQ], const int64_t (&is)[NQ]) {
     if constexpr (OP == OP_COPYIN) {
-        const int64_t s = E + pi.idelta;
-        float x[8];
-        load8<GT>(a.src, s, x);
-        st_f32x8(a.master + E, x);
-        u32x4 w;
-        if constexpr (std::is_same<GT, uint16_t>::value) {
-            w = ld16u(static_cast<const uint16_t*>(a.src) + s);
-        } else {
-            w = u32x4{pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3]), pack_bf16(x[4], x[5]),
-                      pack_bf16(x[6], x[7])};
+#pragma unroll
+        for (int h = 0; h < NQ; ++h) {
+            float x[kQuad];
+            load4<GT>(a.src, is[h], x);
+            st_f32x4(a.master + E[h], x);
+            if constexpr (std::is_same<GT, uint16_t>::value) {
+                const u32x2 raw = ldnt_x2_a2(reinterpret_cast<const u32x2_a2*>(
+                    static_cast<const uint16_t*>(a.src) + is[h]));
+                stnt(reinterpret_cast<u32x2*>(a.work + E[h]), raw);
+            } else {
+                st_bf16x4(a.work + E[h], x);
+            }
+            const float z[kQuad] = {0.0f, 0.0f, 0.0f, 0.0f};
+            st_f32x4(a.m + E[h], z);
+            st_f32x4(a.v + E[h], z);
         }
-        *reinterpret_cast<u32x4*>(a.work + E) = w;
-        const float z[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-        st_f32x8(a.m + E, z);
-        st_f32x8(a.v + E, z);
     } else {
-        float g[8];
-        if constexpr (uses_grads(OP)) {
-            const int64_t s = a.shard_layout ? E : E + pi.gdelta;
-            reduce8<GT>(a, s, g);
+        float p[NQ][kQuad], m[NQ][kQuad], v[NQ][kQuad], c[NQ][kQuad], g[NQ][kQuad];
+        if constexpr (is_adam(OP)) {
+#pragma unroll
+            for (int h = 0; h < NQ; ++h) {
+                ld_f32x4(a.master + E[h], p[h]);
+                ld_f32x4(a.m + E[h], m[h]);
+                ld_f32x4(a.v + E[h], v[h]);
+            }
         }
         if constexpr (reads_acc(OP)) {
-            float c[8];
-            ld_f32x8(a.acc + E, c);
 #pragma unroll
-            for (int k = 0; k < 8; ++k) g[k] = (OP == OP_ADAM) ? c[k] : c[k] + g[k];
+            for (int h = 0; h < NQ; ++h) ld_f32x4(a.acc + E[h], c[h]);
+        }
+        if constexpr (uses_grads(OP)) {
+            reduce_quads<GT, CAP, NQ>(a, gs, g);
+        }
+#pragma unroll
+        for (int h = 0; h < NQ; ++h) {
+#pragma unroll
+            for (int k = 0; k < kQuad; ++k) {
+                if constexpr (OP == OP_ADAM) g[h][k] = c[h][k];
+                else if constexpr (reads_acc(OP)) g[h][k] = c[h][k] + g[h][k];
+            }
         }
         if constexpr (is_reduce(OP)) {
-            st_f32x8(a.acc + E, g);
-        } else {
-            float p[8], m[8], v[8];
-            ld_f32x8(a.master + E, p);
-            ld_f32x8(a.m + E, m);
-            ld_f32x8(a.v + E, v);
 #pragma unroll
-            for (int k = 0; k < 8; ++k) adam1(p[k], m[k], v[k], g[k], a.hp);
-            st_f32x8(a.master + E, p);
-            st_f32x8(a.m + E, m);
-            st_f32x8(a.v + E, v);
-            *reinterpret_cast<u32x4*>(a.work + E) =
-                u32x4{pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3]), pack_bf16(p[4], p[5]),
-                      pack_bf16(p[6], p[7])};
+            for (int h = 0; h < NQ; ++h) st_f32x4(a.acc + E[h], g[h]);
+        } else {
+#pragma unroll
+            for (int h = 0; h < NQ; ++h) {
+#pragma unroll
+                for (int k = 0; k < kQuad; ++k) adam1(p[h][k], m[h][k], v[h][k], g[h][k], a.hp);
+                st_f32x4(a.master + E[h], p[h]);
+                st_f32x4(a.m + E[h], m[h]);
+                st_f32x4(a.v + E[h], v[h]);
+                st_bf16x4(a.work + E[h], p[h]);
+            }
         }
     }
 }
 
-// 8 contiguous in-range pad elements.
+// One quad of in-range pad elements.
 template <int OP, int CAP>
-__device__ __forceinline__ void pad_group(const ShardArgs<CAP>& a, int64_t E) {
-    const float z[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+__device__ __forceinline__ void quad_pad(const ShardArgs<CAP>& a, int64_t E) {
+    const float z[kQuad] = {0.0f, 0.0f, 0.0f, 0.0f};
     if constexpr (OP == OP_COPYIN) {
-        st_f32x8(a.master + E, z);
-        st_f32x8(a.m + E, z);
-        st_f32x8(a.v + E, z);
-        *reinterpret_cast<u32x4*>(a.work + E) = u32x4{0u, 0u, 0u, 0u};
+        st_f32x4(a.master + E, z);
+        st_f32x4(a.m + E, z);
+        st_f32x4(a.v + E, z);
+        stnt(reinterpret_cast<u32x2*>(a.work + E), u32x2{0u, 0u});
     } else if constexpr (is_reduce(OP)) {
-        st_f32x8(a.acc + E, z);
+        st_f32x4(a.acc + E, z);
     }
 }
 
@@ -285,38 +325,76 @@ __device__ __forceinline__ void elem_op(const ShardArgs<CAP>& a, int64_t e, bool
     }
 }
 
-template <int OP, typename GT, int CAP>
-__global__ __launch_bounds__(kBlockThreads) void shard_kernel(const ShardArgs<CAP> a) {
-    const int lane = threadIdx.x & (kWaveLanes - 1);
-    const int64_t tile = a.tile_first + int64_t(blockIdx.x) * kWavesPerBlock +
-                         (threadIdx.x / kWaveLanes);
-    if (tile >= a.tile_end) return;
-    const int64_t E = tile * kTile + int64_t(lane) * kElemsPerLane;
-    if (E >= a.e_end || E + kElemsPerLane <= a.e_begin) return;
+enum QuadKind : int { Q_OUT = 0, Q_FAST = 1, Q_PAD = 2, Q_SLOW = 3 };
 
-    // Piece holding E: the tile table brackets it, usually to one entry.
-    int lo = a.tile[tile];
-    int hi = a.tile[tile + 1];
+// Piece holding element E, searched inside the tile's bracket [lo, hi].
+__device__ __forceinline__ int find_piece(const int64_t* e0, int lo, int hi, int64_t E) {
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
-        if (a.e0[mid] <= E) lo = mid;
+        if (e0[mid] <= E) lo = mid;
         else hi = mid - 1;
     }
-    int p = lo;
-    PieceInfo pi = a.info[p];
+    return lo;
+}
 
-    const bool inside = E >= a.e_begin && E + kElemsPerLane <= a.e_end;
-    if (inside && E + kElemsPerLane <= pi.vend) {
-        fast_group<OP, GT, CAP>(a, E, pi);
-    } else if (inside && E >= pi.vend && E + kElemsPerLane <= pi.end) {
-        pad_group<OP, CAP>(a, E);
-    } else {
-        for (int k = 0; k < kElemsPerLane; ++k) {
+template <int CAP>
+__device__ __forceinline__ int classify(const ShardArgs<CAP>& a, int64_t E, const PieceInfo& pi) {
+    if (E >= a.e_end || E + kQuad <= a.e_begin) return Q_OUT;
+    const bool inside = E >= a.e_begin && E + kQuad <= a.e_end;
+    if (inside && E + kQuad <= pi.vend) return Q_FAST;
+    if (inside && E >= pi.vend && E + kQuad <= pi.end) return Q_PAD;
+    return Q_SLOW;
+}
+
+template <int OP, typename GT, int CAP>
+__device__ __forceinline__ void quad_one(const ShardArgs<CAP>& a, int64_t E, int kind, int p,
+                                         PieceInfo pi) {
+    if (kind == Q_FAST) {
+        const int64_t Ea[1] = {E};
+        const int64_t gs[1] = {a.shard_layout ? E : E + pi.gdelta};
+        const int64_t is[1] = {E + pi.idelta};
+        quads_fast<OP, GT, CAP, 1>(a, Ea, gs, is);
+    } else if (kind == Q_PAD) {
+        quad_pad<OP, CAP>(a, E);
+    } else if (kind == Q_SLOW) {
+        for (int k = 0; k < kQuad; ++k) {
             const int64_t e = E + k;
             if (e < a.e_begin || e >= a.e_end) continue;
             while (e >= pi.end) pi = a.info[++p];
             elem_op<OP, GT, CAP>(a, e, e < pi.vend, pi);
         }
+    }
+}
+
+template <int OP, typename GT, int CAP>
+__global__ __launch_bounds__(kWaveLanes) void shard_kernel(const ShardArgs<CAP> a) {
+    const int lane = threadIdx.x;
+    const int64_t tile = a.tile_first + blockIdx.x;
+    const int64_t E0 = tile * kTile + int64_t(lane) * kQuad;
+    const int64_t E1 = E0 + kHalf;
+    // Wave-uniform bracket of the tile's pieces (scalar loads).
+    const int lo = a.tile[tile];
+    const int hi = a.tile[tile + 1];
+    if (lo == hi) {
+        // Whole tile inside one piece: the common case for large parameters.
+        const PieceInfo pi = a.info[lo];
+        const int k0 = classify(a, E0, pi), k1 = classify(a, E1, pi);
+        if (k0 == Q_FAST && k1 == Q_FAST) {
+            const int64_t Ea[2] = {E0, E1};
+            const int64_t gs[2] = {a.shard_layout ? E0 : E0 + pi.gdelta,
+                                   a.shard_layout ? E1 : E1 + pi.gdelta};
+            const int64_t is[2] = {E0 + pi.idelta, E1 + pi.idelta};
+            quads_fast<OP, GT, CAP, 2>(a, Ea, gs, is);
+        } else {
+            quad_one<OP, GT, CAP>(a, E0, k0, lo, pi);
+            quad_one<OP, GT, CAP>(a, E1, k1, lo, pi);
+        }
+    } else {
+        const int p0 = find_piece(a.e0, lo, hi, E0);
+        const int p1 = find_piece(a.e0, lo, hi, E1);
+        const PieceInfo pi0 = a.info[p0], pi1 = a.info[p1];
+        quad_one<OP, GT, CAP>(a, E0, classify(a, E0, pi0), p0, pi0);
+        quad_one<OP, GT, CAP>(a, E1, classify(a, E1, pi1), p1, pi1);
     }
 }
 
@@ -329,48 +407,51 @@ struct GatherArgs {
     void* out;
 };
 
+// Element groups of 16 bytes: 8 bf16 contiguous per lane, or two fp32 quads
+// per lane (at 4*l and 256 + 4*l), so each instruction stays contiguous.
+template <typename T>
+struct GatherShape {
+    static constexpr int kGroup = 16 / sizeof(T);                       // elements per group
+    static constexpr int kGroups = sizeof(T) == 2 ? 1 : 2;              // groups per lane
+    static constexpr int kStride = sizeof(T) == 2 ? 0 : kHalf;          // between groups
+    static constexpr int kLaneStep = kGroup;                            // lane offset
+};
+
 // out[k] = src[K + delta(piece of K)], K = k_first + k, k < count.
 template <typename T>
-__global__ __launch_bounds__(kBlockThreads) void gather_kernel(const GatherArgs a) {
-    const int lane = threadIdx.x & (kWaveLanes - 1);
-    const int64_t kw = (int64_t(blockIdx.x) * kWavesPerBlock + threadIdx.x / kWaveLanes) * kTile;
-    if (kw >= a.count) return;
-    const int64_t k = kw + int64_t(lane) * kElemsPerLane;
-    if (k >= a.count) return;
-    const int64_t K = a.k_first + k;
+__global__ __launch_bounds__(kWaveLanes) void gather_kernel(const GatherArgs a) {
+    using S = GatherShape<T>;
+    const int lane = threadIdx.x;
+    const int64_t kw = int64_t(blockIdx.x) * kTile;  // local start of the wave's tile
     const int64_t kw_last = a.k_first + min(kw + kTile, a.count) - 1;
-
-    int lo = a.tile[(a.k_first + kw) / kTile];
-    int hi = a.tile[kw_last / kTile + 1];
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (a.k0[mid] <= K) lo = mid;
-        else hi = mid - 1;
-    }
-    int q = lo;
-    int64_t next = a.k0[q + 1];
-    int64_t d = a.delta[q];
+    const int lo = a.tile[(a.k_first + kw) / kTile];
+    const int hi = a.tile[kw_last / kTile + 1];
     const T* src = static_cast<const T*>(a.src);
     T* out = static_cast<T*>(a.out);
-    if (k + kElemsPerLane <= a.count && K + kElemsPerLane <= next) {
-        if constexpr (sizeof(T) == 2) {
-            *reinterpret_cast<u32x4*>(out + k) = ld16u(src + K + d);
+#pragma unroll
+    for (int h = 0; h < S::kGroups; ++h) {
+        const int64_t k = kw + h * S::kStride + int64_t(lane) * S::kLaneStep;
+        if (k >= a.count) continue;
+        const int64_t K = a.k_first + k;
+        int q = lo == hi ? lo : find_piece(a.k0, lo, hi, K);
+        int64_t next = a.k0[q + 1];
+        int64_t d = a.delta[q];
+        if (k + S::kGroup <= a.count && K + S::kGroup <= next) {
+            // src may sit at any element offset; out + k is 16-byte aligned.
+            const u32x4 x = ldnt_x4_a2(reinterpret_cast<const u32x4_a2*>(src + K + d));
+            stnt(reinterpret_cast<u32x4*>(out + k), x);
         } else {
-            u32x4* o = reinterpret_cast<u32x4*>(out + k);
-            o[0] = ld16u(src + K + d);
-            o[1] = ld16u(src + K + d + 4);
-        }
-    } else {
-        for (int i = 0; i < kElemsPerLane; ++i) {
-            const int64_t kk = k + i;
-            if (kk >= a.count) break;
-            const int64_t KK = K + i;
-            while (KK >= next) {
-                ++q;
-                next = a.k0[q + 1];
-                d = a.delta[q];
+            for (int i = 0; i < S::kGroup; ++i) {
+                const int64_t kk = k + i;
+                if (kk >= a.count) break;
+                const int64_t KK = K + i;
+                while (KK >= next) {
+                    ++q;
+                    next = a.k0[q + 1];
+                    d = a.delta[q];
+                }
+                out[kk] = src[KK + d];
             }
-            out[kk] = src[KK + d];
         }
     }
 }
@@ -384,7 +465,7 @@ hipError_t launch_t(const ShardLaunch& L, hipStream_t stream) {
     a.e_begin = L.e_begin;
     a.e_end = L.e_end;
     a.tile_first = L.e_begin / kTile;
-    a.tile_end = (L.e_end + kTile - 1) / kTile;
+    const int64_t tile_end = (L.e_end + kTile - 1) / kTile;
     a.master = L.master;
     a.m = L.m;
     a.v = L.v;
@@ -397,12 +478,11 @@ hipError_t launch_t(const ShardLaunch& L, hipStream_t stream) {
     if constexpr (uses_grads(OP)) {
         for (int r = 0; r < L.nd; ++r) a.grads[r] = L.grads[r];
     }
-    const int64_t waves = a.tile_end - a.tile_first;
-    const int64_t blocks = (waves + kWavesPerBlock - 1) / kWavesPerBlock;
+    const int64_t blocks = tile_end - a.tile_first;  // one wave per tile
     if (blocks <= 0) return hipSuccess;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
     hipLaunchKernelGGL((shard_kernel<OP, GT, CAP>), dim3(static_cast<uint32_t>(blocks)),
-                       dim3(kBlockThreads), 0, stream, a);
+                       dim3(kWaveLanes), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -450,15 +530,14 @@ hipError_t launch_gather(const GatherLaunch& L, zsp_dtype dtype, hipStream_t str
     a.count = L.count;
     a.src = L.src;
     a.out = L.out;
-    const int64_t waves = (L.count + kTile - 1) / kTile;
-    const int64_t blocks = (waves + kWavesPerBlock - 1) / kWavesPerBlock;
+    const int64_t blocks = (L.count + kTile - 1) / kTile;  // one wave per 512 outputs
     if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
     if (dtype == ZSP_BF16)
         hipLaunchKernelGGL(gather_kernel<uint16_t>, dim3(static_cast<uint32_t>(blocks)),
-                           dim3(kBlockThreads), 0, stream, a);
+                           dim3(kWaveLanes), 0, stream, a);
     else
         hipLaunchKernelGGL(gather_kernel<float>, dim3(static_cast<uint32_t>(blocks)),
-                           dim3(kBlockThreads), 0, stream, a);
+                           dim3(kWaveLanes), 0, stream, a);
     return hipGetLastError();
 }
 
