@@ -1,0 +1,197 @@
+"""Parity at the workloads' full sizes, in the launch configuration bench.py
+times (the same Runner builds the plan, binds the state and issues the
+calls).
+
+At these sizes the oracle cannot recompute every element, so each check is
+either on sampled outputs the oracle computes one by one (random positions
+plus the first and last element of many pieces) or a property that holds at
+any size:
+  * copy-in: sampled master/work equal the parameter element the oracle's
+    layout puts there; sampled pad slots are +0;
+  * gather(partition(x)) == x over every element (all-rank workloads);
+  * each step: sampled master, m, v, work after the step equal the oracle's
+    rank-order reduce + Adam of the same inputs (bit-exact expected; the bar
+    is 2 ulp / 1e-6 relative for fp32 state, 1 ulp for bf16); pad slots stay
+    +0;
+  * gather after the step agrees with the sampled work copies.
+The small workload (1000x1003 fp32, N_d = 4) is checked on every element.
+"""
+import numpy as np
+import pytest
+import torch
+
+import bench
+import oracle
+from zero_sharded_mixed_pad_amd import synth
+
+from test_gpu_parity import assert_bf16_close, assert_bits, assert_f32_close, np_of
+
+pytestmark = pytest.mark.gpu
+
+N_SAMPLES = 20000
+
+
+def sample_positions(L, w, rng):
+    """Sample positions in the bound arrays' index space and their layout
+    facts, all from the oracle's tables."""
+    nd, S = w.n_d, L.S
+    local = w.rank_local >= 0
+    total = S if local else nd * S
+    pos = [rng.integers(0, total, size=N_SAMPLES)]
+    # first and last slot of up to 2000 pieces (rank j's slice of tensor t)
+    T = L.T
+    ts = rng.integers(0, T, size=min(2000, T * (1 if local else nd)))
+    js = np.full(ts.size, w.rank_local) if local else rng.integers(0, nd, size=ts.size)
+    base = 0 if local else js * S
+    sl = L.shard_len[ts]
+    ok = sl > 0
+    pos.append((base + L.shard_off[ts])[ok])
+    pos.append((base + L.shard_off[ts] + sl - 1)[ok])
+    E = np.unique(np.concatenate(pos)).astype(np.int64)
+    j = np.full(E.size, w.rank_local) if local else E // S
+    e = E - (0 if local else j * S)
+    t, i = L.locate(e)
+    k = j * L.shard_len[t] + i
+    valid = k < L.numel[t]
+    return dict(E=E, j=j, t=t, k=k, valid=valid, full=L.full_off[t] + k,
+                flat=L.flat_off[t] + k)
+
+
+def take(x, idx):
+    return np_of(x[torch.from_numpy(idx).to(x.device)])
+
+
+def grad_values(r, sp, layout):
+    src = sp["full"] if layout == "full" else sp["E"]
+    src = src[sp["valid"]]
+    return np.stack([take(g, src) for g in r.grads], axis=1)
+
+
+def snapshot(r, E):
+    return [take(x, E) for x in (r.master, r.m, r.v, r.work)]
+
+
+def compare(r, sp, before, g, step, what):
+    w = r.w
+    E, valid = sp["E"], sp["valid"]
+    p, m, v, wk = (x[valid].copy() for x in before)
+    oracle.adam_elems(p, m, v, wk, g, w.lr, w.beta1, w.beta2, w.eps, step)
+    after = snapshot(r, E)
+    worst = max(assert_f32_close(after[0][valid], p, f"{what}/master"),
+                assert_f32_close(after[1][valid], m, f"{what}/m"),
+                assert_f32_close(after[2][valid], v, f"{what}/v"),
+                assert_bf16_close(after[3][valid], wk, f"{what}/work"))
+    for a, b, name in zip(after, before, ("master", "m", "v", "work")):
+        assert_bits(a[~valid], b[~valid], f"{what}/{name} pad slots changed")
+        assert not a[~valid].view(np.uint8).any(), f"{what}/{name} pad slot not +0"
+    return worst, after
+
+
+WORKLOADS = list(synth.workloads())
+
+
+@pytest.mark.parametrize("name", WORKLOADS)
+def test_workload_full_size(name):
+    w = synth.workloads()[name]
+    dev = torch.device("cuda")
+    print(f"\n[workload {name}] setting up", flush=True)
+    r = bench.Runner(w, dev)
+    L = oracle.Layout(w.numel, w.n_d)
+    rng = np.random.default_rng(synth.derive_seed("workload-parity", name))
+    sp = sample_positions(L, w, rng)
+    flat = synth.flat_params(w, device=dev)
+
+    # copy-in on samples
+    st = snapshot(r, sp["E"])
+    valid = sp["valid"]
+    x = take(flat, sp["flat"][valid])
+    x32 = oracle.bf16_to_f32(x) if x.dtype == np.uint16 else x
+    assert_bits(st[0][valid], x32, "copy-in master")
+    want_w = x if x.dtype == np.uint16 else oracle.bf16_rne(x)
+    assert_bits(st[3][valid], want_w, "copy-in work")
+    for a in st:
+        assert not a[~valid].view(np.uint8).any(), "copy-in pad slot not +0"
+    assert not st[1].view(np.uint8).any() and not st[2].view(np.uint8).any()
+
+    # gather(partition(x)) == x over every element
+    if w.rank_local < 0:
+        out = torch.empty(L.total_numel, dtype=torch.float32, device=dev)
+        r.plan.gather_many(0, L.T, out, "master")
+        torch.cuda.synchronize()
+        assert torch.equal(out, flat.float()), "gather(partition(x)) != x (master)"
+        del out
+        outw = torch.empty(L.total_numel, dtype=torch.bfloat16, device=dev)
+        r.plan.gather_many(0, L.T, outw, "work")
+        torch.cuda.synchronize()
+        assert torch.equal(outw, flat.to(torch.bfloat16)), "gather(partition(x)) != x (work)"
+        del outw
+    del flat
+    torch.cuda.empty_cache()
+
+    layout = r.layout
+    steps = w.steps if w.micro_batches == 1 else 2
+    worst = 0
+    for step in range(1, steps + 1):
+        before = snapshot(r, sp["E"])
+        if w.micro_batches == 1:
+            for q, g in enumerate(r.grads):
+                g.copy_(synth.grad_buffer(w, g.numel(), q, step=step, device=dev))
+            vals = grad_values(r, sp, layout)
+            r.step()
+            g = oracle.reduce_values(vals)
+        else:
+            acc = None
+            for mb in range(w.micro_batches):
+                for q, gb in enumerate(r.grads):
+                    gb.copy_(synth.grad_buffer(w, gb.numel(), q, step=step, micro_batch=mb,
+                                               device=dev))
+                vals = grad_values(r, sp, layout)
+                red = oracle.reduce_values(vals)
+                hp = dict(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, step=step)
+                if mb < w.micro_batches - 1:
+                    r.plan.reduce_shard(r.rank, r.grads, layout=layout, accumulate=mb > 0)
+                    acc = red if acc is None else oracle.accumulate(acc, red)
+                else:
+                    r.plan.reduce_adam_step(r.rank, r.grads, layout=layout, use_acc=True, **hp)
+                    g = oracle.accumulate(acc, red)
+            r.step_no = step
+        torch.cuda.synchronize()
+        u, after = compare(r, sp, before, g, step, f"{name} step {step}")
+        worst = max(worst, u)
+        print(f"[workload {name}] step {step}: {int(valid.sum())} sampled elements, "
+              f"max ulp {u}", flush=True)
+        if r.gather_groups and w.micro_batches == 1:
+            # the runner's step ran the gathers after the update
+            for first, n, out, _b in r.gather_groups:
+                lo, hi = L.flat_off[first], L.flat_off[first + n]
+                sel = valid & (sp["flat"] >= lo) & (sp["flat"] < hi)
+                got = take(out, sp["flat"][sel] - lo)
+                assert_bits(got, after[3][sel], "gather after step vs work")
+    assert worst == 0, f"{name}: not bit-exact, max ulp {worst}"
+
+
+def test_small_workload_every_element():
+    """The 1000x1003 fp32 weight at N_d = 4: every element, three steps."""
+    w = synth.workloads()["fp32_1000x1003_nd4"]
+    dev = torch.device("cuda")
+    r = bench.Runner(w, dev)
+    flat = synth.flat_params(w, device=dev)  # the same draw the runner loaded
+    master, work, m, v = oracle.partition(w.numel, w.n_d, np_of(flat))
+    L = oracle.Layout(w.numel, w.n_d)
+    for step in range(1, 4):
+        for q, g in enumerate(r.grads):
+            g.copy_(synth.grad_buffer(w, g.numel(), q, step=step, device=dev))
+        gnp = [np_of(g) for g in r.grads]
+        r.step()
+        for j in range(w.n_d):
+            sl = slice(j * L.S, (j + 1) * L.S)
+            red = oracle.reduce(w.numel, w.n_d, j, gnp)
+            oracle.adam(w.numel, w.n_d, j, master[sl], m[sl], v[sl], work[sl], red, w.lr,
+                        w.beta1, w.beta2, w.eps, step)
+        torch.cuda.synchronize()
+        for name, got, want in (("master", r.master, master), ("m", r.m, m), ("v", r.v, v),
+                                ("work", r.work, work)):
+            assert_bits(np_of(got), want, f"step {step} {name}")
+        first, n, out, _b = r.gather_groups[0]
+        torch.cuda.synchronize()
+        assert_bits(np_of(out), oracle.gather(w.numel, w.n_d, 0, work), f"step {step} gather")
