@@ -33,6 +33,7 @@
 //    hardware round-to-nearest-even convert (v_cvt_pk_bf16_f32).
 #include <hip/hip_runtime.h>
 
+#include <cstddef>
 #include <type_traits>
 
 #include "zsp_internal.hpp"
@@ -78,15 +79,16 @@ __device__ __forceinline__ uint16_t to_bf16(float a) {
     return __builtin_bit_cast(uint16_t, static_cast<__bf16>(a));
 }
 
-// 4 consecutive elements of a bf16 or fp32 source at any element offset.
+// 4 consecutive elements of a bf16 or fp32 source at base[off], any element
+// offset.
 template <typename GT>
-__device__ __forceinline__ void load4(const void* base, int64_t idx, float (&x)[4]) {
+__device__ __forceinline__ void load4(const GT* base, uint32_t off, float (&x)[4]) {
     if constexpr (std::is_same<GT, uint16_t>::value) {
-        const u32x2 u = ldnt_x2_a2(reinterpret_cast<const u32x2_a2*>(static_cast<const uint16_t*>(base) + idx));
+        const u32x2 u = ldnt_x2_a2(reinterpret_cast<const u32x2_a2*>(base + off));
         x[0] = bf_lo(u.x); x[1] = bf_hi(u.x);
         x[2] = bf_lo(u.y); x[3] = bf_hi(u.y);
     } else {
-        const u32x4 u = ldnt_x4_a4(reinterpret_cast<const u32x4_a4*>(static_cast<const float*>(base) + idx));
+        const u32x4 u = ldnt_x4_a4(reinterpret_cast<const u32x4_a4*>(base + off));
         x[0] = __uint_as_float(u.x); x[1] = __uint_as_float(u.y);
         x[2] = __uint_as_float(u.z); x[3] = __uint_as_float(u.w);
     }
@@ -145,6 +147,18 @@ struct ShardArgs {
     const void* grads[CAP];
 };
 
+// Rank r's gradient pointer, read straight from the kernel-argument segment
+// (scalar load; r is wave-uniform). Indexing the by-value argument's array
+// through a reference can make the compiler copy the whole argument into
+// per-lane scratch memory; addressing the segment directly never does. The
+// argument struct is the kernel's only explicit argument, so it starts at
+// offset 0 of the segment.
+template <int CAP>
+__device__ __forceinline__ const void* grad_ptr(int r) {
+    const char* seg = (const char*)__builtin_amdgcn_kernarg_segment_ptr();
+    return reinterpret_cast<const void* const*>(seg + offsetof(ShardArgs<CAP>, grads))[r];
+}
+
 constexpr bool uses_grads(int op) {
     return op == OP_REDUCE_SET || op == OP_REDUCE_ACC || op == OP_FUSED || op == OP_FUSED_ACC;
 }
@@ -154,9 +168,12 @@ constexpr bool reads_acc(int op) {
 constexpr bool is_reduce(int op) { return op == OP_REDUCE_SET || op == OP_REDUCE_ACC; }
 constexpr bool is_adam(int op) { return op == OP_FUSED || op == OP_FUSED_ACC || op == OP_ADAM; }
 
-// Sum over the N_d ranks, in rank order, of NQ quads per lane.
+// Sum over the N_d ranks, in rank order, of NQ quads per lane; quad h of
+// rank r starts at element base[h] + off[h] of grads[r]. When base[] is
+// wave-uniform the address is a scalar base plus a 32-bit lane offset.
 template <typename GT, int CAP, int NQ>
-__device__ __forceinline__ void reduce_quads(const ShardArgs<CAP>& a, const int64_t (&s)[NQ],
+__device__ __forceinline__ void reduce_quads(const ShardArgs<CAP>& a, const int64_t (&base)[NQ],
+                                             const uint32_t (&off)[NQ],
                                              float (&g)[NQ][kQuad]) {
     const int nd = a.nd;
     int r0 = 0;
@@ -165,7 +182,8 @@ __device__ __forceinline__ void reduce_quads(const ShardArgs<CAP>& a, const int6
 #pragma unroll
         for (int q = 0; q < 8; ++q)
 #pragma unroll
-            for (int h = 0; h < NQ; ++h) load4<GT>(a.grads[r0 + q], s[h], x[q][h]);
+            for (int h = 0; h < NQ; ++h)
+                load4<GT>(static_cast<const GT*>(grad_ptr<CAP>(r0 + q)) + base[h], off[h], x[q][h]);
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
             const bool first = (r0 + q) == 0;
@@ -181,7 +199,8 @@ __device__ __forceinline__ void reduce_quads(const ShardArgs<CAP>& a, const int6
         for (int q = 0; q < 8; ++q)
             if (r0 + q < nd)
 #pragma unroll
-                for (int h = 0; h < NQ; ++h) load4<GT>(a.grads[r0 + q], s[h], x[q][h]);
+                for (int h = 0; h < NQ; ++h)
+                load4<GT>(static_cast<const GT*>(grad_ptr<CAP>(r0 + q)) + base[h], off[h], x[q][h]);
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
             if (r0 + q < nd) {
@@ -198,50 +217,54 @@ __device__ __forceinline__ void reduce_quads(const ShardArgs<CAP>& a, const int6
 
 template <typename GT, int CAP>
 __device__ __forceinline__ float reduce1(const ShardArgs<CAP>& a, int64_t sidx) {
-    float g = load1<GT>(a.grads[0], sidx);
-    for (int r = 1; r < a.nd; ++r) g = g + load1<GT>(a.grads[r], sidx);
+    float g = load1<GT>(grad_ptr<CAP>(0), sidx);
+    for (int r = 1; r < a.nd; ++r) g = g + load1<GT>(grad_ptr<CAP>(r), sidx);
     return g;
 }
 
-// NQ quads, each 4 in-range, non-pad elements of one piece. E[h] is a
-// multiple of 4, so every state access is an aligned 16-byte vector;
-// gs[h] / is[h] are the quads' gradient / flat-parameter source indices.
+// NQ quads, each 4 in-range, non-pad elements of one piece. Quad h covers
+// state elements Eb[h] + off[h] ...; its gradient starts at element
+// gb[h] + off[h] of each rank's buffer and its flat parameter at
+// ib[h] + off[h]. Eb[h] + off[h] is a multiple of 4, so every state access is
+// an aligned 16-byte vector. With wave-uniform Eb/gb/ib (a tile inside one
+// piece) every address is a scalar base plus the lane's 32-bit offset.
 template <int OP, typename GT, int CAP, int NQ>
-__device__ __forceinline__ void quads_fast(const ShardArgs<CAP>& a, const int64_t (&E)[NQ],
-                                           const int64_t (&gs)[NQ], const int64_t (&is)[NQ]) {
+__device__ __forceinline__ void quads_fast(const ShardArgs<CAP>& a, const int64_t (&Eb)[NQ],
+                                           const int64_t (&gb)[NQ], const int64_t (&ib)[NQ],
+                                           const uint32_t (&off)[NQ]) {
     if constexpr (OP == OP_COPYIN) {
 #pragma unroll
         for (int h = 0; h < NQ; ++h) {
+            const GT* src = static_cast<const GT*>(a.src) + ib[h];
             float x[kQuad];
-            load4<GT>(a.src, is[h], x);
-            st_f32x4(a.master + E[h], x);
+            load4<GT>(src, off[h], x);
+            st_f32x4(a.master + Eb[h] + off[h], x);
             if constexpr (std::is_same<GT, uint16_t>::value) {
-                const u32x2 raw = ldnt_x2_a2(reinterpret_cast<const u32x2_a2*>(
-                    static_cast<const uint16_t*>(a.src) + is[h]));
-                stnt(reinterpret_cast<u32x2*>(a.work + E[h]), raw);
+                const u32x2 raw = ldnt_x2_a2(reinterpret_cast<const u32x2_a2*>(src + off[h]));
+                stnt(reinterpret_cast<u32x2*>(a.work + Eb[h] + off[h]), raw);
             } else {
-                st_bf16x4(a.work + E[h], x);
+                st_bf16x4(a.work + Eb[h] + off[h], x);
             }
             const float z[kQuad] = {0.0f, 0.0f, 0.0f, 0.0f};
-            st_f32x4(a.m + E[h], z);
-            st_f32x4(a.v + E[h], z);
+            st_f32x4(a.m + Eb[h] + off[h], z);
+            st_f32x4(a.v + Eb[h] + off[h], z);
         }
     } else {
         float p[NQ][kQuad], m[NQ][kQuad], v[NQ][kQuad], c[NQ][kQuad], g[NQ][kQuad];
         if constexpr (is_adam(OP)) {
 #pragma unroll
             for (int h = 0; h < NQ; ++h) {
-                ld_f32x4(a.master + E[h], p[h]);
-                ld_f32x4(a.m + E[h], m[h]);
-                ld_f32x4(a.v + E[h], v[h]);
+                ld_f32x4(a.master + Eb[h] + off[h], p[h]);
+                ld_f32x4(a.m + Eb[h] + off[h], m[h]);
+                ld_f32x4(a.v + Eb[h] + off[h], v[h]);
             }
         }
         if constexpr (reads_acc(OP)) {
 #pragma unroll
-            for (int h = 0; h < NQ; ++h) ld_f32x4(a.acc + E[h], c[h]);
+            for (int h = 0; h < NQ; ++h) ld_f32x4(a.acc + Eb[h] + off[h], c[h]);
         }
         if constexpr (uses_grads(OP)) {
-            reduce_quads<GT, CAP, NQ>(a, gs, g);
+            reduce_quads<GT, CAP, NQ>(a, gb, off, g);
         }
 #pragma unroll
         for (int h = 0; h < NQ; ++h) {
@@ -253,16 +276,16 @@ __device__ __forceinline__ void quads_fast(const ShardArgs<CAP>& a, const int64_
         }
         if constexpr (is_reduce(OP)) {
 #pragma unroll
-            for (int h = 0; h < NQ; ++h) st_f32x4(a.acc + E[h], g[h]);
+            for (int h = 0; h < NQ; ++h) st_f32x4(a.acc + Eb[h] + off[h], g[h]);
         } else {
 #pragma unroll
             for (int h = 0; h < NQ; ++h) {
 #pragma unroll
                 for (int k = 0; k < kQuad; ++k) adam1(p[h][k], m[h][k], v[h][k], g[h][k], a.hp);
-                st_f32x4(a.master + E[h], p[h]);
-                st_f32x4(a.m + E[h], m[h]);
-                st_f32x4(a.v + E[h], v[h]);
-                st_bf16x4(a.work + E[h], p[h]);
+                st_f32x4(a.master + Eb[h] + off[h], p[h]);
+                st_f32x4(a.m + Eb[h] + off[h], m[h]);
+                st_f32x4(a.v + Eb[h] + off[h], v[h]);
+                st_bf16x4(a.work + Eb[h] + off[h], p[h]);
             }
         }
     }
@@ -350,10 +373,11 @@ template <int OP, typename GT, int CAP>
 __device__ __forceinline__ void quad_one(const ShardArgs<CAP>& a, int64_t E, int kind, int p,
                                          PieceInfo pi) {
     if (kind == Q_FAST) {
-        const int64_t Ea[1] = {E};
-        const int64_t gs[1] = {a.shard_layout ? E : E + pi.gdelta};
-        const int64_t is[1] = {E + pi.idelta};
-        quads_fast<OP, GT, CAP, 1>(a, Ea, gs, is);
+        const int64_t Eb[1] = {E};
+        const int64_t gb[1] = {a.shard_layout ? E : E + pi.gdelta};
+        const int64_t ib[1] = {E + pi.idelta};
+        const uint32_t off[1] = {0u};
+        quads_fast<OP, GT, CAP, 1>(a, Eb, gb, ib, off);
     } else if (kind == Q_PAD) {
         quad_pad<OP, CAP>(a, E);
     } else if (kind == Q_SLOW) {
@@ -378,17 +402,21 @@ __global__ __launch_bounds__(kWaveLanes) void shard_kernel(const ShardArgs<CAP> 
     if (lo == hi) {
         // Whole tile inside one piece: the common case for large parameters.
         const PieceInfo pi = a.info[lo];
-        const int k0 = classify(a, E0, pi), k1 = classify(a, E1, pi);
-        if (k0 == Q_FAST && k1 == Q_FAST) {
-            const int64_t Ea[2] = {E0, E1};
-            const int64_t gs[2] = {a.shard_layout ? E0 : E0 + pi.gdelta,
-                                   a.shard_layout ? E1 : E1 + pi.gdelta};
-            const int64_t is[2] = {E0 + pi.idelta, E1 + pi.idelta};
-            quads_fast<OP, GT, CAP, 2>(a, Ea, gs, is);
-        } else {
-            quad_one<OP, GT, CAP>(a, E0, k0, lo, pi);
-            quad_one<OP, GT, CAP>(a, E1, k1, lo, pi);
+        const int64_t T0 = tile * kTile;
+        if (T0 >= a.e_begin && T0 + kTile <= a.e_end && T0 + kTile <= pi.vend) {
+            // Every element real and in range: wave-uniform bases (scalar
+            // registers) plus the lane's 32-bit offsets.
+            const int64_t gbase = a.shard_layout ? T0 : T0 + pi.gdelta;
+            const int64_t Eb[2] = {T0, T0};
+            const int64_t gb[2] = {gbase, gbase};
+            const int64_t ib[2] = {T0 + pi.idelta, T0 + pi.idelta};
+            const uint32_t off[2] = {uint32_t(lane) * kQuad, uint32_t(lane) * kQuad + kHalf};
+            quads_fast<OP, GT, CAP, 2>(a, Eb, gb, ib, off);
+            return;
         }
+        // Tile at a range or pad boundary: one quad at a time.
+        quad_one<OP, GT, CAP>(a, E0, classify(a, E0, pi), lo, pi);
+        quad_one<OP, GT, CAP>(a, E1, classify(a, E1, pi), lo, pi);
     } else {
         const int p0 = find_piece(a.e0, lo, hi, E0);
         const int p1 = find_piece(a.e0, lo, hi, E1);
