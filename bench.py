@@ -63,6 +63,9 @@ def parse():
                     help="also run plain 2 GiB device copies (PMC byte-count calibration)")
     ap.add_argument("--rocprof-summary", metavar="DIR", default=None)
     ap.add_argument("--summary-out", default=None)
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"), default=None,
+                    help="turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of "
+                         "'bench.py --calibrate-copy' into profiles/traffic_<workload>.json")
     return ap.parse_args()
 
 
@@ -296,6 +299,53 @@ def rocprof_summary(d, out):
     print(text)
 
 
+def _counter_rows(d, counter):
+    rows = []
+    for path in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                if row["Counter_Name"] == counter:
+                    rows.append((row["Kernel_Name"], float(row["Counter_Value"])))
+    return rows
+
+
+def traffic_from(fetch_dir, write_dir, workload):
+    """HBM bytes per launch of the fused and gather kernels from PMC counters.
+
+    FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are each scaled by the
+    factor that maps the same counter onto a plain 2 GiB device copy's known
+    2 GiB of reads and 2 GiB of writes."""
+    copy_bytes = float(2 << 30)
+    out = {"workload": workload, "kernel_source_hash": kernel_source_hash(),
+           "calibration": "torch copy_ of a 2 GiB bf16 tensor: 2 GiB read, 2 GiB written"}
+    per = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = _counter_rows(d, counter)
+        copies = [v for n, v in rows if "copy" in n.lower() or "elementwise" in n.lower()]
+        copies = [v for v in copies if v * 1024 > 0.5 * copy_bytes]
+        if not copies:
+            raise SystemExit(f"no calibration copy found among {counter} dispatches")
+        factor = copy_bytes / (sum(copies) / len(copies) * 1024)
+        out[f"{counter}_copy_KiB"] = round(sum(copies) / len(copies), 1)
+        out[f"{counter}_factor"] = round(factor, 4)
+        for n, v in rows:
+            k = _short(n)
+            per.setdefault(k, {}).setdefault(counter, []).append(v * 1024 * factor)
+    for k, d in per.items():
+        if "FETCH_SIZE" in d and "WRITE_SIZE" in d and not k.startswith("at::"):
+            f = sum(d["FETCH_SIZE"]) / len(d["FETCH_SIZE"])
+            w = sum(d["WRITE_SIZE"]) / len(d["WRITE_SIZE"])
+            out.setdefault("kernels", {})[k] = {"read_bytes": int(f), "write_bytes": int(w),
+                                                "bytes_per_launch": int(f + w),
+                                                "dispatches": len(d["FETCH_SIZE"])}
+    fused = [v for k, v in out.get("kernels", {}).items() if k.startswith("fused_reduce_adam_cast")]
+    out["fused_bytes_per_launch"] = fused[0]["bytes_per_launch"] if fused else None
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out, indent=1))
+
+
 def load_traffic(workload):
     """Measured HBM bytes per fused launch from the committed counter summary,
     if it was taken on the current kernel source."""
@@ -315,6 +365,9 @@ def main():
     args = parse()
     if args.rocprof_summary:
         rocprof_summary(args.rocprof_summary, args.summary_out)
+        return 0
+    if args.traffic_from:
+        traffic_from(args.traffic_from[0], args.traffic_from[1], args.workload)
         return 0
     if args.gpus != 1:
         print(f"bench.py runs on one GPU: this build has no multi-GPU path "
