@@ -194,13 +194,15 @@ __device__ __forceinline__ void reduce_quads(const ShardArgs<CAP>& a, const int6
         }
     }
     if (r0 < nd) {
+        // Last, partial batch: every load is issued (ranks past the end
+        // re-read the last rank, a cache hit) so none waits on a branch.
         float x[8][NQ][kQuad];
 #pragma unroll
         for (int q = 0; q < 8; ++q)
-            if (r0 + q < nd)
 #pragma unroll
-                for (int h = 0; h < NQ; ++h)
-                load4<GT>(static_cast<const GT*>(grad_ptr<CAP>(r0 + q)) + base[h], off[h], x[q][h]);
+            for (int h = 0; h < NQ; ++h)
+                load4<GT>(static_cast<const GT*>(grad_ptr<CAP>(min(r0 + q, nd - 1))) + base[h],
+                          off[h], x[q][h]);
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
             if (r0 + q < nd) {
@@ -215,10 +217,19 @@ __device__ __forceinline__ void reduce_quads(const ShardArgs<CAP>& a, const int6
     }
 }
 
+// One element's rank-order sum (per-element path); 8 ranks' loads are issued
+// before their adds.
 template <typename GT, int CAP>
 __device__ __forceinline__ float reduce1(const ShardArgs<CAP>& a, int64_t sidx) {
-    float g = load1<GT>(grad_ptr<CAP>(0), sidx);
-    for (int r = 1; r < a.nd; ++r) g = g + load1<GT>(grad_ptr<CAP>(r), sidx);
+    float g = 0.0f;
+    for (int r0 = 0; r0 < a.nd; r0 += 8) {
+        float x[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) x[q] = load1<GT>(grad_ptr<CAP>(min(r0 + q, a.nd - 1)), sidx);
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+            if (r0 + q < a.nd) g = (r0 + q == 0) ? x[q] : g + x[q];
+    }
     return g;
 }
 
@@ -348,10 +359,24 @@ __device__ __forceinline__ void elem_op(const ShardArgs<CAP>& a, int64_t e, bool
     }
 }
 
-enum QuadKind : int { Q_OUT = 0, Q_FAST = 1, Q_PAD = 2, Q_SLOW = 3 };
+// OUT: no element in range. FAST: 4 real elements of one piece, in range.
+// PAD: 4 pad elements of one piece, in range. MIXED: in range, crossing a
+// piece or pad boundary. SLOW: crossing the call's range boundary.
+enum QuadKind : int { Q_OUT = 0, Q_FAST = 1, Q_PAD = 2, Q_SLOW = 3, Q_MIXED = 4 };
 
-// Piece holding element E, searched inside the tile's bracket [lo, hi].
-__device__ __forceinline__ int find_piece(const int64_t* e0, int lo, int hi, int64_t E) {
+// Pieces of one tile, indexed from 0 (entry i is piece lo + i of the
+// table): either the global table offset by lo, or a copy staged in LDS.
+// Up to this many are staged; a tile holding more (parameters of a few
+// elements per rank) searches the global table.
+constexpr int kStage = 128;
+// Tiles with fewer pieces than this search the global table directly (one or
+// two cached loads); staging pays off only for more.
+constexpr int kStageMin = 2;
+
+// Local index of the piece holding element E among the n pieces whose starts
+// are e0[0..n).
+__device__ __forceinline__ int find_local(const int64_t* e0, int n, int64_t E) {
+    int lo = 0, hi = n - 1;
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
         if (e0[mid] <= E) lo = mid;
@@ -364,14 +389,120 @@ template <int CAP>
 __device__ __forceinline__ int classify(const ShardArgs<CAP>& a, int64_t E, const PieceInfo& pi) {
     if (E >= a.e_end || E + kQuad <= a.e_begin) return Q_OUT;
     const bool inside = E >= a.e_begin && E + kQuad <= a.e_end;
-    if (inside && E + kQuad <= pi.vend) return Q_FAST;
-    if (inside && E >= pi.vend && E + kQuad <= pi.end) return Q_PAD;
-    return Q_SLOW;
+    if (!inside) return Q_SLOW;
+    if (E + kQuad <= pi.vend) return Q_FAST;
+    if (E >= pi.vend && E + kQuad <= pi.end) return Q_PAD;
+    return Q_MIXED;
 }
 
+// A quad inside the call's range whose elements are not all real elements
+// of one piece: it crosses a piece boundary or the pad boundary. The state is
+// still one aligned 16-byte vector per stream; each element finds its piece,
+// all ranks' gradient loads of the 4 elements are issued together, and pad
+// elements keep their state bit for bit (they are loaded and stored back).
+template <int OP, typename GT, int CAP>
+__device__ __forceinline__ void quad_mixed(const ShardArgs<CAP>& a, int64_t E, int p, PieceInfo pi,
+                                           const PieceInfo* info) {
+    // Pad elements read element 0 of the same buffer instead (always valid
+    // memory, value discarded), so that every load is issued unconditionally:
+    // loads under a per-lane condition each get their own wait.
+    bool valid[kQuad];
+    int64_t gs[kQuad], is[kQuad];
+#pragma unroll
+    for (int k = 0; k < kQuad; ++k) {
+        const int64_t e = E + k;
+        while (e >= pi.end) pi = info[++p];
+        valid[k] = e < pi.vend;
+        gs[k] = valid[k] ? (a.shard_layout ? e : e + pi.gdelta) : 0;
+        is[k] = valid[k] ? e + pi.idelta : 0;
+    }
+    if constexpr (OP == OP_COPYIN) {
+        float x[kQuad];
+        uint32_t w[kQuad];
+#pragma unroll
+        for (int k = 0; k < kQuad; ++k) {
+            const float xk = load1<GT>(a.src, is[k]);
+            x[k] = valid[k] ? xk : 0.0f;
+            if constexpr (std::is_same<GT, uint16_t>::value)
+                w[k] = valid[k] ? (__float_as_uint(xk) >> 16) : 0u;
+            else
+                w[k] = to_bf16(x[k]);
+        }
+        st_f32x4(a.master + E, x);
+        stnt(reinterpret_cast<u32x2*>(a.work + E), u32x2{w[0] | (w[1] << 16), w[2] | (w[3] << 16)});
+        const float z[kQuad] = {0.0f, 0.0f, 0.0f, 0.0f};
+        st_f32x4(a.m + E, z);
+        st_f32x4(a.v + E, z);
+    } else {
+        float p4[kQuad], m4[kQuad], v4[kQuad], c4[kQuad], g[kQuad];
+        u32x2 w_old{0u, 0u};
+        if constexpr (is_adam(OP)) {
+            ld_f32x4(a.master + E, p4);
+            ld_f32x4(a.m + E, m4);
+            ld_f32x4(a.v + E, v4);
+            w_old = *reinterpret_cast<const u32x2*>(a.work + E);
+        }
+        if constexpr (reads_acc(OP)) ld_f32x4(a.acc + E, c4);
+        if constexpr (uses_grads(OP)) {
+#pragma unroll
+            for (int k = 0; k < kQuad; ++k) g[k] = 0.0f;
+            for (int r0 = 0; r0 < a.nd; r0 += 8) {
+                float x[8][kQuad];
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    const void* gp = grad_ptr<CAP>(min(r0 + q, a.nd - 1));
+#pragma unroll
+                    for (int k = 0; k < kQuad; ++k) {
+                        const float xk = load1<GT>(gp, gs[k]);
+                        x[q][k] = valid[k] ? xk : 0.0f;
+                    }
+                }
+#pragma unroll
+                for (int q = 0; q < 8; ++q)
+                    if (r0 + q < a.nd)
+#pragma unroll
+                        for (int k = 0; k < kQuad; ++k)
+                            g[k] = (r0 + q == 0) ? x[q][k] : g[k] + x[q][k];
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < kQuad; ++k) {
+            if constexpr (OP == OP_ADAM) g[k] = c4[k];
+            else if constexpr (reads_acc(OP)) g[k] = c4[k] + g[k];
+        }
+        if constexpr (is_reduce(OP)) {
+            float r[kQuad];
+#pragma unroll
+            for (int k = 0; k < kQuad; ++k) r[k] = valid[k] ? g[k] : 0.0f;
+            st_f32x4(a.acc + E, r);
+        } else {
+#pragma unroll
+            for (int k = 0; k < kQuad; ++k) {
+                float pk = p4[k], mk = m4[k], vk = v4[k];
+                adam1(pk, mk, vk, g[k], a.hp);
+                if (valid[k]) {
+                    p4[k] = pk;
+                    m4[k] = mk;
+                    v4[k] = vk;
+                }
+            }
+            const uint32_t wn0 = pack_bf16(p4[0], p4[1]), wn1 = pack_bf16(p4[2], p4[3]);
+            const uint32_t lo0 = valid[0] ? (wn0 & 0xffffu) : (w_old.x & 0xffffu);
+            const uint32_t hi0 = valid[1] ? (wn0 & 0xffff0000u) : (w_old.x & 0xffff0000u);
+            const uint32_t lo1 = valid[2] ? (wn1 & 0xffffu) : (w_old.y & 0xffffu);
+            const uint32_t hi1 = valid[3] ? (wn1 & 0xffff0000u) : (w_old.y & 0xffff0000u);
+            st_f32x4(a.master + E, p4);
+            st_f32x4(a.m + E, m4);
+            st_f32x4(a.v + E, v4);
+            stnt(reinterpret_cast<u32x2*>(a.work + E), u32x2{lo0 | hi0, lo1 | hi1});
+        }
+    }
+}
+
+// One quad of any kind; p is the index of its piece in `info`.
 template <int OP, typename GT, int CAP>
 __device__ __forceinline__ void quad_one(const ShardArgs<CAP>& a, int64_t E, int kind, int p,
-                                         PieceInfo pi) {
+                                         PieceInfo pi, const PieceInfo* info) {
     if (kind == Q_FAST) {
         const int64_t Eb[1] = {E};
         const int64_t gb[1] = {a.shard_layout ? E : E + pi.gdelta};
@@ -380,11 +511,15 @@ __device__ __forceinline__ void quad_one(const ShardArgs<CAP>& a, int64_t E, int
         quads_fast<OP, GT, CAP, 1>(a, Eb, gb, ib, off);
     } else if (kind == Q_PAD) {
         quad_pad<OP, CAP>(a, E);
+    } else if (kind == Q_MIXED) {
+        quad_mixed<OP, GT, CAP>(a, E, p, pi, info);
     } else if (kind == Q_SLOW) {
+        // Only quads that cross the call's range boundary: element by element,
+        // touching nothing outside the range.
         for (int k = 0; k < kQuad; ++k) {
             const int64_t e = E + k;
             if (e < a.e_begin || e >= a.e_end) continue;
-            while (e >= pi.end) pi = a.info[++p];
+            while (e >= pi.end) pi = info[++p];
             elem_op<OP, GT, CAP>(a, e, e < pi.vend, pi);
         }
     }
@@ -392,10 +527,11 @@ __device__ __forceinline__ void quad_one(const ShardArgs<CAP>& a, int64_t E, int
 
 template <int OP, typename GT, int CAP>
 __global__ __launch_bounds__(kWaveLanes) void shard_kernel(const ShardArgs<CAP> a) {
+    __shared__ int64_t s_e0[kStage];
+    __shared__ PieceInfo s_info[kStage];
     const int lane = threadIdx.x;
     const int64_t tile = a.tile_first + blockIdx.x;
     const int64_t E0 = tile * kTile + int64_t(lane) * kQuad;
-    const int64_t E1 = E0 + kHalf;
     // Wave-uniform bracket of the tile's pieces (scalar loads).
     const int lo = a.tile[tile];
     const int hi = a.tile[tile + 1];
@@ -414,15 +550,29 @@ __global__ __launch_bounds__(kWaveLanes) void shard_kernel(const ShardArgs<CAP> 
             quads_fast<OP, GT, CAP, 2>(a, Eb, gb, ib, off);
             return;
         }
-        // Tile at a range or pad boundary: one quad at a time.
-        quad_one<OP, GT, CAP>(a, E0, classify(a, E0, pi), lo, pi);
-        quad_one<OP, GT, CAP>(a, E1, classify(a, E1, pi), lo, pi);
-    } else {
-        const int p0 = find_piece(a.e0, lo, hi, E0);
-        const int p1 = find_piece(a.e0, lo, hi, E1);
-        const PieceInfo pi0 = a.info[p0], pi1 = a.info[p1];
-        quad_one<OP, GT, CAP>(a, E0, classify(a, E0, pi0), p0, pi0);
-        quad_one<OP, GT, CAP>(a, E1, classify(a, E1, pi1), p1, pi1);
+    }
+    // A tile at a piece, pad or range boundary. Several pieces: stage their
+    // table in LDS with one coalesced load and search it there. The two quads
+    // go through one call site (a loop kept rolled): each copy of the update
+    // is long, and fewer copies keep the kernel within the instruction cache.
+    const int n = hi - lo + 1;
+    const int64_t* e0 = a.e0 + lo;
+    const PieceInfo* info = a.info + lo;
+    if (n >= kStageMin && n <= kStage) {
+        for (int i = lane; i < n; i += kWaveLanes) {
+            s_e0[i] = e0[i];
+            s_info[i] = info[i];
+        }
+        __syncthreads();
+        e0 = s_e0;
+        info = s_info;
+    }
+#pragma unroll 1
+    for (int h = 0; h < 2; ++h) {
+        const int64_t E = E0 + h * kHalf;
+        const int p = n == 1 ? 0 : find_local(e0, n, E);
+        const PieceInfo pi = info[p];
+        quad_one<OP, GT, CAP>(a, E, classify(a, E, pi), p, pi, info);
     }
 }
 
@@ -449,25 +599,68 @@ struct GatherShape {
 template <typename T>
 __global__ __launch_bounds__(kWaveLanes) void gather_kernel(const GatherArgs a) {
     using S = GatherShape<T>;
+    __shared__ int64_t s_k0[kStage + 1];
+    __shared__ int64_t s_delta[kStage];
     const int lane = threadIdx.x;
     const int64_t kw = int64_t(blockIdx.x) * kTile;  // local start of the wave's tile
     const int64_t kw_last = a.k_first + min(kw + kTile, a.count) - 1;
     const int lo = a.tile[(a.k_first + kw) / kTile];
     const int hi = a.tile[kw_last / kTile + 1];
+    const int n = hi - lo + 1;
     const T* src = static_cast<const T*>(a.src);
     T* out = static_cast<T*>(a.out);
+    const int64_t* k0 = a.k0 + lo;
+    const int64_t* delta = a.delta + lo;
+    if (n == 1) {
+        const int64_t next = k0[1], d = delta[0];
+        if (kw + kTile <= a.count && a.k_first + kw + kTile <= next) {
+            // The whole tile is one run of one rank's slice: scalar bases plus
+            // the lane's 32-bit offsets.
+            const T* sb = src + (a.k_first + kw + d);
+            T* ob = out + kw;
+#pragma unroll
+            for (int h = 0; h < S::kGroups; ++h) {
+                const uint32_t o = h * S::kStride + uint32_t(lane) * S::kLaneStep;
+                stnt(reinterpret_cast<u32x4*>(ob + o),
+                     ldnt_x4_a2(reinterpret_cast<const u32x4_a2*>(sb + o)));
+            }
+            return;
+        }
+    } else if (n >= kStageMin && n <= kStage) {
+        // Several pieces: stage their starts and deltas in LDS.
+        for (int i = lane; i <= n; i += kWaveLanes) s_k0[i] = k0[i];
+        for (int i = lane; i < n; i += kWaveLanes) s_delta[i] = delta[i];
+        __syncthreads();
+        k0 = s_k0;
+        delta = s_delta;
+    }
 #pragma unroll
     for (int h = 0; h < S::kGroups; ++h) {
         const int64_t k = kw + h * S::kStride + int64_t(lane) * S::kLaneStep;
         if (k >= a.count) continue;
         const int64_t K = a.k_first + k;
-        int q = lo == hi ? lo : find_piece(a.k0, lo, hi, K);
-        int64_t next = a.k0[q + 1];
-        int64_t d = a.delta[q];
+        int q = n == 1 ? 0 : find_local(k0, n, K);
+        int64_t next = k0[q + 1];
+        int64_t d = delta[q];
         if (k + S::kGroup <= a.count && K + S::kGroup <= next) {
             // src may sit at any element offset; out + k is 16-byte aligned.
             const u32x4 x = ldnt_x4_a2(reinterpret_cast<const u32x4_a2*>(src + K + d));
             stnt(reinterpret_cast<u32x4*>(out + k), x);
+        } else if (k + S::kGroup <= a.count) {
+            // The group crosses piece boundaries: find each element's source,
+            // issue all loads, then one aligned 16-byte store.
+            T x[S::kGroup];
+#pragma unroll
+            for (int i = 0; i < S::kGroup; ++i) {
+                const int64_t KK = K + i;
+                while (KK >= next) {
+                    ++q;
+                    next = k0[q + 1];
+                    d = delta[q];
+                }
+                x[i] = src[KK + d];
+            }
+            stnt(reinterpret_cast<u32x4*>(out + k), __builtin_bit_cast(u32x4, x));
         } else {
             for (int i = 0; i < S::kGroup; ++i) {
                 const int64_t kk = k + i;
@@ -475,8 +668,8 @@ __global__ __launch_bounds__(kWaveLanes) void gather_kernel(const GatherArgs a) 
                 const int64_t KK = K + i;
                 while (KK >= next) {
                     ++q;
-                    next = a.k0[q + 1];
-                    d = a.delta[q];
+                    next = k0[q + 1];
+                    d = delta[q];
                 }
                 out[kk] = src[KK + d];
             }
