@@ -595,6 +595,11 @@ struct GatherShape {
     static constexpr int kLaneStep = kGroup;                            // lane offset
 };
 
+// Tiles of the gather holding at most this many pieces read the pieces'
+// starts and deltas with wave-uniform scalar loads and pick per lane with
+// register selects: one scalar round trip, like a single-piece tile.
+constexpr int kPick = 8;
+
 // out[k] = src[K + delta(piece of K)], K = k_first + k, k < count.
 template <typename T>
 __global__ __launch_bounds__(kWaveLanes) void gather_kernel(const GatherArgs a) {
@@ -626,8 +631,60 @@ __global__ __launch_bounds__(kWaveLanes) void gather_kernel(const GatherArgs a) 
             }
             return;
         }
-    } else if (n >= kStageMin && n <= kStage) {
-        // Several pieces: stage their starts and deltas in LDS.
+    }
+    if (n <= kPick) {
+        // Few pieces: starts and deltas in scalar registers (indices clamped
+        // so no load passes the table's end), picked per element by selects.
+        int64_t sk[kPick + 1], sd[kPick];
+#pragma unroll
+        for (int i = 0; i <= kPick; ++i) sk[i] = k0[min(i, n)];
+#pragma unroll
+        for (int i = 0; i < kPick; ++i) sd[i] = delta[min(i, n - 1)];
+        // next start and delta of the piece holding element K
+        auto pick = [&](int64_t K, int64_t& next, int64_t& d) {
+            next = sk[1];
+            d = sd[0];
+#pragma unroll
+            for (int i = 1; i < kPick; ++i) {
+                const bool c = i < n && sk[i] <= K;
+                next = c ? sk[i + 1] : next;
+                d = c ? sd[i] : d;
+            }
+        };
+#pragma unroll
+        for (int h = 0; h < S::kGroups; ++h) {
+            const int64_t k = kw + h * S::kStride + int64_t(lane) * S::kLaneStep;
+            if (k >= a.count) continue;
+            const int64_t K = a.k_first + k;
+            int64_t next, d;
+            pick(K, next, d);
+            if (k + S::kGroup <= a.count && K + S::kGroup <= next) {
+                stnt(reinterpret_cast<u32x4*>(out + k),
+                     ldnt_x4_a2(reinterpret_cast<const u32x4_a2*>(src + K + d)));
+            } else {
+                // Crosses a piece boundary or the end: each element picks its
+                // own piece; every load is issued unconditionally.
+                T x[S::kGroup];
+#pragma unroll
+                for (int i = 0; i < S::kGroup; ++i) {
+                    const int64_t KK = min(K + i, a.k_first + a.count - 1);
+                    int64_t nx, di;
+                    pick(KK, nx, di);
+                    x[i] = src[KK + di];
+                }
+                if (k + S::kGroup <= a.count) {
+                    stnt(reinterpret_cast<u32x4*>(out + k), __builtin_bit_cast(u32x4, x));
+                } else {
+#pragma unroll
+                    for (int i = 0; i < S::kGroup; ++i)
+                        if (k + i < a.count) out[k + i] = x[i];
+                }
+            }
+        }
+        return;
+    }
+    if (n <= kStage) {
+        // Many pieces: stage their starts and deltas in LDS.
         for (int i = lane; i <= n; i += kWaveLanes) s_k0[i] = k0[i];
         for (int i = lane; i < n; i += kWaveLanes) s_delta[i] = delta[i];
         __syncthreads();
@@ -639,28 +696,13 @@ __global__ __launch_bounds__(kWaveLanes) void gather_kernel(const GatherArgs a) 
         const int64_t k = kw + h * S::kStride + int64_t(lane) * S::kLaneStep;
         if (k >= a.count) continue;
         const int64_t K = a.k_first + k;
-        int q = n == 1 ? 0 : find_local(k0, n, K);
+        int q = find_local(k0, n, K);
         int64_t next = k0[q + 1];
         int64_t d = delta[q];
         if (k + S::kGroup <= a.count && K + S::kGroup <= next) {
             // src may sit at any element offset; out + k is 16-byte aligned.
             const u32x4 x = ldnt_x4_a2(reinterpret_cast<const u32x4_a2*>(src + K + d));
             stnt(reinterpret_cast<u32x4*>(out + k), x);
-        } else if (k + S::kGroup <= a.count) {
-            // The group crosses piece boundaries: find each element's source,
-            // issue all loads, then one aligned 16-byte store.
-            T x[S::kGroup];
-#pragma unroll
-            for (int i = 0; i < S::kGroup; ++i) {
-                const int64_t KK = K + i;
-                while (KK >= next) {
-                    ++q;
-                    next = k0[q + 1];
-                    d = delta[q];
-                }
-                x[i] = src[KK + d];
-            }
-            stnt(reinterpret_cast<u32x4*>(out + k), __builtin_bit_cast(u32x4, x));
         } else {
             for (int i = 0; i < S::kGroup; ++i) {
                 const int64_t kk = k + i;
