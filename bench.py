@@ -35,15 +35,23 @@ HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, AMD's published figure
 DEFAULT_WORKLOAD = "llama7b_layer_nd8"
 METRIC = "effective GB/s (and % HBM peak) of shard reduce+Adam+cast step and param gather"
 KERNEL_SOURCES = ["zero_sharded_mixed_pad_amd/csrc/zsp_kernels.hip",
-                  "zero_sharded_mixed_pad_amd/csrc/zsp_internal.hpp",
-                  "zero_sharded_mixed_pad_amd/_build.py"]
+                  "zero_sharded_mixed_pad_amd/csrc/zsp_internal.hpp"]
 
 
 def kernel_source_hash():
+    """Hash of what determines the kernels' code: their source, its header and
+    the device compile flags (other library sources do not enter it)."""
+    import importlib.util
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
+    spec = importlib.util.spec_from_file_location(
+        "_zsp_build_flags", os.path.join(ROOT, "zero_sharded_mixed_pad_amd", "_build.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    flags = [f for f in mod.FLAGS if not f.startswith("/")]
+    h.update(repr((mod.ARCH, flags)).encode())
     return h.hexdigest()[:16]
 
 

@@ -74,7 +74,8 @@ typedef enum {
     ZSP_ERANGE = -2, /* index or size out of the supported range */
     ZSP_ENOMEM = -3, /* host or device allocation for the plan's tables failed */
     ZSP_EHIP = -4,   /* a HIP runtime call or kernel launch failed */
-    ZSP_ESTATE = -5  /* call not valid in the plan's current binding/device */
+    ZSP_ESTATE = -5, /* call not valid in the plan's current binding/device */
+    ZSP_EIO = -6     /* checkpoint file missing, unreadable, corrupt or of another model */
 } zsp_status;
 
 typedef enum { ZSP_F32 = 0, ZSP_BF16 = 1 } zsp_dtype;
@@ -191,6 +192,46 @@ zsp_status zsp_gather(zsp_plan* plan, int32_t param_id, zsp_source src, void* ou
  * flat_off[t] - flat_off[first_param]. */
 zsp_status zsp_gather_many(zsp_plan* plan, int32_t first_param, int32_t n_params,
                            zsp_source src, void* out, void* stream);
+
+/* ---- Sharded checkpoint, resume and reshard ------------------------------
+ * [ZST] "Where the shards live and what happens on failure": each rank
+ * writes its own shard set together with the layout it was cut with; loading
+ * under a different rank count reshuffles the shards; the consistent point is
+ * between steps (the gradient accumulator is not saved).
+ * A checkpoint is a directory holding one file per rank,
+ * "rank-<r>-of-<n_d>.zsp": a header (magic "ZSPCKPT1", n_d, rank, number of
+ * parameters, S, step), the numel list, master[S], m[S], v[S] (fp32), work[S]
+ * (bf16 bits), and an FNV-1a hash of all of it. The directory must exist. */
+
+/* Write rank `rank`'s shard set from host arrays of S elements each. Host
+ * only. Files are written under a temporary name and renamed. */
+zsp_status zsp_checkpoint_write_host(const zsp_plan* plan, int32_t rank, const char* dir,
+                                     int64_t step, const float* master, const float* m,
+                                     const float* v, const uint16_t* work);
+
+/* Read rank `rank`'s shard set for this plan's layout into host arrays of S
+ * elements each; *step receives the saved step. If the checkpoint was written
+ * with another rank count, every one of its rank files is read and the shard
+ * is rebuilt for this plan (element k of parameter t comes from old rank
+ * k / s_old, pads are +0): a reshard, bit-exact. The saved numel list must
+ * equal the plan's, else ZSP_EIO. Host only. */
+zsp_status zsp_checkpoint_read_host(const zsp_plan* plan, int32_t rank, const char* dir,
+                                    int64_t* step, float* master, float* m, float* v,
+                                    uint16_t* work);
+
+/* Save the bound state of one rank or of every bound rank
+ * (ZSP_ALL_RANKS) to `dir`. Waits for `stream` first, so everything already
+ * enqueued on it is included; returns after the files are written. */
+zsp_status zsp_checkpoint_save(zsp_plan* plan, int32_t rank_or_all, const char* dir,
+                               int64_t step, void* stream);
+
+/* Load one rank or every bound rank from `dir` into the bound state,
+ * resharding if the checkpoint has another rank count; *step receives the
+ * saved step. The copies are ordered on `stream` and complete before the
+ * call returns. Restoring only rank r (e.g. after losing it) leaves the other
+ * ranks' state untouched. */
+zsp_status zsp_checkpoint_load(zsp_plan* plan, int32_t rank_or_all, const char* dir,
+                               int64_t* step, void* stream);
 
 /* Message for the calling thread's most recent failed call ("" if none). */
 const char* zsp_last_error(void);

@@ -303,7 +303,8 @@ def test_rank_local_binding(layout):
             M.o_adam(j, M.o_reduce(j, grads, layout), step)
             assert M.check_state(f"rank-local {j} step {step}") == 0
         with pytest.raises(zsp.ZspError) as e:
-            M.plan.reduce_adam_step((j + 1) % nd, [g.to(dev()) for g in grads], step=3, **HP)
+            M.plan.reduce_adam_step((j + 1) % nd, [g.to(dev()) for g in grads], step=3,
+                                    layout=layout, **HP)
         assert e.value.status == zsp.binding.ESTATE
         out = torch.empty(64, dtype=torch.bfloat16, device=dev())
         with pytest.raises(zsp.ZspError) as e:

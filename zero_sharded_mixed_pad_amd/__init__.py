@@ -10,7 +10,8 @@ include/zsp.h; this package is its thin ctypes binding.
 """
 from .binding import (  # noqa: F401
     ALL_RANKS, BF16, F32, GRADS_FULL, GRADS_SHARD, MAX_RANKS, SRC_MASTER, SRC_WORK, Plan,
-    ZspError, last_error, partition, zsp_adam_step, zsp_bind_state, zsp_destroy, zsp_gather,
+    ZspError, last_error, partition, zsp_adam_step, zsp_bind_state, zsp_checkpoint_load,
+    zsp_checkpoint_read_host, zsp_checkpoint_save, zsp_checkpoint_write_host, zsp_destroy, zsp_gather,
     zsp_gather_many, zsp_load_params, zsp_partition, zsp_plan_info, zsp_plan_tensor,
     zsp_reduce_adam_step, zsp_reduce_shard,
 )

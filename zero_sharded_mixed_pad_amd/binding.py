@@ -13,7 +13,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libzsp.so")
 
-OK, EINVAL, ERANGE, ENOMEM, EHIP, ESTATE = 0, -1, -2, -3, -4, -5
+OK, EINVAL, ERANGE, ENOMEM, EHIP, ESTATE, EIO = 0, -1, -2, -3, -4, -5, -6
 F32, BF16 = 0, 1
 GRADS_FULL, GRADS_SHARD = 0, 1
 SRC_WORK, SRC_MASTER = 0, 1
@@ -21,7 +21,7 @@ ALL_RANKS = -1
 MAX_RANKS = 256
 
 _STATUS_NAMES = {EINVAL: "ZSP_EINVAL", ERANGE: "ZSP_ERANGE", ENOMEM: "ZSP_ENOMEM",
-                 EHIP: "ZSP_EHIP", ESTATE: "ZSP_ESTATE"}
+                 EHIP: "ZSP_EHIP", ESTATE: "ZSP_ESTATE", EIO: "ZSP_EIO"}
 
 
 class ZspError(RuntimeError):
@@ -51,6 +51,10 @@ def _load():
                                        vp]),
         "zsp_gather": (i32, [vp, i32, i32, vp, vp]),
         "zsp_gather_many": (i32, [vp, i32, i32, i32, vp, vp]),
+        "zsp_checkpoint_write_host": (i32, [vp, i32, ctypes.c_char_p, i64, vp, vp, vp, vp]),
+        "zsp_checkpoint_read_host": (i32, [vp, i32, ctypes.c_char_p, i64p, vp, vp, vp, vp]),
+        "zsp_checkpoint_save": (i32, [vp, i32, ctypes.c_char_p, i64, vp]),
+        "zsp_checkpoint_load": (i32, [vp, i32, ctypes.c_char_p, i64p, vp]),
         "zsp_last_error": (ctypes.c_char_p, []),
     }
     for name, (res, args) in sigs.items():
@@ -102,12 +106,21 @@ def _dtype_code(t):
     raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
 
 
-def _grad_array(grads, n_d):
+def _grad_array(grads, n_d, min_elems=0):
     if len(grads) != n_d:
         raise ValueError(f"need {n_d} gradient buffers, got {len(grads)}")
     dt = grads[0].dtype
+    for i, g in enumerate(grads):
+        if isinstance(g, torch.Tensor) and g.numel() < min_elems:
+            raise ValueError(f"grads[{i}] holds {g.numel()} elements; this layout reads "
+                             f"{min_elems}")
     ptrs = [_ptr(g, dt, f"grads[{i}]").value for i, g in enumerate(grads)]
     return (ctypes.c_void_p * n_d)(*ptrs), _dtype_code(grads[0])
+
+
+def _need(t, n, what):
+    if t is not None and t.numel() < n:
+        raise ValueError(f"{what} holds {t.numel()} elements; {n} are needed")
 
 
 _LAYOUTS = {"full": GRADS_FULL, "shard": GRADS_SHARD, GRADS_FULL: GRADS_FULL,
@@ -155,8 +168,9 @@ def zsp_load_params(h, flat, stream=None):
                                _stream(stream)))
 
 
-def zsp_reduce_shard(h, n_d, rank, grads, layout="full", accumulate=False, stream=None):
-    arr, code = _grad_array(grads, n_d)
+def zsp_reduce_shard(h, n_d, rank, grads, layout="full", accumulate=False, stream=None,
+                     min_elems=0):
+    arr, code = _grad_array(grads, n_d, min_elems)
     _check(lib.zsp_reduce_shard(h, int(rank), arr, code, _LAYOUTS[layout], int(bool(accumulate)),
                                 _stream(stream)))
 
@@ -167,8 +181,8 @@ def zsp_adam_step(h, rank, lr, beta1, beta2, eps, step, stream=None):
 
 
 def zsp_reduce_adam_step(h, n_d, rank, grads, lr, beta1, beta2, eps, step, layout="full",
-                         use_acc=False, stream=None):
-    arr, code = _grad_array(grads, n_d)
+                         use_acc=False, stream=None, min_elems=0):
+    arr, code = _grad_array(grads, n_d, min_elems)
     _check(lib.zsp_reduce_adam_step(h, int(rank), arr, code, _LAYOUTS[layout],
                                     int(bool(use_acc)), float(lr), float(beta1), float(beta2),
                                     float(eps), int(step), _stream(stream)))
@@ -187,6 +201,47 @@ def zsp_gather_many(h, first, n, out, source="work", stream=None):
                                _stream(stream)))
 
 
+def _host_arrays(S, master, m, v, work, writable):
+    import numpy as np
+    out = []
+    for a, dt, name in ((master, np.float32, "master"), (m, np.float32, "m"),
+                        (v, np.float32, "v"), (work, np.uint16, "work")):
+        if not isinstance(a, np.ndarray) or a.dtype != dt or not a.flags.c_contiguous:
+            raise TypeError(f"{name} must be a contiguous numpy {dt.__name__} array")
+        if a.size < S or (writable and not a.flags.writeable):
+            raise ValueError(f"{name} must hold {S} elements" + (" and be writable" if writable else ""))
+        out.append(ctypes.c_void_p(a.ctypes.data))
+    return out
+
+
+def zsp_checkpoint_write_host(h, rank, directory, step, master, m, v, work):
+    """Write one rank's shard set from host numpy arrays (float32 x3, uint16 bf16 bits)."""
+    S = zsp_plan_info(h)["shard_elems"]
+    _check(lib.zsp_checkpoint_write_host(h, int(rank), str(directory).encode(), int(step),
+                                         *_host_arrays(S, master, m, v, work, False)))
+
+
+def zsp_checkpoint_read_host(h, rank, directory, master, m, v, work):
+    """Read (resharding if needed) one rank's shard set into host numpy arrays; returns step."""
+    S = zsp_plan_info(h)["shard_elems"]
+    step = ctypes.c_int64()
+    _check(lib.zsp_checkpoint_read_host(h, int(rank), str(directory).encode(), ctypes.byref(step),
+                                        *_host_arrays(S, master, m, v, work, True)))
+    return step.value
+
+
+def zsp_checkpoint_save(h, rank, directory, step, stream=None):
+    _check(lib.zsp_checkpoint_save(h, int(rank), str(directory).encode(), int(step),
+                                   _stream(stream)))
+
+
+def zsp_checkpoint_load(h, rank, directory, stream=None):
+    step = ctypes.c_int64()
+    _check(lib.zsp_checkpoint_load(h, int(rank), str(directory).encode(), ctypes.byref(step),
+                                   _stream(stream)))
+    return step.value
+
+
 # ---- a plan object over the same calls -------------------------------------
 
 class Plan:
@@ -202,6 +257,7 @@ class Plan:
         self.total_numel = info["total_numel"]
         self.model_state_bytes_per_rank = info["model_state_bytes_per_rank"]
         self._bound = None
+        self._bound_rank = None
 
     @property
     def handle(self):
@@ -224,16 +280,34 @@ class Plan:
     def tensor(self, t):
         return zsp_plan_tensor(self._h, t)
 
+    # The C calls take raw pointers and cannot see buffer sizes; these methods
+    # check every tensor against the plan before anything is launched.
+
+    def _state_elems(self):
+        if self._bound_rank is None:
+            return 0
+        return self.S * (self.n_d if self._bound_rank == ALL_RANKS else 1)
+
+    def _grad_elems(self, layout):
+        return self.total_padded if _LAYOUTS[layout] == GRADS_FULL else self._state_elems()
+
     def bind_state(self, rank, master, m, v, work, grad_acc=None):
+        n = self.S * (self.n_d if rank == ALL_RANKS else 1)
+        for t, name in ((master, "master"), (m, "m"), (v, "v"), (work, "work"),
+                        (grad_acc, "grad_acc")):
+            _need(t, n, name)
         zsp_bind_state(self._h, rank, master, m, v, work, grad_acc)
         # keep the tensors alive for as long as they are bound
         self._bound = (master, m, v, work, grad_acc)
+        self._bound_rank = rank
 
     def load_params(self, flat, stream=None):
+        _need(flat, self.total_numel, "flat_params")
         zsp_load_params(self._h, flat, stream)
 
     def reduce_shard(self, rank, grads, layout="full", accumulate=False, stream=None):
-        zsp_reduce_shard(self._h, self.n_d, rank, grads, layout, accumulate, stream)
+        zsp_reduce_shard(self._h, self.n_d, rank, grads, layout, accumulate, stream,
+                         self._grad_elems(layout))
 
     def adam_step(self, rank, lr, beta1, beta2, eps, step, stream=None):
         zsp_adam_step(self._h, rank, lr, beta1, beta2, eps, step, stream)
@@ -241,13 +315,29 @@ class Plan:
     def reduce_adam_step(self, rank, grads, lr, beta1, beta2, eps, step, layout="full",
                          use_acc=False, stream=None):
         zsp_reduce_adam_step(self._h, self.n_d, rank, grads, lr, beta1, beta2, eps, step,
-                             layout, use_acc, stream)
+                             layout, use_acc, stream, self._grad_elems(layout))
 
     def gather(self, param_id, out, source="work", stream=None):
+        if 0 <= param_id < len(self.numel):
+            _need(out, self.numel[param_id], "out")
         zsp_gather(self._h, param_id, out, source, stream)
 
     def gather_many(self, first, n, out, source="work", stream=None):
+        if 0 <= first and n >= 1 and first + n <= len(self.numel):
+            _need(out, sum(self.numel[first:first + n]), "out")
         zsp_gather_many(self._h, first, n, out, source, stream)
+
+    def checkpoint_save(self, rank, directory, step, stream=None):
+        zsp_checkpoint_save(self._h, rank, directory, step, stream)
+
+    def checkpoint_load(self, rank, directory, stream=None):
+        return zsp_checkpoint_load(self._h, rank, directory, stream)
+
+    def checkpoint_write_host(self, rank, directory, step, master, m, v, work):
+        zsp_checkpoint_write_host(self._h, rank, directory, step, master, m, v, work)
+
+    def checkpoint_read_host(self, rank, directory, master, m, v, work):
+        return zsp_checkpoint_read_host(self._h, rank, directory, master, m, v, work)
 
 
 def partition(numel, n_d):
