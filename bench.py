@@ -74,6 +74,10 @@ def parse():
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"), default=None,
                     help="turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of "
                          "'bench.py --calibrate-copy' into profiles/traffic_<workload>.json")
+    ap.add_argument("--checkpoint", metavar="DIR", default=None,
+                    help="instead of the step: time a sharded checkpoint save, load, and "
+                         "load under half the rank count (reshard) of the workload's state "
+                         "in a fresh directory under DIR, check the bits, print one JSON line")
     return ap.parse_args()
 
 
@@ -194,6 +198,81 @@ class Runner:
                          "min_us": round(min(ms) * 1e3, 2), "bytes_per_launch": int(nbytes),
                          "GBps": round(gbps, 1), "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4)}
         return out
+
+
+# ---------------------------------------------------------------------------
+# Sharded checkpoint: save, load, load resharded
+# ---------------------------------------------------------------------------
+
+def checkpoint_bench(r, parent):
+    """Wall time of zsp_checkpoint_save / zsp_checkpoint_load over every rank
+    of the workload, after one real step, and of a load under N_d/2 ranks that
+    rebuilds every shard from the saved ones. Loads are checked bit for bit
+    (the resharded one by gathering every parameter from both plans)."""
+    import shutil
+    import tempfile
+    torch, zsp, w = r.torch, r.zsp, r.w
+    r.step()
+    torch.cuda.synchronize()
+    state = (r.master, r.m, r.v, r.work)
+    before = [x.clone() for x in state]
+    n_files = 1 if w.rank_local >= 0 else w.n_d
+    file_bytes = n_files * (8 + 5 * 8 + 8 * len(w.numel) + 14 * r.plan.S + 8)
+    d = tempfile.mkdtemp(prefix="zsp_ckpt_", dir=parent)
+    out = {"dir_parent": parent, "files": n_files, "file_bytes": file_bytes}
+    try:
+        t = time.perf_counter()
+        r.plan.checkpoint_save(r.rank, d, r.step_no)
+        out["save_s"] = time.perf_counter() - t
+        for x in state:
+            x.zero_()
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        step = r.plan.checkpoint_load(r.rank, d)
+        out["load_s"] = time.perf_counter() - t
+        assert step == r.step_no
+        out["load_bit_exact"] = all(torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16
+                                                else a.view(torch.int32),
+                                                b.view(torch.int16) if b.dtype == torch.bfloat16
+                                                else b.view(torch.int32))
+                                    for a, b in zip(state, before))
+        del before
+        if w.rank_local < 0 and w.n_d % 2 == 0:
+            nd2 = w.n_d // 2
+            p2 = zsp.partition(w.numel, nd2)
+            n2 = nd2 * p2.S
+            st2 = [torch.empty(n2, dtype=torch.float32, device=r.dev) for _ in range(3)]
+            st2.append(torch.empty(n2, dtype=torch.bfloat16, device=r.dev))
+            p2.bind_state(zsp.ALL_RANKS, *st2)
+            torch.cuda.synchronize()
+            t = time.perf_counter()
+            p2.checkpoint_load(zsp.ALL_RANKS, d)
+            out["reshard_load_s"] = time.perf_counter() - t
+            out["reshard_to_n_d"] = nd2
+            ok = True
+            for first, n, buf, _b in r.gather_groups:
+                a = torch.empty_like(buf)
+                r.plan.gather_many(first, n, a, "work")
+                p2.gather_many(first, n, buf, "work")
+                ok = ok and torch.equal(a.view(torch.int16), buf.view(torch.int16))
+            for src in ("master",):
+                for t_ in range(len(w.numel)):
+                    a = torch.empty(w.numel[t_], dtype=torch.float32, device=r.dev)
+                    b = torch.empty_like(a)
+                    r.plan.gather(t_, a, src)
+                    p2.gather(t_, b, src)
+                    ok = ok and torch.equal(a.view(torch.int32), b.view(torch.int32))
+            torch.cuda.synchronize()
+            out["reshard_bit_exact"] = bool(ok)
+            p2.destroy()
+            del st2
+    finally:
+        shutil.rmtree(d, ignore_errors=True)
+    for k in ("save", "load", "reshard_load"):
+        if k + "_s" in out:
+            out[k + "_GBps"] = round(file_bytes / out[k + "_s"] / 1e9, 3)
+            out[k + "_s"] = round(out[k + "_s"], 3)
+    return out
 
 
 # ---------------------------------------------------------------------------
@@ -395,6 +474,11 @@ def main():
     device = torch.device("cuda:0")
     torch.cuda.set_device(device)
     r = Runner(w, device)
+    if args.checkpoint:
+        res = checkpoint_bench(r, args.checkpoint)
+        print(json.dumps({"mode": "checkpoint", "workload": w.name, "n_d": w.n_d, **res}),
+              flush=True)
+        return 0
     flush = args.flush == "on" or (args.flush == "auto" and r.bytes_fused < 2e9)
     scratch = torch.empty(1 << 30, dtype=torch.uint8, device=device) if flush else None
 

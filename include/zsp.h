@@ -201,7 +201,8 @@ zsp_status zsp_gather_many(zsp_plan* plan, int32_t first_param, int32_t n_params
  * A checkpoint is a directory holding one file per rank,
  * "rank-<r>-of-<n_d>.zsp": a header (magic "ZSPCKPT1", n_d, rank, number of
  * parameters, S, step), the numel list, master[S], m[S], v[S] (fp32), work[S]
- * (bf16 bits), and an FNV-1a hash of all of it. The directory must exist. */
+ * (bf16 bits), and the XXH64 hash (seed 0) of all of it, all little-endian.
+ * The directory must exist. */
 
 /* Write rank `rank`'s shard set from host arrays of S elements each. Host
  * only. Files are written under a temporary name and renamed. */

@@ -10,6 +10,7 @@ import os
 
 import numpy as np
 import pytest
+import xxhash
 
 import oracle
 import zero_sharded_mixed_pad_amd as zsp
@@ -40,6 +41,17 @@ def write_all(plan, d, L, master, m, v, work, step):
         plan.checkpoint_write_host(r, d, step, master[sl], m[sl], v[sl], work[sl])
 
 
+def check_file(path, numels, nd, r, S, step, arrays):
+    """The file's bytes are the documented layout, and its trailing checksum
+    is XXH64 (seed 0) of everything before it, as the xxhash package computes."""
+    raw = open(path, "rb").read()
+    want = (b"ZSPCKPT1" + np.array([nd, r, len(numels), S, step], "<i8").tobytes()
+            + np.array(numels, "<i8").tobytes()
+            + b"".join(np.ascontiguousarray(a).tobytes() for a in arrays))
+    assert raw[:-8] == want
+    assert int.from_bytes(raw[-8:], "little") == xxhash.xxh64(want, seed=0).intdigest()
+
+
 def read_rank(plan, d, S, r):
     out = [np.empty(S, np.float32) for _ in range(3)] + [np.empty(S, np.uint16)]
     step = plan.checkpoint_read_host(r, d, *out)
@@ -56,6 +68,9 @@ def test_roundtrip_same_layout(tmp_path, numels, nd):
     plan = zsp.partition(numels, nd)
     write_all(plan, str(tmp_path), L, master, m, v, work, step=42)
     assert sorted(os.listdir(tmp_path)) == sorted(f"rank-{r}-of-{nd}.zsp" for r in range(nd))
+    for r in range(nd):
+        check_file(os.path.join(tmp_path, f"rank-{r}-of-{nd}.zsp"), numels, nd, r, L.S, 42,
+                   [a[r * L.S:(r + 1) * L.S] for a in (master, m, v, work)])
     for r in range(nd):
         step, (a, b, c, d) = read_rank(plan, str(tmp_path), L.S, r)
         sl = slice(r * L.S, (r + 1) * L.S)

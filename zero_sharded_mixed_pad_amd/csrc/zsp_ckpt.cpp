@@ -11,11 +11,12 @@
 //   int64    numel[T]
 //   float    master[S], m[S], v[S]
 //   uint16   work[S]
-//   uint64   FNV-1a hash of every byte above
+//   uint64   XXH64 (seed 0) of every byte above
 // Files are written to a temporary name and renamed, so a crash mid-write
 // never leaves a truncated file under the final name.
 #include <dirent.h>
 
+#include <algorithm>
 #include <cerrno>
 #include <cstdarg>
 #include <cstdio>
@@ -31,15 +32,87 @@ namespace {
 
 const char kMagic[8] = {'Z', 'S', 'P', 'C', 'K', 'P', 'T', '1'};
 
-struct Fnv {
-    uint64_t h = 1469598103934665603ull;
-    void add(const void* p, size_t n) {
-        const unsigned char* b = static_cast<const unsigned char*>(p);
-        for (size_t i = 0; i < n; ++i) {
-            h ^= b[i];
-            h *= 1099511628211ull;
+// XXH64 (Yann Collet's xxHash, 64-bit variant, as its specification
+// defines it), fed incrementally: four accumulators over 32-byte stripes,
+// then the stripes' merge, the length, the tail and the final avalanche.
+// Four independent multiply chains hash at several GB/s, so the checksum
+// does not limit a fast file system. Assumes a little-endian host.
+class Xxh64 {
+  public:
+    void add(const void* data, size_t n) {
+        const unsigned char* p = static_cast<const unsigned char*>(data);
+        total_ += n;
+        if (nbuf_ > 0) {
+            const size_t k = std::min(n, sizeof(buf_) - nbuf_);
+            std::memcpy(buf_ + nbuf_, p, k);
+            nbuf_ += k;
+            p += k;
+            n -= k;
+            if (nbuf_ < sizeof(buf_)) return;
+            stripes(buf_, 1);
+            nbuf_ = 0;
         }
+        const size_t whole = n / 32;
+        stripes(p, whole);
+        p += whole * 32;
+        n -= whole * 32;
+        std::memcpy(buf_, p, n);
+        nbuf_ = n;
     }
+    uint64_t digest() const {
+        uint64_t h;
+        if (total_ >= 32) {
+            h = rotl(a_[0], 1) + rotl(a_[1], 7) + rotl(a_[2], 12) + rotl(a_[3], 18);
+            for (uint64_t a : a_) h = (h ^ mix(0, a)) * kP1 + kP4;
+        } else {
+            h = kP5;  // seed 0
+        }
+        h += total_;
+        const unsigned char* p = buf_;
+        size_t n = nbuf_;
+        for (; n >= 8; n -= 8, p += 8) h = rotl(h ^ mix(0, load64(p)), 27) * kP1 + kP4;
+        if (n >= 4) {
+            uint32_t w;
+            std::memcpy(&w, p, 4);
+            h = rotl(h ^ (uint64_t(w) * kP1), 23) * kP2 + kP3;
+            p += 4;
+            n -= 4;
+        }
+        for (; n > 0; --n, ++p) h = rotl(h ^ (uint64_t(*p) * kP5), 11) * kP1;
+        h ^= h >> 33;
+        h *= kP2;
+        h ^= h >> 29;
+        h *= kP3;
+        h ^= h >> 32;
+        return h;
+    }
+
+  private:
+    static constexpr uint64_t kP1 = 0x9E3779B185EBCA87ull, kP2 = 0xC2B2AE3D27D4EB4Full,
+                              kP3 = 0x165667B19E3779F9ull, kP4 = 0x85EBCA77C2B2AE63ull,
+                              kP5 = 0x27D4EB2F165667C5ull;
+    static uint64_t rotl(uint64_t x, int r) { return (x << r) | (x >> (64 - r)); }
+    static uint64_t mix(uint64_t acc, uint64_t in) { return rotl(acc + in * kP2, 31) * kP1; }
+    static uint64_t load64(const unsigned char* p) {
+        uint64_t x;
+        std::memcpy(&x, p, 8);
+        return x;
+    }
+    void stripes(const unsigned char* p, size_t count) {
+        uint64_t a0 = a_[0], a1 = a_[1], a2 = a_[2], a3 = a_[3];
+        for (size_t i = 0; i < count; ++i, p += 32) {
+            a0 = mix(a0, load64(p));
+            a1 = mix(a1, load64(p + 8));
+            a2 = mix(a2, load64(p + 16));
+            a3 = mix(a3, load64(p + 24));
+        }
+        a_[0] = a0, a_[1] = a1, a_[2] = a2, a_[3] = a3;
+    }
+
+    uint64_t a_[4] = {kP1 + kP2, kP2, 0, 0 - kP1};  // seed 0
+    uint64_t total_ = 0;
+    unsigned char buf_[32];
+    size_t nbuf_ = 0;
 };
 
 std::string rank_path(const char* dir, int64_t r, int64_t nd) {
@@ -50,23 +123,23 @@ std::string rank_path(const char* dir, int64_t r, int64_t nd) {
 
 struct Writer {
     FILE* f = nullptr;
-    Fnv fnv;
+    Xxh64 hash;
     bool ok = true;
     void put(const void* p, size_t n) {
         if (!ok || n == 0) return;
-        fnv.add(p, n);
+        hash.add(p, n);
         ok = std::fwrite(p, 1, n, f) == n;
     }
 };
 
 struct Reader {
     FILE* f = nullptr;
-    Fnv fnv;
+    Xxh64 hash;
     bool ok = true;
     void get(void* p, size_t n) {
         if (!ok || n == 0) return;
         ok = std::fread(p, 1, n, f) == n;
-        if (ok) fnv.add(p, n);
+        if (ok) hash.add(p, n);
     }
 };
 
@@ -93,7 +166,7 @@ CkptStatus ckpt_write_rank(const char* dir, int32_t nd, int32_t rank,
     w.put(m, size_t(S) * sizeof(float));
     w.put(v, size_t(S) * sizeof(float));
     w.put(work, size_t(S) * sizeof(uint16_t));
-    const uint64_t h = w.fnv.h;
+    const uint64_t h = w.hash.digest();
     if (w.ok) w.ok = std::fwrite(&h, 1, sizeof(h), w.f) == sizeof(h);
     if (std::fclose(w.f) != 0) w.ok = false;
     if (!w.ok || std::rename(tmp.c_str(), path.c_str()) != 0) {
@@ -140,7 +213,7 @@ CkptStatus ckpt_read_rank(const char* dir, int32_t nd, int32_t rank, std::vector
     r.get(m->data(), size_t(*S) * sizeof(float));
     r.get(v->data(), size_t(*S) * sizeof(float));
     r.get(work->data(), size_t(*S) * sizeof(uint16_t));
-    const uint64_t want = r.fnv.h;
+    const uint64_t want = r.hash.digest();
     uint64_t got = 0;
     const bool tail_ok = r.ok && std::fread(&got, 1, sizeof(got), r.f) == sizeof(got);
     char extra;
