@@ -78,6 +78,14 @@ def parse():
                     help="instead of the step: time a sharded checkpoint save, load, and "
                          "load under half the rank count (reshard) of the workload's state "
                          "in a fresh directory under DIR, check the bits, print one JSON line")
+    ap.add_argument("--prefetch", action="store_true",
+                    help="instead of the step: time forward+backward passes of a Llama-7B "
+                         "decoder stack through the per-layer gather schedule at several "
+                         "prefetch depths, with a matmul stand-in for the layer compute, and "
+                         "print the hidden fraction of gather time as one JSON line")
+    ap.add_argument("--layers", type=int, default=32)
+    ap.add_argument("--tokens", type=int, nargs="+", default=[512, 1024, 4096])
+    ap.add_argument("--depths", type=int, nargs="+", default=[1, 2])
     return ap.parse_args()
 
 
@@ -273,6 +281,121 @@ def checkpoint_bench(r, parent):
             out[k + "_GBps"] = round(file_bytes / out[k + "_s"] / 1e9, 3)
             out[k + "_s"] = round(out[k + "_s"], 3)
     return out
+
+
+# ---------------------------------------------------------------------------
+# Per-layer gather schedule with prefetch
+# ---------------------------------------------------------------------------
+
+def prefetch_bench(args, device):
+    """Forward (layers 0..L-1) then backward (L-1..0) over a Llama-7B decoder
+    stack whose layers are gathered by zsp_sched_* into a (D+1)-slot arena.
+    Per layer the compute stand-in runs the seven weight matmuls: forward
+    Y = X W^T; backward dX = dY W and dW = dY^T X. Each pass is timed with
+    events on the compute stream, whose last work waits for every gather.
+    Modes are interleaved pass by pass over `steps` rounds (medians), since
+    the hidden time is a small difference of large ones:
+
+      compute  = passes on one fixed, already gathered layer (no gathers)
+      gathers  = passes of gathers alone (depth 0, no compute)
+      depth D  = gathers through the schedule with compute
+      hidden(D) = (compute + gathers - depth D) / gathers
+    """
+    import statistics
+    import torch
+    import zero_sharded_mixed_pad_amd as zsp
+    from zero_sharded_mixed_pad_amd import synth
+
+    w = synth.llama_stack(args.layers, 8)
+    plan = zsp.partition(w.numel, w.n_d)
+    n = w.n_d * plan.S
+    state = [torch.empty(n, dtype=torch.float32, device=device) for _ in range(3)]
+    state.append(torch.empty(n, dtype=torch.bfloat16, device=device))
+    plan.bind_state(zsp.ALL_RANKS, *state)
+    flat = synth.flat_params(w, device=device)
+    plan.load_params(flat)
+    torch.cuda.synchronize()
+    del flat
+    L = args.layers
+    groups = [(9 * l, 9) for l in range(L)]
+    order = list(range(L)) + list(range(L - 1, -1, -1))
+    shapes = [(4096, 4096)] * 4 + [(11008, 4096)] * 2 + [(4096, 11008)]  # (out, in)
+    layer_elems = sum(w.numel[:9])
+    cs, gs = torch.cuda.Stream(), torch.cuda.Stream()
+    fixed = torch.empty(layer_elems, dtype=torch.bfloat16, device=device)
+    plan.gather_many(0, 9, fixed, "work")
+    fixed_views, k = [], 0
+    for t in range(9):
+        fixed_views.append(fixed[k:k + w.numel[t]])
+        k += w.numel[t]
+    scheds = {}
+    for D in [0] + list(args.depths):
+        s = zsp.Schedule(plan, groups, order, D)
+        arena = torch.empty(s.arena_bytes, dtype=torch.uint8, device=device)
+        s.bind(arena, gs if D > 0 else None)
+        scheds[D] = (s, arena)
+    torch.cuda.synchronize()
+
+    results = {"layers": L, "n_d": w.n_d, "positions": len(order),
+               "gather_bytes_per_layer": 4 * layer_elems,
+               "arena_bytes": {str(D): s.arena_bytes for D, (s, _a) in scheds.items()},
+               "runs": []}
+    for T in args.tokens:
+        x = {d: torch.randn(T, d, device=device, dtype=torch.bfloat16) * 0.1
+             for d in (4096, 11008)}
+        dw = {sh: torch.empty(sh, device=device, dtype=torch.bfloat16) for sh in set(shapes)}
+
+        def compute(views, backward):
+            for v, (o, i) in zip(views[:7], shapes):
+                W = v.view(o, i)
+                if not backward:
+                    torch.nn.functional.linear(x[i], W)
+                else:
+                    dy = x[o]
+                    torch.mm(dy, W)
+                    torch.mm(dy.t(), x[i], out=dw[(o, i)])
+
+        def one_pass(sched, with_compute):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            with torch.cuda.stream(cs):
+                a.record(cs)
+                for p in range(len(order)):
+                    if sched is None:
+                        compute(fixed_views, p >= L)
+                        continue
+                    views = sched.acquire(p, cs)
+                    if with_compute:
+                        compute(views, p >= L)
+                    sched.release(p, cs)
+                b.record(cs)
+            return a, b
+
+        modes = [("compute", None, True), ("gathers", scheds[0][0], False)]
+        modes += [(f"depth{D}", scheds[D][0], True) for D in [0] + list(args.depths)]
+        for _ in range(max(1, args.warmup)):
+            for _name, sch, wc in modes:
+                one_pass(sch, wc)
+        torch.cuda.synchronize()
+        evs = {name: [] for name, _s, _w in modes}
+        for _ in range(args.steps):
+            for name, sch, wc in modes:
+                evs[name].append(one_pass(sch, wc))
+        torch.cuda.synchronize()
+        ms = {name: statistics.median(a.elapsed_time(b) for a, b in e) for name, e in evs.items()}
+        c, g = ms["compute"], ms["gathers"]
+        row = {"tokens": T, "compute_ms": round(c, 3), "gathers_ms": round(g, 3),
+               "gather_GBps": round(4 * layer_elems * len(order) / g / 1e6, 1), "depth": {}}
+        for D in [0] + list(args.depths):
+            t = ms[f"depth{D}"]
+            row["depth"][str(D)] = {"ms": round(t, 3), "exposed_gather_ms": round(t - c, 3),
+                                    "hidden": round((c + g - t) / g, 3)}
+        results["runs"].append(row)
+        print(json.dumps(row), file=sys.stderr, flush=True)
+        del x, dw
+    for s, _a in scheds.values():
+        s.destroy()
+    plan.destroy()
+    return results
 
 
 # ---------------------------------------------------------------------------
@@ -473,6 +596,11 @@ def main():
     w = wl[args.workload]
     device = torch.device("cuda:0")
     torch.cuda.set_device(device)
+    if args.prefetch:
+        res = prefetch_bench(args, device)
+        print(json.dumps({"mode": "prefetch", "steps": args.steps, "warmup": args.warmup,
+                          **res}), flush=True)
+        return 0
     r = Runner(w, device)
     if args.checkpoint:
         res = checkpoint_bench(r, args.checkpoint)

@@ -67,6 +67,7 @@ extern "C" {
 #endif
 
 typedef struct zsp_plan zsp_plan;
+typedef struct zsp_sched zsp_sched;
 
 typedef enum {
     ZSP_OK = 0,
@@ -192,6 +193,68 @@ zsp_status zsp_gather(zsp_plan* plan, int32_t param_id, zsp_source src, void* ou
  * flat_off[t] - flat_off[first_param]. */
 zsp_status zsp_gather_many(zsp_plan* plan, int32_t first_param, int32_t n_params,
                            zsp_source src, void* out, void* stream);
+
+/* ---- Per-layer gather schedule with prefetch ------------------------------
+ * [ZS3] on-demand fetch list (gather layer l before its computation, discard
+ * after) and prefetch paragraph (gather layer l+1 while layer l computes);
+ * [ZST] "Stage 3 partitions parameters" (gather before forward, again before
+ * backward, release after use; prefetch depth trades memory for latency).
+ * A schedule visits groups of consecutive parameters (one layer each) in a
+ * fixed order of positions. Position p is gathered into slot p mod (D+1) of
+ * a caller-owned device arena, D = prefetch depth; with D > 0 the gathers of
+ * positions up to p+D run on a gather stream of the caller's while the
+ * compute stream works on p. All ordering is by HIP events (no host waits):
+ * a gather into a slot follows the release of the slot's previous position,
+ * a pass's first gathers follow what the compute stream did before position
+ * 0's acquire (e.g. the optimizer step), and the compute stream's work after
+ * an acquire follows that position's gather. D = 0 gathers on the compute
+ * stream in line. The plan must outlive the schedule. */
+
+/* Build a schedule over `plan` (host only). Group g is the parameters
+ * [group_first[g], group_first[g] + group_count[g]); order[p] is the group
+ * of position p, 0 <= p < n_steps. 0 <= depth <= 64 (depths beyond
+ * n_steps - 1 act as n_steps - 1). *arena_bytes receives the device bytes
+ * zsp_sched_bind needs: (D+1) slots, each the largest group's gathered size
+ * (2 B per element for ZSP_SRC_WORK, 4 for ZSP_SRC_MASTER) rounded up to
+ * 256 B. Every gather is zsp_gather_many's kernel. */
+zsp_status zsp_sched_create(zsp_plan* plan, int32_t n_groups, const int32_t* group_first,
+                            const int32_t* group_count, int32_t n_steps, const int32_t* order,
+                            int32_t depth, zsp_source src, int64_t* arena_bytes,
+                            zsp_sched** out);
+
+/* Attach the arena (caller-owned device memory of at least *arena_bytes,
+ * 256-byte aligned) and the gather stream (required when D > 0; a stream
+ * other than the compute stream, at default priority). Needs an all-rank
+ * binding of the plan, on the current device. Creates the schedule's HIP
+ * events; a later bind replaces them and restarts at position 0. */
+zsp_status zsp_sched_bind(zsp_sched* sched, void* arena, int64_t arena_bytes,
+                          void* gather_stream);
+
+/* Acquire position `position` for work on `compute_stream`: issue any
+ * gathers not yet issued up to position + D, order the compute stream after
+ * this position's gather, and return in *params the device address of its
+ * group: parameter t at flat_off[t] - flat_off[first] elements, unpadded.
+ * Positions are acquired in order 0..n_steps-1, each released before the
+ * next is acquired; after the last, the next pass starts at 0. Otherwise
+ * ZSP_ESTATE. */
+zsp_status zsp_sched_acquire(zsp_sched* sched, int32_t position, void* compute_stream,
+                             void** params);
+
+/* Release the held position: every use of its slot must already be enqueued
+ * on `compute_stream`; the slot may be overwritten once that work is done. */
+zsp_status zsp_sched_release(zsp_sched* sched, int32_t position, void* compute_stream);
+
+/* Abandon the current pass; the next acquire is position 0. Gathers already
+ * issued still complete in stream order before any later one. */
+zsp_status zsp_sched_reset(zsp_sched* sched);
+
+/* Effective depth, slot count and slot stride in bytes. Host only. */
+zsp_status zsp_sched_info(const zsp_sched* sched, int32_t* depth, int32_t* slots,
+                          int64_t* slot_bytes);
+
+/* Free the schedule and its events (the arena stays the caller's). Work
+ * already enqueued is unaffected. NULL is a no-op. */
+void zsp_sched_destroy(zsp_sched* sched);
 
 /* ---- Sharded checkpoint, resume and reshard ------------------------------
  * [ZST] "Where the shards live and what happens on failure": each rank

@@ -195,3 +195,39 @@ def test_small_workload_every_element():
         first, n, out, _b = r.gather_groups[0]
         torch.cuda.synchronize()
         assert_bits(np_of(out), oracle.gather(w.numel, w.n_d, 0, work), f"step {step} gather")
+
+
+def test_decoder_stack_beyond_32bit_indices():
+    """32 Llama-7B layers at N_d = 8, every rank resident: 6.48e9 state
+    elements, so element indices pass 2^32. Copy-in then the per-layer
+    gathers of the last layers (and one in the middle) return the source
+    parameters bit for bit; the master copy is fp32(x) exactly."""
+    import zero_sharded_mixed_pad_amd as zsp
+    w = synth.llama_stack(32, 8)
+    dev = torch.device("cuda")
+    plan = zsp.partition(w.numel, w.n_d)
+    n = w.n_d * plan.S
+    assert n > 2 ** 32
+    master = torch.empty(n, dtype=torch.float32, device=dev)
+    m = torch.empty(n, dtype=torch.float32, device=dev)
+    v = torch.empty(n, dtype=torch.float32, device=dev)
+    work = torch.empty(n, dtype=torch.bfloat16, device=dev)
+    plan.bind_state(zsp.ALL_RANKS, master, m, v, work)
+    flat = synth.flat_params(w, device=dev)
+    plan.load_params(flat)
+    offs = np.concatenate([[0], np.cumsum(w.numel)])
+    out = torch.empty(sum(w.numel[:9]), dtype=torch.bfloat16, device=dev)
+    out32 = torch.empty(w.numel[4], dtype=torch.float32, device=dev)
+    for layer in (31, 30, 17, 0):
+        first = 9 * layer
+        plan.gather_many(first, 9, out, "work")
+        want = flat[int(offs[first]):int(offs[first + 9])]
+        assert torch.equal(out.view(torch.int16), want.view(torch.int16)), f"layer {layer}"
+        plan.gather(first + 4, out32, "master")   # W1 of the layer, fp32 master
+        want32 = flat[int(offs[first + 4]):int(offs[first + 5])].float()
+        assert torch.equal(out32.view(torch.int32), want32.view(torch.int32)), f"master {layer}"
+    # m and v start at +0 everywhere, including past 2^32
+    for x in (m, v):
+        assert int((x[-(1 << 20):].view(torch.int32) != 0).sum()) == 0
+        assert int((x[2 ** 32:2 ** 32 + (1 << 20)].view(torch.int32) != 0).sum()) == 0
+    plan.destroy()

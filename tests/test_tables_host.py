@@ -50,3 +50,11 @@ def test_workload_tables(checker, name):
     run(checker, w.numel, w.n_d, -1 if w.rank_local < 0 else w.rank_local)
     if w.rank_local < 0:
         run(checker, w.numel, w.n_d, w.n_d - 1)
+
+
+def test_decoder_stack_tables(checker):
+    """The 32-layer stack the gather schedule walks: 6.48e9 state elements,
+    beyond 32-bit indexing in every table."""
+    w = synth.llama_stack(32, 8)
+    assert sum(w.numel) > 2 ** 32
+    run(checker, w.numel, w.n_d, -1)

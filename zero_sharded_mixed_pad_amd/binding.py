@@ -37,6 +37,7 @@ def _load():
     L = ctypes.CDLL(LIB_PATH)
     i32, i64, vp, f32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_float
     i64p = ctypes.POINTER(ctypes.c_int64)
+    i32p = ctypes.POINTER(ctypes.c_int32)
     vpp = ctypes.POINTER(ctypes.c_void_p)
     sigs = {
         "zsp_partition": (i32, [i64p, i32, i32, ctypes.POINTER(vp)]),
@@ -55,6 +56,14 @@ def _load():
         "zsp_checkpoint_read_host": (i32, [vp, i32, ctypes.c_char_p, i64p, vp, vp, vp, vp]),
         "zsp_checkpoint_save": (i32, [vp, i32, ctypes.c_char_p, i64, vp]),
         "zsp_checkpoint_load": (i32, [vp, i32, ctypes.c_char_p, i64p, vp]),
+        "zsp_sched_create": (i32, [vp, i32, i32p, i32p, i32, i32p, i32, i32, i64p,
+                                   ctypes.POINTER(vp)]),
+        "zsp_sched_bind": (i32, [vp, vp, i64, vp]),
+        "zsp_sched_acquire": (i32, [vp, i32, vp, ctypes.POINTER(vp)]),
+        "zsp_sched_release": (i32, [vp, i32, vp]),
+        "zsp_sched_reset": (i32, [vp]),
+        "zsp_sched_info": (i32, [vp, i32p, i32p, i64p]),
+        "zsp_sched_destroy": (None, [vp]),
         "zsp_last_error": (ctypes.c_char_p, []),
     }
     for name, (res, args) in sigs.items():
@@ -240,6 +249,110 @@ def zsp_checkpoint_load(h, rank, directory, stream=None):
     _check(lib.zsp_checkpoint_load(h, int(rank), str(directory).encode(), ctypes.byref(step),
                                    _stream(stream)))
     return step.value
+
+
+# ---- per-layer gather schedule -----------------------------------------------
+
+def _i32_array(xs):
+    xs = [int(x) for x in xs]
+    return (ctypes.c_int32 * max(len(xs), 1))(*xs), len(xs)
+
+
+def zsp_sched_create(h, groups, order, depth, source="work"):
+    """groups: [(first_param, n_params), ...]; order: group index per position.
+    Returns (handle, arena_bytes)."""
+    first, n_groups = _i32_array(g[0] for g in groups)
+    count, _ = _i32_array(g[1] for g in groups)
+    order_c, n_steps = _i32_array(order)
+    src = SRC_WORK if source == "work" else SRC_MASTER
+    nbytes = ctypes.c_int64()
+    out = ctypes.c_void_p()
+    _check(lib.zsp_sched_create(h, n_groups, first, count, n_steps, order_c, int(depth), src,
+                                ctypes.byref(nbytes), ctypes.byref(out)))
+    return out, nbytes.value
+
+
+def zsp_sched_bind(s, arena, gather_stream):
+    if not isinstance(arena, torch.Tensor) or not arena.is_cuda or not arena.is_contiguous():
+        raise TypeError("arena must be a contiguous torch tensor on the GPU")
+    gs = None if gather_stream is None else _stream(gather_stream)
+    _check(lib.zsp_sched_bind(s, ctypes.c_void_p(arena.data_ptr()),
+                              arena.numel() * arena.element_size(), gs))
+
+
+def zsp_sched_acquire(s, position, stream=None):
+    """Returns the device address of the position's gathered group."""
+    out = ctypes.c_void_p()
+    _check(lib.zsp_sched_acquire(s, int(position), _stream(stream), ctypes.byref(out)))
+    return out.value
+
+
+def zsp_sched_release(s, position, stream=None):
+    _check(lib.zsp_sched_release(s, int(position), _stream(stream)))
+
+
+def zsp_sched_reset(s):
+    _check(lib.zsp_sched_reset(s))
+
+
+def zsp_sched_info(s):
+    d, n, b = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int64()
+    _check(lib.zsp_sched_info(s, ctypes.byref(d), ctypes.byref(n), ctypes.byref(b)))
+    return {"depth": d.value, "slots": n.value, "slot_bytes": b.value}
+
+
+def zsp_sched_destroy(s):
+    lib.zsp_sched_destroy(s)
+
+
+class Schedule:
+    """Owns a zsp_sched handle over a Plan. acquire() returns the
+    position's gathered parameters as tensor views of the arena, one per
+    parameter of its group (unpadded, flattened)."""
+
+    def __init__(self, plan, groups, order, depth, source="work"):
+        self.plan = plan
+        self.groups = [(int(f), int(c)) for f, c in groups]
+        self.order = [int(g) for g in order]
+        self.dtype = torch.bfloat16 if source == "work" else torch.float32
+        self._h, self.arena_bytes = zsp_sched_create(plan._h, self.groups, self.order, depth,
+                                                     source)
+        self.info = zsp_sched_info(self._h)
+        self.arena = None
+
+    def bind(self, arena, gather_stream):
+        zsp_sched_bind(self._h, arena, gather_stream)
+        self.arena = arena
+
+    def acquire(self, position, stream=None):
+        addr = zsp_sched_acquire(self._h, position, stream)
+        off = addr - self.arena.data_ptr()
+        first, count = self.groups[self.order[position]]
+        esz = torch.finfo(self.dtype).bits // 8
+        flat = self.arena.view(torch.uint8)[off:off + esz * sum(
+            self.plan.numel[first:first + count])].view(self.dtype)
+        views, k = [], 0
+        for t in range(first, first + count):
+            views.append(flat[k:k + self.plan.numel[t]])
+            k += self.plan.numel[t]
+        return views
+
+    def release(self, position, stream=None):
+        zsp_sched_release(self._h, position, stream)
+
+    def reset(self):
+        zsp_sched_reset(self._h)
+
+    def destroy(self):
+        if self._h:
+            zsp_sched_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.destroy()
+        except Exception:
+            pass
 
 
 # ---- a plan object over the same calls -------------------------------------

@@ -10,19 +10,25 @@
 #include <string>
 
 #include "zsp_ckpt.hpp"
+#include "zsp_entry.hpp"
 #include "zsp_internal.hpp"
 
 namespace {
 
 thread_local std::string g_last_error;
 
-zsp_status fail(zsp_status st, const char* fmt, ...) {
+zsp_status vfail(zsp_status st, const char* fmt, va_list ap) {
     char buf[512];
+    std::vsnprintf(buf, sizeof(buf), fmt, ap);
+    g_last_error = buf;
+    return st;
+}
+
+zsp_status fail(zsp_status st, const char* fmt, ...) {
     va_list ap;
     va_start(ap, fmt);
-    std::vsnprintf(buf, sizeof(buf), fmt, ap);
+    vfail(st, fmt, ap);
     va_end(ap);
-    g_last_error = buf;
     return st;
 }
 
@@ -244,6 +250,20 @@ int64_t rank_base(const zsp_plan* P, int32_t r) {
 }
 
 }  // namespace
+
+namespace zsp {
+
+zsp_status set_error(zsp_status st, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vfail(st, fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+zsp_status set_hip_error(hipError_t e, const char* what) { return fail_hip(e, what); }
+
+}  // namespace zsp
 
 extern "C" {
 
@@ -487,6 +507,13 @@ zsp_status zsp_reduce_adam_step(zsp_plan* P, int32_t rank_or_all, const void* co
 
 zsp_status zsp_gather_many(zsp_plan* P, int32_t first_param, int32_t n_params, zsp_source src,
                            void* out, void* stream) {
+    return zsp::gather_range(P, first_param, n_params, src, out, static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"
+
+zsp_status zsp::gather_range(zsp_plan* P, int32_t first_param, int32_t n_params, zsp_source src,
+                             void* out, hipStream_t stream) {
     zsp_status st = check_bound(P);
     if (st != ZSP_OK) return st;
     if (P->bind_rank != ZSP_ALL_RANKS)
@@ -507,11 +534,12 @@ zsp_status zsp_gather_many(zsp_plan* P, int32_t first_param, int32_t n_params, z
     L.src = src == ZSP_SRC_WORK ? static_cast<const void*>(P->work)
                                 : static_cast<const void*>(P->master);
     L.out = out;
-    hipError_t e = zsp::launch_gather(L, src == ZSP_SRC_WORK ? ZSP_BF16 : ZSP_F32,
-                                      static_cast<hipStream_t>(stream));
+    hipError_t e = zsp::launch_gather(L, src == ZSP_SRC_WORK ? ZSP_BF16 : ZSP_F32, stream);
     if (e != hipSuccess) return fail_hip(e, "gather launch");
     return ZSP_OK;
 }
+
+extern "C" {
 
 zsp_status zsp_gather(zsp_plan* P, int32_t param_id, zsp_source src, void* out, void* stream) {
     if (P && (param_id < 0 || param_id >= P->T))

@@ -74,6 +74,16 @@ def _llama_layer(d=4096, f=11008):
     return [d * d] * 4 + [d * f] * 3 + [d] * 2
 
 
+def llama_stack(n_layers=32, n_d=8) -> Workload:
+    """n_layers Llama-7B decoder layers (the shapes of _llama_layer), bf16,
+    every rank resident: the model a per-layer gather schedule walks."""
+    layer = _llama_layer()
+    return Workload(
+        f"llama7b_{n_layers}layers_nd{n_d}", layer * n_layers, n_d, torch.bfloat16,
+        torch.bfloat16, 0.02, 1e-3,
+        ones=[9 * i + 7 for i in range(n_layers)] + [9 * i + 8 for i in range(n_layers)])
+
+
 def small_tensor_sizes(count=10_000, lo=64, hi=65536, seed=0) -> List[int]:
     """numel = round(exp(U(ln lo, ln hi))) for `count` tensors, seeded."""
     rng = np.random.default_rng(derive_seed("small_tensor_sizes", seed))
