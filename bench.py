@@ -78,6 +78,8 @@ def parse():
                     help="instead of the step: time a sharded checkpoint save, load, and "
                          "load under half the rank count (reshard) of the workload's state "
                          "in a fresh directory under DIR, check the bits, print one JSON line")
+    ap.add_argument("--stage", type=int, choices=[1, 2, 3], default=3,
+                    help="ZeRO stage whose step schedule runs (3: the partitioned hot path)")
     ap.add_argument("--prefetch", action="store_true",
                     help="instead of the step: time forward+backward passes of a Llama-7B "
                          "decoder stack through the per-layer gather schedule at several "
@@ -94,13 +96,27 @@ def parse():
 # ---------------------------------------------------------------------------
 
 class Runner:
-    def __init__(self, w, device):
+    """One training step's ZeRO work on the workload, in the schedule of a
+    stage ("ZeRO Stages: ...", stage sections):
+      3: fused reduce-scatter + Adam, then each layer gathered before forward
+         and again before backward (two gathers per step);
+      2: the same reduction and update, then one all-gather of the updated
+         parameters (the replica forward and backward use);
+      1: the gradients all-reduced -- reduce-scatter into the accumulator,
+         then its all-gather into a full fp32 gradient replica -- Adam from
+         each rank's received slice, then the parameter all-gather.
+    With micro-batches, stages 2 and 3 reduce per micro-batch and accumulate
+    the reduced slices; stage 1 all-reduces once per step."""
+
+    def __init__(self, w, device, stage=3):
         import torch
         import zero_sharded_mixed_pad_amd as zsp
         from zero_sharded_mixed_pad_amd import synth
 
         self.torch, self.zsp, self.synth = torch, zsp, synth
-        self.w, self.dev = w, device
+        self.w, self.dev, self.stage = w, device, stage
+        if stage < 3 and w.rank_local >= 0:
+            raise ValueError("stages 1 and 2 gather every rank's shard; the workload holds one")
         self.plan = zsp.partition(w.numel, w.n_d)
         S, nd = self.plan.S, w.n_d
         self.rank = zsp.ALL_RANKS if w.rank_local < 0 else w.rank_local
@@ -110,7 +126,11 @@ class Runner:
         self.m = torch.empty(n_state, dtype=f32, device=device)
         self.v = torch.empty(n_state, dtype=f32, device=device)
         self.work = torch.empty(n_state, dtype=bf16, device=device)
-        self.acc = torch.empty(n_state, dtype=f32, device=device) if w.micro_batches > 1 else None
+        need_acc = w.micro_batches > 1 or stage == 1
+        self.acc = torch.empty(n_state, dtype=f32, device=device) if need_acc else None
+        # stage 1: every rank's full fp32 gradient after the all-reduce
+        self.grad_replica = (torch.empty(self.plan.total_numel, dtype=f32, device=device)
+                             if stage == 1 else None)
         self.plan.bind_state(self.rank, self.master, self.m, self.v, self.work, self.acc)
         flat = synth.flat_params(w, device=device)
         self.plan.load_params(flat)
@@ -133,6 +153,8 @@ class Runner:
         self.bytes_fused = self.valid * (nd * gb + 26 + acc_read)
         self.bytes_reduce_first = self.valid * (nd * gb + 4)
         self.bytes_reduce_acc = self.valid * (nd * gb + 8)
+        self.bytes_adam = self.valid * (4 + 26)          # Adam from the accumulator
+        self.bytes_gather_acc = self.valid * 8           # fp32 read + write
         # gathers: one per layer-sized group, before forward and before backward
         self.gather_groups = []
         if w.rank_local < 0:
@@ -145,7 +167,7 @@ class Runner:
                 out = torch.empty(cnt, dtype=bf16, device=device)
                 self.gather_groups.append((first, n, out, cnt * 4))
         self.step_no = 0
-        self.ev = {"fused": [], "reduce": [], "gather": []}
+        self.ev = {"fused": [], "reduce": [], "gather": [], "adam": [], "gather_acc": []}
 
     def _event(self):
         return self.torch.cuda.Event(enable_timing=True)
@@ -164,6 +186,16 @@ class Runner:
         w, p = self.w, self.plan
         self.step_no += 1
         hp = dict(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, step=self.step_no)
+        if self.stage == 1:
+            self._timed("reduce", lambda: p.reduce_shard(
+                self.rank, self.grads, layout=self.layout, accumulate=False), record)
+            self._timed("gather_acc", lambda: p.gather_many(
+                0, len(w.numel), self.grad_replica, "acc"), record)
+            self._timed("adam", lambda: p.adam_step(self.rank, **hp), record)
+            for first, n, out, _b in self.gather_groups:
+                self._timed("gather", lambda first=first, n=n, out=out: p.gather_many(
+                    first, n, out, "work"), record)
+            return
         if w.micro_batches > 1:
             for mb in range(w.micro_batches - 1):
                 self._timed("reduce", lambda mb=mb: p.reduce_shard(
@@ -173,17 +205,22 @@ class Runner:
         else:
             self._timed("fused", lambda: p.reduce_adam_step(
                 self.rank, self.grads, layout=self.layout, **hp), record)
-        for _ in range(2):  # before forward, and again before backward
+        # stage 3: before forward, and again before backward; stage 2: once,
+        # after the update
+        for _ in range(2 if self.stage == 3 else 1):
             for first, n, out, _b in self.gather_groups:
                 self._timed("gather", lambda first=first, n=n, out=out: p.gather_many(
                     first, n, out, "work"), record)
 
     def step_bytes(self):
         w = self.w
+        gathers = sum(g[3] for g in self.gather_groups)
+        if self.stage == 1:
+            return self.bytes_reduce_first + self.bytes_gather_acc + self.bytes_adam + gathers
         b = self.bytes_fused
         if w.micro_batches > 1:
             b += self.bytes_reduce_first + (w.micro_batches - 2) * self.bytes_reduce_acc
-        b += 2 * sum(g[3] for g in self.gather_groups)
+        b += (2 if self.stage == 3 else 1) * gathers
         return b
 
     def kernel_stats(self):
@@ -197,8 +234,15 @@ class Runner:
             if kind == "fused":
                 nbytes = self.bytes_fused
             elif kind == "reduce":
-                nb = [self.bytes_reduce_first] + [self.bytes_reduce_acc] * (w.micro_batches - 2)
+                if self.stage == 1:
+                    nb = [self.bytes_reduce_first]
+                else:
+                    nb = [self.bytes_reduce_first] + [self.bytes_reduce_acc] * (w.micro_batches - 2)
                 nbytes = sum(nb) / len(nb)
+            elif kind == "adam":
+                nbytes = self.bytes_adam
+            elif kind == "gather_acc":
+                nbytes = self.bytes_gather_acc
             else:
                 nbytes = sum(g[3] for g in self.gather_groups) / len(self.gather_groups)
             gbps = nbytes / avg_s / 1e9
@@ -601,7 +645,7 @@ def main():
         print(json.dumps({"mode": "prefetch", "steps": args.steps, "warmup": args.warmup,
                           **res}), flush=True)
         return 0
-    r = Runner(w, device)
+    r = Runner(w, device, args.stage)
     if args.checkpoint:
         res = checkpoint_bench(r, args.checkpoint)
         print(json.dumps({"mode": "checkpoint", "workload": w.name, "n_d": w.n_d, **res}),
@@ -644,10 +688,14 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
 
-    fused = ks["fused"]
+    # the dominant kernel: the fused step, or (stage 1) the unfused reduce
+    dom = "fused" if "fused" in ks else "reduce"
+    fused = ks[dom]
     roof = {"bound": "hbm", "achieved": fused["GBps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-            "frac": round(fused["GBps"] / HBM_PEAK_GBPS, 4), "traffic": load_traffic(w.name),
-            "kernel": "fused reduce+Adam+cast (all ranks, one launch)",
+            "frac": round(fused["GBps"] / HBM_PEAK_GBPS, 4),
+            "traffic": load_traffic(w.name) if dom == "fused" else None,
+            "kernel": ("fused reduce+Adam+cast (all ranks, one launch)" if dom == "fused"
+                       else "shard reduce (all ranks, one launch)"),
             "bytes_per_launch": fused["bytes_per_launch"], "avg_launch_us": fused["avg_us"]}
     cpu = None
     if not args.no_cpu_baseline:
@@ -666,7 +714,8 @@ def main():
                    "state": "fp32 master, m, v + bf16 working copy",
                    "micro_batches": w.micro_batches,
                    "rank_local": w.rank_local if w.rank_local >= 0 else None,
-                   "gathers_per_step": 2 * len(r.gather_groups),
+                   "zero_stage": args.stage,
+                   "gathers_per_step": (2 if args.stage == 3 else 1) * len(r.gather_groups),
                    "bytes_per_step": int(step_bytes), "cache_flush": bool(flush),
                    "wall_ms_per_step": round(wall * 1e3 / args.steps, 4)},
         "roofline": roof, "cpu_baseline": cpu, "kernels": ks,

@@ -86,7 +86,11 @@ typedef enum {
     ZSP_GRADS_SHARD = 1  /* grads[r]: indexed like the bound state arrays (see below) */
 } zsp_grad_layout;
 
-typedef enum { ZSP_SRC_WORK = 0, ZSP_SRC_MASTER = 1 } zsp_source;
+typedef enum {
+    ZSP_SRC_WORK = 0,    /* bf16 working copy of the parameters */
+    ZSP_SRC_MASTER = 1,  /* fp32 master parameters */
+    ZSP_SRC_ACC = 2      /* fp32 gradient accumulator: each rank's reduced slice */
+} zsp_source;
 
 #define ZSP_ALL_RANKS (-1)
 #define ZSP_MAX_RANKS 256
@@ -182,8 +186,12 @@ zsp_status zsp_reduce_adam_step(zsp_plan* plan, int32_t rank_or_all,
  * ([ZD] section 3; [ZS3] on-demand fetch, step 2; [ZST] "Stage 3
  * partitions parameters"). Writes numel[param_id] elements to `out`, pad
  * dropped: out[k] = src_r[shard_off[t] + k - r*s_t] with r = k / s_t.
- * src = ZSP_SRC_WORK (bf16 out) or ZSP_SRC_MASTER (fp32 out). Needs an
- * all-rank binding. */
+ * src = ZSP_SRC_WORK (bf16 out), ZSP_SRC_MASTER (fp32 out) or ZSP_SRC_ACC
+ * (fp32 out, needs an accumulator bound): gathering the reduced gradient
+ * slices completes an all-reduce of the gradients, the reduction stage 1
+ * keeps ([ZST] "What stage 1 partitions": gradients arrive complete on
+ * every rank, each rank updates its own slice); pad slots are dropped as
+ * for parameters. Needs an all-rank binding. */
 zsp_status zsp_gather(zsp_plan* plan, int32_t param_id, zsp_source src, void* out,
                       void* stream);
 

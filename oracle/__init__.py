@@ -49,6 +49,11 @@ def lib():
                                  _i64p, _i64p, _i64p, _i64p, _i64p, _i64p]
         L.orc_model_state_bytes.restype = ctypes.c_int64
         L.orc_model_state_bytes.argtypes = [ctypes.c_int64]
+        L.orc_stage_state_bytes.restype = ctypes.c_int64
+        L.orc_stage_state_bytes.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int64,
+                                            ctypes.c_int32]
+        L.orc_stage_comm_elems.restype = ctypes.c_double
+        L.orc_stage_comm_elems.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32]
         L.orc_bf16_rne.restype = ctypes.c_uint16
         L.orc_bf16_rne.argtypes = [ctypes.c_float]
         L.orc_bf16_rne_array.restype = None
@@ -148,6 +153,15 @@ class Layout:
 
 def model_state_bytes(shard_elems):
     return int(lib().orc_model_state_bytes(int(shard_elems)))
+
+
+def stage_state_bytes(stage, psi, shard_elems, grad_bytes=2):
+    return int(lib().orc_stage_state_bytes(int(stage), int(psi), int(shard_elems),
+                                           int(grad_bytes)))
+
+
+def stage_comm_elems(stage, n, p):
+    return float(lib().orc_stage_comm_elems(int(stage), int(n), int(p)))
 
 
 def bf16_rne(x):

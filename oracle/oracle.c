@@ -97,6 +97,32 @@ int64_t orc_model_state_bytes(int64_t shard_elems) {
     return shard_elems * (2 + 2 + 4 + 4 + 4);
 }
 
+int64_t orc_stage_state_bytes(int32_t stage, int64_t psi, int64_t shard_elems,
+                              int32_t grad_bytes) {
+    const int64_t param_b = 2, optim_b = 4 + 4 + 4;  /* master, m, v */
+    /* count of parameters each term is held for: all of them when
+     * replicated, the rank's own slice when sharded */
+    const int64_t params_n = stage >= 3 ? shard_elems : psi;
+    const int64_t grads_n = stage >= 2 ? shard_elems : psi;
+    const int64_t optim_n = stage >= 1 ? shard_elems : psi;
+    if (stage < 0 || stage > 3) return -1;
+    return param_b * params_n + (int64_t)grad_bytes * grads_n + optim_b * optim_n;
+}
+
+double orc_stage_comm_elems(int32_t stage, int64_t n, int32_t p) {
+    if (p < 1 || n < 0) return -1.0;
+    const double reduce_scatter = (double)n * (double)(p - 1) / (double)p;
+    const double all_gather = reduce_scatter;
+    const double all_reduce = reduce_scatter + all_gather;
+    switch (stage) {
+        case 0: return all_reduce;
+        case 1: return all_reduce + all_gather;
+        case 2: return reduce_scatter + all_gather;
+        case 3: return reduce_scatter + 2.0 * all_gather;
+        default: return -1.0;
+    }
+}
+
 typedef struct {
     int64_t *pad, *shard_len, *full_off, *shard_off, *flat_off;
     int64_t S;

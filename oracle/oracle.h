@@ -52,6 +52,25 @@ int orc_layout(int32_t T, const int64_t* numel, int32_t nd,
  * ([ZS3] equation M_Stage3). */
 int64_t orc_model_state_bytes(int64_t shard_elems);
 
+/* Model-state bytes one rank holds under ZeRO stage `stage` (0 = plain data
+ * parallelism, every term replicated) for psi parameters of which the rank
+ * owns shard_elems ([ZST] stage 1 and stage 2 sections; [ZS3] M_Stage3):
+ * 16-bit parameters (2 B), gradients of grad_bytes (2 in [ZS3]'s 16-byte
+ * budget, 4 in [ZST]'s 18-byte one) and the fp32 master + Adam moments
+ * (12 B). Stage 1 shards the optimizer bytes, stage 2 the gradients too,
+ * stage 3 everything. Returns -1 for a stage outside 0..3. */
+int64_t orc_stage_state_bytes(int32_t stage, int64_t psi, int64_t shard_elems,
+                              int32_t grad_bytes);
+
+/* Elements one rank sends per step under ZeRO stage `stage` for n
+ * parameters over p ranks, from the collectives each stage runs ([ZST]
+ * stage sections and "Communication volume compared"): a reduce-scatter or
+ * an all-gather moves n(p-1)/p per rank, an all-reduce is the two in turn.
+ * Stage 0 all-reduces gradients; 1 all-reduces them and all-gathers the
+ * updated parameters; 2 reduce-scatters and all-gathers; 3 reduce-scatters
+ * and gathers the parameters twice (forward and backward). -1 if invalid. */
+double orc_stage_comm_elems(int32_t stage, int64_t n, int32_t p);
+
 /* fp32 -> bf16, round to nearest, ties to even (bit pattern). */
 uint16_t orc_bf16_rne(float x);
 void orc_bf16_rne_array(int64_t n, const float* x, uint16_t* out);

@@ -22,8 +22,17 @@ from oracle.build import CFLAGS  # noqa: E402
 LAYOUT = "tests/test_oracle_layout.py"
 REDUCE = "tests/test_oracle_reduce.py"
 ADAM = "tests/test_oracle_adam.py"
+STAGES = "tests/test_oracle_stages.py"
 
 MUTANTS = [
+    ("stage 1 shards the gradients too", "const int64_t grads_n = stage >= 2 ? shard_elems : psi;",
+     "const int64_t grads_n = stage >= 1 ? shard_elems : psi;", STAGES),
+    ("stage 3 keeps the parameter replica", "const int64_t params_n = stage >= 3 ? shard_elems : psi;",
+     "const int64_t params_n = psi;", STAGES),
+    ("stage 2 all-reduces", "case 2: return reduce_scatter + all_gather;",
+     "case 2: return all_reduce + all_gather;", STAGES),
+    ("stage 3 gathers once", "case 3: return reduce_scatter + 2.0 * all_gather;",
+     "case 3: return reduce_scatter + all_gather;", STAGES),
     ("pad even when divisible",
      "return rem == 0 ? 0 : (int64_t)nd - rem;", "return (int64_t)nd - rem;", LAYOUT),
     ("full layout forgets the pad",

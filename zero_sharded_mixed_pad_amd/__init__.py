@@ -9,7 +9,7 @@ All work runs in the HIP kernels of libzsp.so behind the C ABI in
 include/zsp.h; this package is its thin ctypes binding.
 """
 from .binding import (  # noqa: F401
-    ALL_RANKS, BF16, F32, GRADS_FULL, GRADS_SHARD, MAX_RANKS, SRC_MASTER, SRC_WORK, Plan,
+    ALL_RANKS, BF16, F32, GRADS_FULL, GRADS_SHARD, MAX_RANKS, SRC_ACC, SRC_MASTER, SRC_WORK, Plan,
     Schedule,
     ZspError, last_error, partition, zsp_adam_step, zsp_bind_state, zsp_checkpoint_load,
     zsp_checkpoint_read_host, zsp_checkpoint_save, zsp_checkpoint_write_host, zsp_destroy, zsp_gather,

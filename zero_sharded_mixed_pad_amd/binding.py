@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(_HERE, "libzsp.so")
 OK, EINVAL, ERANGE, ENOMEM, EHIP, ESTATE, EIO = 0, -1, -2, -3, -4, -5, -6
 F32, BF16 = 0, 1
 GRADS_FULL, GRADS_SHARD = 0, 1
-SRC_WORK, SRC_MASTER = 0, 1
+SRC_WORK, SRC_MASTER, SRC_ACC = 0, 1, 2
 ALL_RANKS = -1
 MAX_RANKS = 256
 
@@ -134,8 +134,8 @@ def _need(t, n, what):
 
 _LAYOUTS = {"full": GRADS_FULL, "shard": GRADS_SHARD, GRADS_FULL: GRADS_FULL,
             GRADS_SHARD: GRADS_SHARD}
-_SOURCES = {"work": SRC_WORK, "master": SRC_MASTER, SRC_WORK: SRC_WORK,
-            SRC_MASTER: SRC_MASTER}
+_SOURCES = {"work": SRC_WORK, "master": SRC_MASTER, "acc": SRC_ACC, SRC_WORK: SRC_WORK,
+            SRC_MASTER: SRC_MASTER, SRC_ACC: SRC_ACC}
 
 
 # ---- one function per C entry point ---------------------------------------

@@ -522,7 +522,10 @@ zsp_status zsp::gather_range(zsp_plan* P, int32_t first_param, int32_t n_params,
     if (n_params < 1 || first_param < 0 || first_param > P->T - n_params)
         return fail(ZSP_ERANGE, "parameters [%d, %d+%d) outside [0, %d)", first_param,
                     first_param, n_params, P->T);
-    if (src != ZSP_SRC_WORK && src != ZSP_SRC_MASTER) return fail(ZSP_EINVAL, "bad source %d", src);
+    if (src != ZSP_SRC_WORK && src != ZSP_SRC_MASTER && src != ZSP_SRC_ACC)
+        return fail(ZSP_EINVAL, "bad source %d", src);
+    if (src == ZSP_SRC_ACC && !P->acc)
+        return fail(ZSP_ESTATE, "gather of the accumulator, but none is bound");
     const int64_t k_first = P->flat_off[first_param];
     const int64_t count = P->flat_off[first_param + n_params] - k_first;
     if (count > 0 && !out) return fail(ZSP_EINVAL, "out is NULL");
@@ -531,8 +534,9 @@ zsp_status zsp::gather_range(zsp_plan* P, int32_t first_param, int32_t n_params,
     L.tab = P->gather;
     L.k_first = k_first;
     L.count = count;
-    L.src = src == ZSP_SRC_WORK ? static_cast<const void*>(P->work)
-                                : static_cast<const void*>(P->master);
+    L.src = src == ZSP_SRC_WORK     ? static_cast<const void*>(P->work)
+            : src == ZSP_SRC_MASTER ? static_cast<const void*>(P->master)
+                                    : static_cast<const void*>(P->acc);
     L.out = out;
     hipError_t e = zsp::launch_gather(L, src == ZSP_SRC_WORK ? ZSP_BF16 : ZSP_F32, stream);
     if (e != hipSuccess) return fail_hip(e, "gather launch");
