@@ -286,22 +286,29 @@ zsp_status zsp_checkpoint_write_host(const zsp_plan* plan, int32_t rank, const c
  * with another rank count, every one of its rank files is read and the shard
  * is rebuilt for this plan (element k of parameter t comes from old rank
  * k / s_old, pads are +0): a reshard, bit-exact. The saved numel list must
- * equal the plan's, else ZSP_EIO. Host only. */
+ * equal the plan's, else ZSP_EIO; a file whose S differs is refused before
+ * anything is written to the arrays, otherwise on error their contents are
+ * unspecified. Host only. */
 zsp_status zsp_checkpoint_read_host(const zsp_plan* plan, int32_t rank, const char* dir,
                                     int64_t* step, float* master, float* m, float* v,
                                     uint16_t* work);
 
 /* Save the bound state of one rank or of every bound rank
- * (ZSP_ALL_RANKS) to `dir`. Waits for `stream` first, so everything already
- * enqueued on it is included; returns after the files are written. */
+ * (ZSP_ALL_RANKS) to `dir`. The copies follow everything already enqueued
+ * on `stream` (an event taken on it orders the library's own copy streams);
+ * returns after the files are written. Up to 8 files are written at once,
+ * through pinned host chunks the plan keeps until zsp_destroy (about 32 MiB
+ * per file in flight). */
 zsp_status zsp_checkpoint_save(zsp_plan* plan, int32_t rank_or_all, const char* dir,
                                int64_t step, void* stream);
 
 /* Load one rank or every bound rank from `dir` into the bound state,
  * resharding if the checkpoint has another rank count; *step receives the
- * saved step. The copies are ordered on `stream` and complete before the
- * call returns. Restoring only rank r (e.g. after losing it) leaves the other
- * ranks' state untouched. */
+ * saved step. Every file involved is read and checked (header, parameter
+ * list, checksum, one common step) before any device write, so a failed
+ * load leaves the state untouched. The copies follow everything already
+ * enqueued on `stream` and complete before the call returns. Restoring only
+ * rank r (e.g. after losing it) leaves the other ranks' state untouched. */
 zsp_status zsp_checkpoint_load(zsp_plan* plan, int32_t rank_or_all, const char* dir,
                                int64_t* step, void* stream);
 

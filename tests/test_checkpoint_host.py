@@ -137,10 +137,17 @@ def test_damaged_and_foreign_files_are_rejected(tmp_path):
     assert _status(plan.checkpoint_read_host, 2, d, *out) == binding.EIO
     open(path, "wb").write(good)
     assert _status(plan.checkpoint_read_host, 2, d, *out) == 0
-    # another model's parameter list
+    # another model's parameter list, with the same S and with a larger one
     other = zsp.partition([1003, 64, 6], nd)
     assert _status(other.checkpoint_read_host, 0, d, *out) == binding.EIO
     assert "another parameter list" in zsp.last_error()
+    small = zsp.partition([1003], nd)
+    Ls = oracle.Layout([1003], nd)
+    outs = [np.zeros(Ls.S, np.float32) for _ in range(3)] + [np.zeros(Ls.S, np.uint16)]
+    assert _status(small.checkpoint_read_host, 0, d, *outs) == binding.EIO
+    assert "another parameter list" in zsp.last_error()
+    assert all(not a.any() for a in outs)   # refused before any payload was written
+    small.destroy()
     # resharding needs every old rank file, all at one step
     eight = zsp.partition(numels, 8)
     L8 = oracle.Layout(numels, 8)

@@ -105,3 +105,45 @@ def test_rank_local_binding(tmp_path):
     with pytest.raises(zsp.ZspError) as e:
         A.plan.checkpoint_load((j + 1) % nd, str(tmp_path))
     assert e.value.status == zsp.binding.ESTATE
+
+
+def test_state_spanning_many_chunks(tmp_path):
+    """Each state array larger than one 16 MiB staging chunk (S = 6.5M), and
+    two ranks' files written and read in parallel."""
+    numels = [9_000_001, 4_000_003, 77]
+    A, B = Mirror(numels, 2, with_acc=False), Mirror(numels, 2, with_acc=False)
+    grads = A.grads(torch.bfloat16, "big", poison=False)
+    step(A, grads, 1)
+    step(B, grads, 1)
+    A.plan.checkpoint_save(zsp.ALL_RANKS, str(tmp_path), 1)
+    for x in (A.g_master, A.g_m, A.g_v):
+        x.fill_(float("nan"))
+    A.g_work.fill_(7.0)
+    assert A.plan.checkpoint_load(zsp.ALL_RANKS, str(tmp_path)) == 1
+    for got, want, name in zip(state_bits(A), state_bits(B), ("master", "m", "v", "work")):
+        assert_bits(got, want, f"many chunks: {name}")
+
+
+def test_more_ranks_than_lanes_and_stream_order(tmp_path):
+    """Twelve rank files over fewer worker lanes; the save is queued right
+    after a step on a non-blocking stream, with no host wait in between, and
+    must hold the state after that step."""
+    nd = 12
+    A, B = Mirror(NUMELS, nd), Mirror(NUMELS, nd)
+    g1 = A.grads(torch.bfloat16, "lanes1")
+    g2 = A.grads(torch.bfloat16, "lanes2")
+    step(A, g1, 1)
+    step(B, g1, 1)
+    step(B, g2, 2)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    gdev = [g.to("cuda") for g in g2]
+    torch.cuda.synchronize()
+    A.plan.reduce_adam_step(zsp.ALL_RANKS, gdev, step=2, stream=s, **HP)
+    A.plan.checkpoint_save(zsp.ALL_RANKS, str(tmp_path), 2, stream=s)
+    assert len(list(tmp_path.iterdir())) == nd
+    C = Mirror(NUMELS, nd)
+    torch.cuda.synchronize()   # C's copy-in ran on the default stream
+    assert C.plan.checkpoint_load(zsp.ALL_RANKS, str(tmp_path), stream=s) == 2
+    for got, want, name in zip(state_bits(C), state_bits(B), ("master", "m", "v", "work")):
+        assert_bits(got, want, f"saved after the queued step: {name}")

@@ -9,9 +9,9 @@
 #include <new>
 #include <string>
 
-#include "zsp_ckpt.hpp"
 #include "zsp_entry.hpp"
 #include "zsp_internal.hpp"
+#include "zsp_plan.hpp"
 
 namespace {
 
@@ -130,124 +130,6 @@ size_t bytes_of(const std::vector<T>& v) {
 size_t round_up(size_t x) { return (x + 255) & ~size_t(255); }
 
 
-// ---- checkpoint helpers ----------------------------------------------------
-
-struct HostShards {  // one rank's shard set on the host
-    std::vector<float> master, m, v;
-    std::vector<uint16_t> work;
-};
-
-struct RankLayout {
-    std::vector<int64_t> shard_len, shard_off;
-    int64_t S = 0;
-};
-
-RankLayout rank_layout(const std::vector<int64_t>& numel, int32_t nd) {
-    RankLayout L;
-    L.shard_len.resize(numel.size());
-    L.shard_off.assign(numel.size() + 1, 0);
-    for (size_t t = 0; t < numel.size(); ++t) {
-        L.shard_len[t] = (numel[t] + zsp::pad_for(numel[t], nd)) / nd;
-        L.shard_off[t + 1] = L.shard_off[t] + L.shard_len[t];
-    }
-    L.S = L.shard_off.back();
-    return L;
-}
-
-zsp_status ckpt_fail(zsp::CkptStatus st, const std::string& err) {
-    (void)st;
-    return fail(ZSP_EIO, "%s", err.c_str());
-}
-
-// Every rank file of an nd_old-rank checkpoint, checked against the plan's
-// parameter list and for one common step.
-zsp_status read_all_ranks(const zsp_plan* P, const char* dir, int32_t nd_old,
-                          std::vector<HostShards>* out, int64_t* step) {
-    out->assign(size_t(nd_old), HostShards{});
-    const RankLayout Lo = rank_layout(P->numel, nd_old);
-    for (int32_t r = 0; r < nd_old; ++r) {
-        std::vector<int64_t> numel;
-        int64_t S = 0, st = 0;
-        std::string err;
-        HostShards& h = (*out)[r];
-        const zsp::CkptStatus cs =
-            zsp::ckpt_read_rank(dir, nd_old, r, &numel, &S, &st, &h.master, &h.m, &h.v, &h.work, &err);
-        if (cs != zsp::CkptStatus::Ok) return ckpt_fail(cs, err);
-        if (numel != P->numel || S != Lo.S)
-            return fail(ZSP_EIO, "checkpoint in %s holds another parameter list", dir);
-        if (r == 0) *step = st;
-        else if (st != *step)
-            return fail(ZSP_EIO, "checkpoint in %s mixes steps %lld and %lld", dir,
-                        (long long)*step, (long long)st);
-    }
-    return ZSP_OK;
-}
-
-// Rank j's shard set under the plan's layout, cut from the old ranks'
-// shards: element k of parameter t lives in old rank k / s_old at
-// k - r*s_old of its slice; pads are +0.
-template <typename T>
-void reshard_array(const zsp_plan* P, const RankLayout& Lo, int32_t j,
-                   const std::vector<const T*>& old, T* out) {
-    for (int32_t t = 0; t < P->T; ++t) {
-        const int64_t s = P->shard_len[t], so = Lo.shard_len[t];
-        int64_t dst = P->shard_off[t];
-        int64_t k = int64_t(j) * s;
-        const int64_t kend = std::min<int64_t>(P->numel[t], k + s);
-        while (k < kend) {
-            const int64_t r = k / so;
-            const int64_t run_end = std::min<int64_t>(kend, (r + 1) * so);
-            std::memcpy(out + dst, old[size_t(r)] + Lo.shard_off[t] + (k - r * so),
-                        size_t(run_end - k) * sizeof(T));
-            dst += run_end - k;
-            k = run_end;
-        }
-        const int64_t end = P->shard_off[t] + s;
-        if (dst < end) std::memset(out + dst, 0, size_t(end - dst) * sizeof(T));
-    }
-}
-
-void reshard_rank(const zsp_plan* P, int32_t nd_old, const std::vector<HostShards>& old,
-                  int32_t j, float* master, float* m, float* v, uint16_t* work) {
-    const RankLayout Lo = rank_layout(P->numel, nd_old);
-    std::vector<const float*> pm, pmm, pv;
-    std::vector<const uint16_t*> pw;
-    for (const HostShards& h : old) {
-        pm.push_back(h.master.data());
-        pmm.push_back(h.m.data());
-        pv.push_back(h.v.data());
-        pw.push_back(h.work.data());
-    }
-    reshard_array(P, Lo, j, pm, master);
-    reshard_array(P, Lo, j, pmm, m);
-    reshard_array(P, Lo, j, pv, v);
-    reshard_array(P, Lo, j, pw, work);
-}
-
-// Ranks a save/load call covers under the plan's binding.
-zsp_status ckpt_ranks(const zsp_plan* P, int32_t rank_or_all, std::vector<int32_t>* ranks) {
-    ranks->clear();
-    if (P->bind_rank != ZSP_ALL_RANKS) {
-        if (rank_or_all != ZSP_ALL_RANKS && rank_or_all != P->bind_rank)
-            return fail(ZSP_ESTATE, "state is bound for rank %d only, call named rank %d",
-                        P->bind_rank, rank_or_all);
-        ranks->push_back(P->bind_rank);
-        return ZSP_OK;
-    }
-    if (rank_or_all == ZSP_ALL_RANKS) {
-        for (int32_t r = 0; r < P->nd; ++r) ranks->push_back(r);
-        return ZSP_OK;
-    }
-    if (rank_or_all < 0 || rank_or_all >= P->nd)
-        return fail(ZSP_EINVAL, "rank %d outside [0, %d) and not ZSP_ALL_RANKS", rank_or_all,
-                    P->nd);
-    ranks->push_back(rank_or_all);
-    return ZSP_OK;
-}
-
-int64_t rank_base(const zsp_plan* P, int32_t r) {
-    return P->bind_rank == ZSP_ALL_RANKS ? int64_t(r) * P->S : 0;
-}
 
 }  // namespace
 
@@ -262,6 +144,8 @@ zsp_status set_error(zsp_status st, const char* fmt, ...) {
 }
 
 zsp_status set_hip_error(hipError_t e, const char* what) { return fail_hip(e, what); }
+
+zsp_status check_bound(const zsp_plan* P) { return ::check_bound(P); }
 
 }  // namespace zsp
 
@@ -316,6 +200,7 @@ zsp_status zsp_partition(const int64_t* numel, int32_t n_params, int32_t n_d, zs
 
 void zsp_destroy(zsp_plan* plan) {
     if (!plan) return;
+    zsp::staging_free(plan->staging);
     free_tables(plan);
     delete plan;
 }
@@ -551,159 +436,6 @@ zsp_status zsp_gather(zsp_plan* P, int32_t param_id, zsp_source src, void* out, 
     return zsp_gather_many(P, param_id, 1, src, out, stream);
 }
 
-
-zsp_status zsp_checkpoint_write_host(const zsp_plan* P, int32_t rank, const char* dir,
-                                     int64_t step, const float* master, const float* m,
-                                     const float* v, const uint16_t* work) {
-    if (!P) return fail(ZSP_EINVAL, "plan is NULL");
-    if (!dir) return fail(ZSP_EINVAL, "dir is NULL");
-    if (rank < 0 || rank >= P->nd) return fail(ZSP_EINVAL, "rank %d outside [0, %d)", rank, P->nd);
-    if (P->S > 0 && (!master || !m || !v || !work))
-        return fail(ZSP_EINVAL, "state arrays must not be NULL");
-    std::string err;
-    const zsp::CkptStatus cs =
-        zsp::ckpt_write_rank(dir, P->nd, rank, P->numel, P->S, step, master, m, v, work, &err);
-    if (cs != zsp::CkptStatus::Ok) return ckpt_fail(cs, err);
-    return ZSP_OK;
-}
-
-zsp_status zsp_checkpoint_read_host(const zsp_plan* P, int32_t rank, const char* dir,
-                                    int64_t* step, float* master, float* m, float* v,
-                                    uint16_t* work) {
-    if (!P) return fail(ZSP_EINVAL, "plan is NULL");
-    if (!dir || !step) return fail(ZSP_EINVAL, "dir and step must not be NULL");
-    if (rank < 0 || rank >= P->nd) return fail(ZSP_EINVAL, "rank %d outside [0, %d)", rank, P->nd);
-    if (P->S > 0 && (!master || !m || !v || !work))
-        return fail(ZSP_EINVAL, "state arrays must not be NULL");
-    const int32_t nd_old = zsp::ckpt_find_nd(dir);
-    if (nd_old == 0) return fail(ZSP_EIO, "no checkpoint (rank-<r>-of-<n>.zsp) in %s", dir);
-    if (nd_old < 0) return fail(ZSP_EIO, "%s holds shard files of several rank counts", dir);
-    try {
-        std::vector<HostShards> old;
-        if (nd_old == P->nd) {
-            old.resize(1);
-            std::vector<int64_t> numel;
-            int64_t S = 0;
-            std::string err;
-            HostShards& h = old[0];
-            const zsp::CkptStatus cs = zsp::ckpt_read_rank(dir, P->nd, rank, &numel, &S, step,
-                                                           &h.master, &h.m, &h.v, &h.work, &err);
-            if (cs != zsp::CkptStatus::Ok) return ckpt_fail(cs, err);
-            if (numel != P->numel || S != P->S)
-                return fail(ZSP_EIO, "checkpoint in %s holds another parameter list", dir);
-            const size_t n = size_t(P->S);
-            std::copy(h.master.begin(), h.master.begin() + n, master);
-            std::copy(h.m.begin(), h.m.begin() + n, m);
-            std::copy(h.v.begin(), h.v.begin() + n, v);
-            std::copy(h.work.begin(), h.work.begin() + n, work);
-            return ZSP_OK;
-        }
-        zsp_status st = read_all_ranks(P, dir, nd_old, &old, step);
-        if (st != ZSP_OK) return st;
-        reshard_rank(P, nd_old, old, rank, master, m, v, work);
-    } catch (const std::bad_alloc&) {
-        return fail(ZSP_ENOMEM, "out of host memory reading the checkpoint");
-    }
-    return ZSP_OK;
-}
-
-zsp_status zsp_checkpoint_save(zsp_plan* P, int32_t rank_or_all, const char* dir, int64_t step,
-                               void* stream) {
-    zsp_status st = check_bound(P);
-    if (st != ZSP_OK) return st;
-    if (!dir) return fail(ZSP_EINVAL, "dir is NULL");
-    std::vector<int32_t> ranks;
-    if ((st = ckpt_ranks(P, rank_or_all, &ranks)) != ZSP_OK) return st;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    try {
-        HostShards h;
-        const size_t n = size_t(P->S);
-        h.master.resize(n);
-        h.m.resize(n);
-        h.v.resize(n);
-        h.work.resize(n);
-        for (int32_t r : ranks) {
-            const int64_t b = rank_base(P, r);
-            hipError_t e = hipSuccess;
-            if (n > 0) {
-                e = hipMemcpyAsync(h.master.data(), P->master + b, n * 4, hipMemcpyDeviceToHost, s);
-                if (e == hipSuccess)
-                    e = hipMemcpyAsync(h.m.data(), P->m + b, n * 4, hipMemcpyDeviceToHost, s);
-                if (e == hipSuccess)
-                    e = hipMemcpyAsync(h.v.data(), P->v + b, n * 4, hipMemcpyDeviceToHost, s);
-                if (e == hipSuccess)
-                    e = hipMemcpyAsync(h.work.data(), P->work + b, n * 2, hipMemcpyDeviceToHost, s);
-            }
-            if (e == hipSuccess) e = hipStreamSynchronize(s);
-            if (e != hipSuccess) return fail_hip(e, "copying the shards to the host");
-            std::string err;
-            const zsp::CkptStatus cs = zsp::ckpt_write_rank(dir, P->nd, r, P->numel, P->S, step,
-                                                            h.master.data(), h.m.data(),
-                                                            h.v.data(), h.work.data(), &err);
-            if (cs != zsp::CkptStatus::Ok) return ckpt_fail(cs, err);
-        }
-    } catch (const std::bad_alloc&) {
-        return fail(ZSP_ENOMEM, "out of host memory staging the checkpoint");
-    }
-    return ZSP_OK;
-}
-
-zsp_status zsp_checkpoint_load(zsp_plan* P, int32_t rank_or_all, const char* dir, int64_t* step,
-                               void* stream) {
-    zsp_status st = check_bound(P);
-    if (st != ZSP_OK) return st;
-    if (!dir || !step) return fail(ZSP_EINVAL, "dir and step must not be NULL");
-    std::vector<int32_t> ranks;
-    if ((st = ckpt_ranks(P, rank_or_all, &ranks)) != ZSP_OK) return st;
-    const int32_t nd_old = zsp::ckpt_find_nd(dir);
-    if (nd_old == 0) return fail(ZSP_EIO, "no checkpoint (rank-<r>-of-<n>.zsp) in %s", dir);
-    if (nd_old < 0) return fail(ZSP_EIO, "%s holds shard files of several rank counts", dir);
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    try {
-        std::vector<HostShards> old;
-        if (nd_old != P->nd) {
-            if ((st = read_all_ranks(P, dir, nd_old, &old, step)) != ZSP_OK) return st;
-        }
-        HostShards h;
-        const size_t n = size_t(P->S);
-        h.master.resize(n);
-        h.m.resize(n);
-        h.v.resize(n);
-        h.work.resize(n);
-        for (int32_t r : ranks) {
-            if (nd_old == P->nd) {
-                std::vector<int64_t> numel;
-                int64_t S = 0;
-                std::string err;
-                const zsp::CkptStatus cs = zsp::ckpt_read_rank(dir, P->nd, r, &numel, &S, step,
-                                                               &h.master, &h.m, &h.v, &h.work,
-                                                               &err);
-                if (cs != zsp::CkptStatus::Ok) return ckpt_fail(cs, err);
-                if (numel != P->numel || S != P->S)
-                    return fail(ZSP_EIO, "checkpoint in %s holds another parameter list", dir);
-            } else {
-                reshard_rank(P, nd_old, old, r, h.master.data(), h.m.data(), h.v.data(),
-                             h.work.data());
-            }
-            const int64_t b = rank_base(P, r);
-            hipError_t e = hipSuccess;
-            if (n > 0) {
-                e = hipMemcpyAsync(P->master + b, h.master.data(), n * 4, hipMemcpyHostToDevice, s);
-                if (e == hipSuccess)
-                    e = hipMemcpyAsync(P->m + b, h.m.data(), n * 4, hipMemcpyHostToDevice, s);
-                if (e == hipSuccess)
-                    e = hipMemcpyAsync(P->v + b, h.v.data(), n * 4, hipMemcpyHostToDevice, s);
-                if (e == hipSuccess)
-                    e = hipMemcpyAsync(P->work + b, h.work.data(), n * 2, hipMemcpyHostToDevice, s);
-            }
-            if (e == hipSuccess) e = hipStreamSynchronize(s);
-            if (e != hipSuccess) return fail_hip(e, "copying the shards to the device");
-        }
-    } catch (const std::bad_alloc&) {
-        return fail(ZSP_ENOMEM, "out of host memory reading the checkpoint");
-    }
-    return ZSP_OK;
-}
 
 const char* zsp_last_error(void) { return g_last_error.c_str(); }
 

@@ -143,13 +143,129 @@ struct Reader {
     }
 };
 
+// Open rank `rank`'s file and read its header and numel list.
+CkptStatus open_and_read_header(const char* dir, int32_t nd, int32_t rank, Reader* r,
+                                std::vector<int64_t>* numel, int64_t* S, int64_t* step,
+                                std::string* path, std::string* err) {
+    *path = rank_path(dir, rank, nd);
+    r->f = std::fopen(path->c_str(), "rb");
+    if (!r->f) {
+        *err = "cannot open " + *path + ": " + std::strerror(errno);
+        return CkptStatus::Missing;
+    }
+    char magic[8];
+    int64_t hdr[5];
+    r->get(magic, sizeof(magic));
+    r->get(hdr, sizeof(hdr));
+    if (!r->ok || std::memcmp(magic, kMagic, 8) != 0 || hdr[0] != nd || hdr[1] != rank ||
+        hdr[2] < 1 || hdr[2] > (int64_t(1) << 31) || hdr[3] < 0 || hdr[3] > (int64_t(1) << 40)) {
+        std::fclose(r->f);
+        r->f = nullptr;
+        *err = *path + ": not a shard file of rank " + std::to_string(rank) + " of " +
+               std::to_string(nd);
+        return CkptStatus::Corrupt;
+    }
+    numel->resize(size_t(hdr[2]));
+    r->get(numel->data(), numel->size() * sizeof(int64_t));
+    *S = hdr[3];
+    *step = hdr[4];
+    return CkptStatus::Ok;
+}
+
+// After the payload: the stored checksum must match and end the file.
+CkptStatus finish_read(Reader* r, const std::string& path, std::string* err) {
+    const uint64_t want = r->hash.digest();
+    uint64_t got = 0;
+    const bool tail_ok = r->ok && std::fread(&got, 1, sizeof(got), r->f) == sizeof(got);
+    char extra;
+    const bool at_end = std::fread(&extra, 1, 1, r->f) == 0;
+    std::fclose(r->f);
+    r->f = nullptr;
+    if (!tail_ok || got != want || !at_end) {
+        *err = path + ": truncated or corrupt (hash mismatch)";
+        return CkptStatus::Corrupt;
+    }
+    return CkptStatus::Ok;
+}
+
 }  // namespace
 
-// Write rank r's shard set (host arrays of S elements) to its file.
+HostPayload::HostPayload(const float* master, const float* m, const float* v,
+                         const uint16_t* work, int64_t S)
+    : S_(S) {
+    seg_[0] = reinterpret_cast<char*>(const_cast<float*>(master));
+    seg_[1] = reinterpret_cast<char*>(const_cast<float*>(m));
+    seg_[2] = reinterpret_cast<char*>(const_cast<float*>(v));
+    seg_[3] = reinterpret_cast<char*>(const_cast<uint16_t*>(work));
+    set_segments(S);
+}
+
+HostPayload::HostPayload(std::vector<float>* master, std::vector<float>* m,
+                         std::vector<float>* v, std::vector<uint16_t>* work, int64_t S)
+    : vm_(master), vmm_(m), vv_(v), vw_(work), S_(S) {}
+
+void HostPayload::set_segments(int64_t S) {
+    for (int i = 0; i < 4; ++i) len_[i] = size_t(S) * (i < 3 ? 4 : 2);
+    cur_ = 0;
+    off_ = 0;
+}
+
+bool HostPayload::next(const void** data, size_t* n, std::string*) {
+    while (cur_ < 4 && off_ == len_[cur_]) {
+        ++cur_;
+        off_ = 0;
+    }
+    if (cur_ == 4) {
+        *n = 0;
+        return true;
+    }
+    *data = seg_[cur_] + off_;
+    *n = len_[cur_] - off_;
+    off_ = len_[cur_];
+    return true;
+}
+
+bool HostPayload::begin(int64_t S, std::string* err) {
+    if (S != S_) {
+        *err = "holds another parameter list";
+        return false;
+    }
+    if (vm_) {  // vectors: size them to the file's S
+        vm_->resize(size_t(S));
+        vmm_->resize(size_t(S));
+        vv_->resize(size_t(S));
+        vw_->resize(size_t(S));
+        seg_[0] = reinterpret_cast<char*>(vm_->data());
+        seg_[1] = reinterpret_cast<char*>(vmm_->data());
+        seg_[2] = reinterpret_cast<char*>(vv_->data());
+        seg_[3] = reinterpret_cast<char*>(vw_->data());
+    }
+    set_segments(S);
+    return true;
+}
+
+bool HostPayload::buffer(void** data, size_t* cap, std::string* err) {
+    while (cur_ < 4 && off_ == len_[cur_]) {
+        ++cur_;
+        off_ = 0;
+    }
+    if (cur_ == 4) {
+        *err = "payload longer than the arrays";
+        return false;
+    }
+    *data = seg_[cur_] + off_;
+    *cap = len_[cur_] - off_;
+    return true;
+}
+
+bool HostPayload::commit(size_t n, std::string*) {
+    off_ += n;
+    return true;
+}
+
 CkptStatus ckpt_write_rank(const char* dir, int32_t nd, int32_t rank,
                            const std::vector<int64_t>& numel, int64_t S, int64_t step,
-                           const float* master, const float* m, const float* v,
-                           const uint16_t* work, std::string* err) {
+                           PayloadSource& src, std::string* err) {
     const std::string path = rank_path(dir, rank, nd);
     const std::string tmp = path + ".tmp";
     Writer w;
@@ -162,68 +278,82 @@ CkptStatus ckpt_write_rank(const char* dir, int32_t nd, int32_t rank,
     w.put(kMagic, sizeof(kMagic));
     w.put(hdr, sizeof(hdr));
     w.put(numel.data(), numel.size() * sizeof(int64_t));
-    w.put(master, size_t(S) * sizeof(float));
-    w.put(m, size_t(S) * sizeof(float));
-    w.put(v, size_t(S) * sizeof(float));
-    w.put(work, size_t(S) * sizeof(uint16_t));
+    int64_t total = 0;
+    std::string why;
+    bool src_ok = true;
+    while (w.ok) {
+        const void* data = nullptr;
+        size_t n = 0;
+        if (!src.next(&data, &n, &why)) {
+            src_ok = false;
+            break;
+        }
+        if (n == 0) break;
+        w.put(data, n);
+        total += int64_t(n);
+    }
+    if (src_ok && total != ckpt_payload_bytes(S)) {
+        src_ok = false;
+        why = "payload of " + std::to_string(total) + " bytes, expected " +
+              std::to_string(ckpt_payload_bytes(S));
+    }
     const uint64_t h = w.hash.digest();
-    if (w.ok) w.ok = std::fwrite(&h, 1, sizeof(h), w.f) == sizeof(h);
+    if (w.ok && src_ok) w.ok = std::fwrite(&h, 1, sizeof(h), w.f) == sizeof(h);
     if (std::fclose(w.f) != 0) w.ok = false;
-    if (!w.ok || std::rename(tmp.c_str(), path.c_str()) != 0) {
+    if (!src_ok || !w.ok || std::rename(tmp.c_str(), path.c_str()) != 0) {
         std::remove(tmp.c_str());
-        *err = "cannot write " + path;
+        *err = !src_ok ? "writing " + path + ": " + why : "cannot write " + path;
         return CkptStatus::Io;
     }
     return CkptStatus::Ok;
 }
 
-// Read the file of rank r of an nd-rank checkpoint; checks magic, header and
-// hash, and returns the header's numel list, S and step.
-CkptStatus ckpt_read_rank(const char* dir, int32_t nd, int32_t rank, std::vector<int64_t>* numel,
-                          int64_t* S, int64_t* step, std::vector<float>* master,
-                          std::vector<float>* m, std::vector<float>* v,
-                          std::vector<uint16_t>* work, std::string* err) {
-    const std::string path = rank_path(dir, rank, nd);
+CkptStatus ckpt_stream_rank(const char* dir, int32_t nd, int32_t rank,
+                            std::vector<int64_t>* numel, int64_t* S, int64_t* step,
+                            PayloadSink& sink, std::string* err) {
     Reader r;
-    r.f = std::fopen(path.c_str(), "rb");
-    if (!r.f) {
-        *err = "cannot open " + path + ": " + std::strerror(errno);
-        return CkptStatus::Missing;
-    }
-    char magic[8];
-    int64_t hdr[5];
-    r.get(magic, sizeof(magic));
-    r.get(hdr, sizeof(hdr));
-    if (!r.ok || std::memcmp(magic, kMagic, 8) != 0 || hdr[0] != nd || hdr[1] != rank ||
-        hdr[2] < 1 || hdr[2] > (int64_t(1) << 31) || hdr[3] < 0 || hdr[3] > (int64_t(1) << 40)) {
+    std::string path;
+    CkptStatus st = open_and_read_header(dir, nd, rank, &r, numel, S, step, &path, err);
+    if (st != CkptStatus::Ok) return st;
+    std::string why;
+    if (!r.ok || !sink.begin(*S, &why)) {
         std::fclose(r.f);
-        *err = path + ": not a shard file of rank " + std::to_string(rank) + " of " +
-               std::to_string(nd);
-        return CkptStatus::Corrupt;
+        *err = r.ok ? path + ": " + why : path + ": truncated or corrupt (hash mismatch)";
+        return r.ok ? CkptStatus::Io : CkptStatus::Corrupt;
     }
-    numel->resize(size_t(hdr[2]));
-    r.get(numel->data(), numel->size() * sizeof(int64_t));
-    *S = hdr[3];
-    *step = hdr[4];
-    master->resize(size_t(*S));
-    m->resize(size_t(*S));
-    v->resize(size_t(*S));
-    work->resize(size_t(*S));
-    r.get(master->data(), size_t(*S) * sizeof(float));
-    r.get(m->data(), size_t(*S) * sizeof(float));
-    r.get(v->data(), size_t(*S) * sizeof(float));
-    r.get(work->data(), size_t(*S) * sizeof(uint16_t));
-    const uint64_t want = r.hash.digest();
-    uint64_t got = 0;
-    const bool tail_ok = r.ok && std::fread(&got, 1, sizeof(got), r.f) == sizeof(got);
-    char extra;
-    const bool at_end = std::fread(&extra, 1, 1, r.f) == 0;
-    std::fclose(r.f);
-    if (!tail_ok || got != want || !at_end) {
-        *err = path + ": truncated or corrupt (hash mismatch)";
-        return CkptStatus::Corrupt;
+    int64_t left = ckpt_payload_bytes(*S);
+    while (left > 0 && r.ok) {
+        void* data = nullptr;
+        size_t cap = 0;
+        if (!sink.buffer(&data, &cap, &why)) break;
+        const size_t n = size_t(std::min<int64_t>(left, int64_t(cap)));
+        r.get(data, n);
+        if (!r.ok) break;
+        if (!sink.commit(n, &why)) break;
+        left -= int64_t(n);
     }
-    return CkptStatus::Ok;
+    if (left > 0 && r.ok) {  // the sink failed
+        std::fclose(r.f);
+        *err = path + ": " + why;
+        return CkptStatus::Io;
+    }
+    return finish_read(&r, path, err);
+}
+
+CkptStatus ckpt_verify_rank(const char* dir, int32_t nd, int32_t rank,
+                            std::vector<int64_t>* numel, int64_t* S, int64_t* step,
+                            void* scratch, size_t scratch_bytes, std::string* err) {
+    Reader r;
+    std::string path;
+    CkptStatus st = open_and_read_header(dir, nd, rank, &r, numel, S, step, &path, err);
+    if (st != CkptStatus::Ok) return st;
+    int64_t left = ckpt_payload_bytes(*S);
+    while (left > 0 && r.ok) {
+        const size_t n = size_t(std::min<int64_t>(left, int64_t(scratch_bytes)));
+        r.get(scratch, n);
+        left -= int64_t(n);
+    }
+    return finish_read(&r, path, err);
 }
 
 // Number of ranks of the checkpoint in `dir`, from the names of the shard

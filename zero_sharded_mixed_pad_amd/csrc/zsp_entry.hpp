@@ -14,6 +14,9 @@ namespace zsp {
 zsp_status set_error(zsp_status st, const char* fmt, ...);
 zsp_status set_hip_error(hipError_t e, const char* what);
 
+// ZSP_OK if the plan has state bound on the current device, else the error.
+zsp_status check_bound(const zsp_plan* P);
+
 // zsp_gather_many on a HIP stream (argument checks, then one launch).
 zsp_status gather_range(zsp_plan* P, int32_t first_param, int32_t n_params, zsp_source src,
                         void* out, hipStream_t stream);

@@ -1,6 +1,6 @@
-// zsp_internal.hpp -- plan structure, device-table formats and kernel launch
-// interfaces shared by the host side (zsp_layout.cpp, zsp_capi.cpp) and the
-// HIP kernels (zsp_kernels.hip) of libzsp.
+// zsp_internal.hpp -- device-table formats and kernel launch interfaces
+// shared by the host side (zsp_layout.cpp, zsp_capi.cpp) and the HIP kernels
+// (zsp_kernels.hip) of libzsp.
 #pragma once
 
 #include <hip/hip_runtime_api.h>
@@ -134,25 +134,3 @@ void build_tile_index(const std::vector<int64_t>& starts, int64_t total,
                       std::vector<int32_t>& tile);
 
 }  // namespace zsp
-
-struct zsp_plan {
-    int32_t T = 0;
-    int32_t nd = 0;
-    std::vector<int64_t> numel, pad, shard_len, full_off, shard_off, flat_off;
-    int64_t S = 0;
-    int64_t total_padded = 0;
-    int64_t total_numel = 0;
-
-    bool bound = false;
-    int32_t bind_rank = ZSP_ALL_RANKS;
-    int device = -1;
-    float* master = nullptr;
-    float* m = nullptr;
-    float* v = nullptr;
-    uint16_t* work = nullptr;
-    float* acc = nullptr;
-
-    void* dev_blob = nullptr;  // one device allocation holding both tables
-    zsp::ShardTable shard;
-    zsp::GatherTable gather;
-};

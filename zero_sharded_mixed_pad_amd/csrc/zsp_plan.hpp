@@ -1,0 +1,40 @@
+// zsp_plan.hpp -- the plan behind the opaque zsp_plan handle: layout
+// tables on the host, the bound state pointers, the device copies of the
+// piece tables, and the checkpoint staging the plan keeps between calls.
+#pragma once
+
+#include <cstdint>
+#include <vector>
+
+#include "zsp.h"
+#include "zsp_internal.hpp"
+
+namespace zsp {
+struct CkptStaging;                    // pinned chunks, streams, events (zsp_ckpt_dev.cpp)
+void staging_free(CkptStaging* st);    // NULL is a no-op
+}  // namespace zsp
+
+struct zsp_plan {
+    int32_t T = 0;
+    int32_t nd = 0;
+    std::vector<int64_t> numel, pad, shard_len, full_off, shard_off, flat_off;
+    int64_t S = 0;
+    int64_t total_padded = 0;
+    int64_t total_numel = 0;
+
+    bool bound = false;
+    int32_t bind_rank = ZSP_ALL_RANKS;
+    int device = -1;
+    float* master = nullptr;
+    float* m = nullptr;
+    float* v = nullptr;
+    uint16_t* work = nullptr;
+    float* acc = nullptr;
+
+    void* dev_blob = nullptr;  // one device allocation holding both tables
+    zsp::ShardTable shard;
+    zsp::GatherTable gather;
+
+    zsp::CkptStaging* staging = nullptr;  // made by the first checkpoint save / load
+};
+

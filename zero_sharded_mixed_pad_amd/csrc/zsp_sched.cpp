@@ -28,6 +28,7 @@
 
 #include "zsp_entry.hpp"
 #include "zsp_internal.hpp"
+#include "zsp_plan.hpp"
 
 namespace {
 
