@@ -147,3 +147,28 @@ def test_more_ranks_than_lanes_and_stream_order(tmp_path):
     assert C.plan.checkpoint_load(zsp.ALL_RANKS, str(tmp_path), stream=s) == 2
     for got, want, name in zip(state_bits(C), state_bits(B), ("master", "m", "v", "work")):
         assert_bits(got, want, f"saved after the queued step: {name}")
+
+
+def test_reshard_of_a_state_spanning_many_chunks(tmp_path):
+    """Saved by 2 ranks, loaded by 3: each new array (S = 4.33M) spans more
+    than one 16 MiB staging chunk, so chunk windows split parameters."""
+    numels = [9_000_001, 4_000_003, 77]
+    A = Mirror(numels, 2, with_acc=False)
+    step(A, A.grads(torch.bfloat16, "big-reshard", poison=False), 1)
+    old = state_bits(A)
+    A.plan.checkpoint_save(zsp.ALL_RANKS, str(tmp_path), 1)
+    B = Mirror(numels, 3, with_acc=False)
+    torch.cuda.synchronize()
+    assert B.plan.checkpoint_load(zsp.ALL_RANKS, str(tmp_path)) == 1
+    got = state_bits(B)
+
+    def regathered(arr):
+        return np.concatenate([oracle.gather(numels, 2, t, arr) for t in range(len(numels))])
+
+    want_master, _, _, _ = oracle.partition(numels, 3, regathered(old[0]))
+    want_m, _, _, _ = oracle.partition(numels, 3, regathered(old[1]))
+    want_v, _, _, _ = oracle.partition(numels, 3, regathered(old[2]))
+    _, want_work, _, _ = oracle.partition(numels, 3, regathered(old[3]))
+    for g, w, name in zip(got, (want_master, want_m, want_v, want_work),
+                          ("master", "m", "v", "work")):
+        assert_bits(g, w, f"resharded 2->3, many chunks: {name}")

@@ -15,6 +15,10 @@
 // Files are written to a temporary name and renamed, so a crash mid-write
 // never leaves a truncated file under the final name.
 #include <dirent.h>
+#include <fcntl.h>
+#include <sys/mman.h>
+#include <sys/stat.h>
+#include <unistd.h>
 
 #include <algorithm>
 #include <cerrno>
@@ -191,75 +195,23 @@ CkptStatus finish_read(Reader* r, const std::string& path, std::string* err) {
 }  // namespace
 
 HostPayload::HostPayload(const float* master, const float* m, const float* v,
-                         const uint16_t* work, int64_t S)
-    : S_(S) {
-    seg_[0] = reinterpret_cast<char*>(const_cast<float*>(master));
-    seg_[1] = reinterpret_cast<char*>(const_cast<float*>(m));
-    seg_[2] = reinterpret_cast<char*>(const_cast<float*>(v));
-    seg_[3] = reinterpret_cast<char*>(const_cast<uint16_t*>(work));
-    set_segments(S);
-}
-
-HostPayload::HostPayload(std::vector<float>* master, std::vector<float>* m,
-                         std::vector<float>* v, std::vector<uint16_t>* work, int64_t S)
-    : vm_(master), vmm_(m), vv_(v), vw_(work), S_(S) {}
-
-void HostPayload::set_segments(int64_t S) {
+                         const uint16_t* work, int64_t S) {
+    seg_[0] = reinterpret_cast<const char*>(master);
+    seg_[1] = reinterpret_cast<const char*>(m);
+    seg_[2] = reinterpret_cast<const char*>(v);
+    seg_[3] = reinterpret_cast<const char*>(work);
     for (int i = 0; i < 4; ++i) len_[i] = size_t(S) * (i < 3 ? 4 : 2);
-    cur_ = 0;
-    off_ = 0;
 }
 
 bool HostPayload::next(const void** data, size_t* n, std::string*) {
-    while (cur_ < 4 && off_ == len_[cur_]) {
-        ++cur_;
-        off_ = 0;
-    }
+    while (cur_ < 4 && len_[cur_] == 0) ++cur_;
     if (cur_ == 4) {
         *n = 0;
         return true;
     }
-    *data = seg_[cur_] + off_;
-    *n = len_[cur_] - off_;
-    off_ = len_[cur_];
-    return true;
-}
-
-bool HostPayload::begin(int64_t S, std::string* err) {
-    if (S != S_) {
-        *err = "holds another parameter list";
-        return false;
-    }
-    if (vm_) {  // vectors: size them to the file's S
-        vm_->resize(size_t(S));
-        vmm_->resize(size_t(S));
-        vv_->resize(size_t(S));
-        vw_->resize(size_t(S));
-        seg_[0] = reinterpret_cast<char*>(vm_->data());
-        seg_[1] = reinterpret_cast<char*>(vmm_->data());
-        seg_[2] = reinterpret_cast<char*>(vv_->data());
-        seg_[3] = reinterpret_cast<char*>(vw_->data());
-    }
-    set_segments(S);
-    return true;
-}
-
-bool HostPayload::buffer(void** data, size_t* cap, std::string* err) {
-    while (cur_ < 4 && off_ == len_[cur_]) {
-        ++cur_;
-        off_ = 0;
-    }
-    if (cur_ == 4) {
-        *err = "payload longer than the arrays";
-        return false;
-    }
-    *data = seg_[cur_] + off_;
-    *cap = len_[cur_] - off_;
-    return true;
-}
-
-bool HostPayload::commit(size_t n, std::string*) {
-    off_ += n;
+    *data = seg_[cur_];
+    *n = len_[cur_];
+    ++cur_;
     return true;
 }
 
@@ -308,38 +260,6 @@ CkptStatus ckpt_write_rank(const char* dir, int32_t nd, int32_t rank,
     return CkptStatus::Ok;
 }
 
-CkptStatus ckpt_stream_rank(const char* dir, int32_t nd, int32_t rank,
-                            std::vector<int64_t>* numel, int64_t* S, int64_t* step,
-                            PayloadSink& sink, std::string* err) {
-    Reader r;
-    std::string path;
-    CkptStatus st = open_and_read_header(dir, nd, rank, &r, numel, S, step, &path, err);
-    if (st != CkptStatus::Ok) return st;
-    std::string why;
-    if (!r.ok || !sink.begin(*S, &why)) {
-        std::fclose(r.f);
-        *err = r.ok ? path + ": " + why : path + ": truncated or corrupt (hash mismatch)";
-        return r.ok ? CkptStatus::Io : CkptStatus::Corrupt;
-    }
-    int64_t left = ckpt_payload_bytes(*S);
-    while (left > 0 && r.ok) {
-        void* data = nullptr;
-        size_t cap = 0;
-        if (!sink.buffer(&data, &cap, &why)) break;
-        const size_t n = size_t(std::min<int64_t>(left, int64_t(cap)));
-        r.get(data, n);
-        if (!r.ok) break;
-        if (!sink.commit(n, &why)) break;
-        left -= int64_t(n);
-    }
-    if (left > 0 && r.ok) {  // the sink failed
-        std::fclose(r.f);
-        *err = path + ": " + why;
-        return CkptStatus::Io;
-    }
-    return finish_read(&r, path, err);
-}
-
 CkptStatus ckpt_verify_rank(const char* dir, int32_t nd, int32_t rank,
                             std::vector<int64_t>* numel, int64_t* S, int64_t* step,
                             void* scratch, size_t scratch_bytes, std::string* err) {
@@ -354,6 +274,39 @@ CkptStatus ckpt_verify_rank(const char* dir, int32_t nd, int32_t rank,
         left -= int64_t(n);
     }
     return finish_read(&r, path, err);
+}
+
+MappedRank::~MappedRank() {
+    if (base_) munmap(base_, len_);
+}
+
+CkptStatus MappedRank::map(const char* dir, int32_t nd, int32_t rank, int64_t T, int64_t S,
+                           std::string* err) {
+    const std::string path = rank_path(dir, rank, nd);
+    const size_t head = sizeof(kMagic) + 5 * sizeof(int64_t) + size_t(T) * sizeof(int64_t);
+    const size_t want = head + size_t(ckpt_payload_bytes(S)) + sizeof(uint64_t);
+    const int fd = open(path.c_str(), O_RDONLY);
+    if (fd < 0) {
+        *err = "cannot open " + path + ": " + std::strerror(errno);
+        return CkptStatus::Missing;
+    }
+    struct stat sb;
+    if (fstat(fd, &sb) != 0 || size_t(sb.st_size) != want) {
+        close(fd);
+        *err = path + ": changed since it was checked";
+        return CkptStatus::Corrupt;
+    }
+    void* p = mmap(nullptr, want, PROT_READ, MAP_PRIVATE, fd, 0);
+    close(fd);
+    if (p == MAP_FAILED) {
+        *err = "cannot map " + path + ": " + std::strerror(errno);
+        return CkptStatus::Io;
+    }
+    base_ = p;
+    len_ = want;
+    payload_ = static_cast<const char*>(p) + head;
+    S_ = S;
+    return CkptStatus::Ok;
 }
 
 // Number of ranks of the checkpoint in `dir`, from the names of the shard

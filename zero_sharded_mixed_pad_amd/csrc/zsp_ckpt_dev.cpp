@@ -10,10 +10,13 @@
 // separate host threads, so files are written or read in parallel:
 //   save: the device-to-host copy of chunk k+1 runs while chunk k is
 //         checksummed and written;
-//   load: every file is first read and checked whole (header, parameter
-//         list, checksum, one common step), so a bad checkpoint never
-//         touches device state; then each file is read again into the
-//         chunks, each chunk copied host-to-device while the next is read.
+//   load: every file the load needs (the loaded ranks' own files, or all
+//         of them under another rank count) is first read and checked whole
+//         (header, parameter list, checksum, one common step), so a bad
+//         checkpoint never touches device state; the checked files are then
+//         mapped read-only and each of the plan's shards is cut from them
+//         straight into the chunks, a chunk-sized window at a time, each
+//         chunk copied host-to-device while the next is cut.
 // The lanes' streams wait on an event taken on the caller's stream, so a
 // save or load follows the work queued there before the call; both return
 // after their copies are done.
@@ -22,6 +25,7 @@
 #include <algorithm>
 #include <atomic>
 #include <cstring>
+#include <memory>
 #include <mutex>
 #include <new>
 #include <string>
@@ -235,10 +239,11 @@ class DevSource : public PayloadSource {
     int issued_ = 0, consumed_ = 0;
 };
 
-// One rank's device state as a payload sink: the file side reads into a
-// pinned chunk, which is then copied host-to-device; a chunk is handed out
-// again only once its previous copy has finished.
-class DevSink : public PayloadSink {
+// One rank's device state filled through the lane's pinned chunks: the
+// caller writes a chunk, which is then copied host-to-device; a chunk is
+// handed out again only once its previous copy has finished. The state is
+// filled in payload order (master, m, v, work), each array whole.
+class DevSink {
   public:
     DevSink(Lane& lane, const zsp_plan* P, int64_t base) : lane_(lane), S_(P->S) {
         dst_[0] = reinterpret_cast<char*>(P->master + base);
@@ -247,14 +252,15 @@ class DevSink : public PayloadSink {
         dst_[3] = reinterpret_cast<char*>(P->work + base);
         for (int i = 0; i < 4; ++i) len_[i] = size_t(P->S) * (i < 3 ? 4 : 2);
     }
-    bool begin(int64_t S, std::string* err) override {
+    bool begin(int64_t S, std::string* err) {
         if (S != S_) {
             *err = "holds another parameter list";
             return false;
         }
         return true;
     }
-    bool buffer(void** data, size_t* cap, std::string* err) override {
+    // A chunk for the next bytes, at most *cap of them (never past an array).
+    bool buffer(void** data, size_t* cap, std::string* err) {
         while (seg_ < 4 && off_ == len_[seg_]) {
             ++seg_;
             off_ = 0;
@@ -275,7 +281,8 @@ class DevSink : public PayloadSink {
         *cap = std::min(kChunk, len_[seg_] - off_);
         return true;
     }
-    bool commit(size_t n, std::string* err) override {
+    // The chunk last handed out now holds the next n bytes.
+    bool commit(size_t n, std::string* err) {
         const int b = k_ % 2;
         hipError_t e = hipMemcpyAsync(dst_[seg_] + off_, lane_.buf[b], n, hipMemcpyHostToDevice,
                                       lane_.stream);
@@ -303,10 +310,7 @@ class DevSink : public PayloadSink {
 
 // ---- rank layouts and resharding -------------------------------------------
 
-struct HostShards {  // one rank's shard set on the host
-    std::vector<float> master, m, v;
-    std::vector<uint16_t> work;
-};
+constexpr size_t kVerifyChunk = size_t(8) << 20;  // read buffer of a verify pass
 
 struct RankLayout {
     std::vector<int64_t> shard_len, shard_off;
@@ -331,76 +335,99 @@ bool same_model(const zsp_plan* P, const std::vector<int64_t>& numel, int64_t S,
     return numel == P->numel && S == S_want;
 }
 
-// Every rank file of an nd_old-rank checkpoint read whole into host memory
-// (one lane per file), checked against the plan's parameter list and for
-// one common step.
-zsp_status read_all_ranks(const zsp_plan* P, const char* dir, int32_t nd_old,
-                          std::vector<HostShards>* out, int64_t* step) {
-    out->assign(size_t(nd_old), HostShards{});
-    std::vector<int64_t> steps(size_t(nd_old), 0);
-    const RankLayout Lo = rank_layout(P->numel, nd_old);
-    zsp_status st = run_lanes(nd_old, kLanes, -1, [&](int r, int, std::string* m) {
-        HostShards& h = (*out)[size_t(r)];
-        HostPayload sink(&h.master, &h.m, &h.v, &h.work, Lo.S);
+// The files of a checkpoint that a load needs: checked whole (one lane per
+// file), then mapped read-only, so that the plan's shards are cut from the
+// page cache without another copy. Under the plan's own rank count a shard
+// is one old file's payload; under another, it takes runs of every file.
+struct OldCheckpoint {
+    int32_t nd = 0;
+    RankLayout L;
+    std::vector<std::unique_ptr<MappedRank>> files;
+    std::vector<const float*> master, m, v;
+    std::vector<const uint16_t*> work;
+};
+
+// Check and map the files of the old ranks that the plan's ranks `ranks`
+// need (all of them under another rank count); the others stay unmapped.
+// The checked files must hold the plan's parameter list and one step.
+zsp_status open_old(const zsp_plan* P, const char* dir, int32_t nd_old,
+                    const std::vector<int32_t>& ranks, OldCheckpoint* old, int64_t* step) {
+    old->nd = nd_old;
+    old->L = rank_layout(P->numel, nd_old);
+    std::vector<int32_t> need;
+    if (nd_old == P->nd) {
+        need = ranks;
+    } else {
+        for (int32_t r = 0; r < nd_old; ++r) need.push_back(r);
+    }
+    const int n = int(need.size());
+    std::vector<int64_t> steps(size_t(n), 0);
+    zsp_status st = run_lanes(n, kLanes, -1, [&](int i, int, std::string* m) {
+        std::unique_ptr<char[]> scratch(new char[kVerifyChunk]);
         std::vector<int64_t> numel;
         int64_t S = 0;
-        const CkptStatus cs = ckpt_stream_rank(dir, nd_old, r, &numel, &S, &steps[size_t(r)],
-                                               sink, m);
-        if (cs != CkptStatus::Ok) return ZSP_EIO;
-        if (!same_model(P, numel, S, Lo.S)) {
+        if (ckpt_verify_rank(dir, nd_old, need[size_t(i)], &numel, &S, &steps[size_t(i)],
+                             scratch.get(), kVerifyChunk, m) != CkptStatus::Ok)
+            return ZSP_EIO;
+        if (!same_model(P, numel, S, old->L.S)) {
             *m = std::string("checkpoint in ") + dir + " holds another parameter list";
             return ZSP_EIO;
         }
         return ZSP_OK;
     });
     if (st != ZSP_OK) return st;
-    for (int32_t r = 1; r < nd_old; ++r)
-        if (steps[size_t(r)] != steps[0])
+    for (int i = 1; i < n; ++i)
+        if (steps[size_t(i)] != steps[0])
             return set_error(ZSP_EIO, "checkpoint in %s mixes steps %lld and %lld", dir,
-                             (long long)steps[0], (long long)steps[size_t(r)]);
-    *step = steps[0];
+                             (long long)steps[0], (long long)steps[size_t(i)]);
+    *step = n > 0 ? steps[0] : 0;
+    old->files.resize(size_t(nd_old));
+    old->master.assign(size_t(nd_old), nullptr);
+    old->m.assign(size_t(nd_old), nullptr);
+    old->v.assign(size_t(nd_old), nullptr);
+    old->work.assign(size_t(nd_old), nullptr);
+    for (int32_t r : need) {
+        std::unique_ptr<MappedRank> f(new MappedRank);
+        std::string err;
+        if (f->map(dir, nd_old, r, P->T, old->L.S, &err) != CkptStatus::Ok)
+            return set_error(ZSP_EIO, "%s", err.c_str());
+        old->master[size_t(r)] = f->master();
+        old->m[size_t(r)] = f->m();
+        old->v[size_t(r)] = f->v();
+        old->work[size_t(r)] = f->work();
+        old->files[size_t(r)] = std::move(f);
+    }
     return ZSP_OK;
 }
 
-// Rank j's shard set under the plan's layout, cut from the old ranks'
-// shards: element k of parameter t lives in old rank k / s_old at
-// k - r*s_old of its slice; pads are +0.
+// Elements [e_lo, e_hi) of rank j's shard array under the plan's layout,
+// cut from the old ranks' arrays: element k of parameter t lives in old
+// rank k / s_old at k - r*s_old of its slice; pads are +0.
 template <typename T>
-void reshard_array(const zsp_plan* P, const RankLayout& Lo, int32_t j,
-                   const std::vector<const T*>& old, T* out) {
-    for (int32_t t = 0; t < P->T; ++t) {
-        const int64_t s = P->shard_len[t], so = Lo.shard_len[t];
-        int64_t dst = P->shard_off[t];
-        int64_t k = int64_t(j) * s;
-        const int64_t kend = std::min<int64_t>(P->numel[t], k + s);
+void reshard_range(const zsp_plan* P, const RankLayout& Lo, int32_t j,
+                   const std::vector<const T*>& old, int64_t e_lo, int64_t e_hi, T* out) {
+    // last parameter starting at or before e_lo
+    int32_t t = int32_t(std::upper_bound(P->shard_off.begin(), P->shard_off.end(), e_lo) -
+                        P->shard_off.begin()) - 1;
+    for (t = std::max(t, 0); t < P->T && P->shard_off[size_t(t)] < e_hi; ++t) {
+        const int64_t s = P->shard_len[size_t(t)], so = Lo.shard_len[size_t(t)];
+        const int64_t off = P->shard_off[size_t(t)];
+        const int64_t i0 = std::max(e_lo, off) - off, i1 = std::min(e_hi, off + s) - off;
+        if (i0 >= i1) continue;
+        T* dst = out + (off + i0 - e_lo);
+        int64_t k = int64_t(j) * s + i0;
+        const int64_t k_slot_end = int64_t(j) * s + i1;
+        const int64_t kend = std::min<int64_t>(P->numel[size_t(t)], k_slot_end);
         while (k < kend) {
             const int64_t r = k / so;
             const int64_t run_end = std::min<int64_t>(kend, (r + 1) * so);
-            std::memcpy(out + dst, old[size_t(r)] + Lo.shard_off[t] + (k - r * so),
+            std::memcpy(dst, old[size_t(r)] + Lo.shard_off[size_t(t)] + (k - r * so),
                         size_t(run_end - k) * sizeof(T));
             dst += run_end - k;
             k = run_end;
         }
-        const int64_t end = P->shard_off[t] + s;
-        if (dst < end) std::memset(out + dst, 0, size_t(end - dst) * sizeof(T));
+        if (k < k_slot_end) std::memset(dst, 0, size_t(k_slot_end - k) * sizeof(T));
     }
-}
-
-void reshard_rank(const zsp_plan* P, int32_t nd_old, const std::vector<HostShards>& old,
-                  int32_t j, float* master, float* m, float* v, uint16_t* work) {
-    const RankLayout Lo = rank_layout(P->numel, nd_old);
-    std::vector<const float*> pm, pmm, pv;
-    std::vector<const uint16_t*> pw;
-    for (const HostShards& h : old) {
-        pm.push_back(h.master.data());
-        pmm.push_back(h.m.data());
-        pv.push_back(h.v.data());
-        pw.push_back(h.work.data());
-    }
-    reshard_array(P, Lo, j, pm, master);
-    reshard_array(P, Lo, j, pmm, m);
-    reshard_array(P, Lo, j, pv, v);
-    reshard_array(P, Lo, j, pw, work);
 }
 
 // Ranks a save/load call covers under the plan's binding.
@@ -472,21 +499,13 @@ zsp_status zsp_checkpoint_read_host(const zsp_plan* P, int32_t rank, const char*
     zsp_status st = find_checkpoint(dir, &nd_old);
     if (st != ZSP_OK) return st;
     try {
-        if (nd_old == P->nd) {
-            HostPayload sink(master, m, v, work, P->S);
-            std::vector<int64_t> numel;
-            int64_t S = 0;
-            std::string err;
-            if (ckpt_stream_rank(dir, P->nd, rank, &numel, &S, step, sink, &err) !=
-                CkptStatus::Ok)
-                return set_error(ZSP_EIO, "%s", err.c_str());
-            if (!same_model(P, numel, S, P->S))
-                return set_error(ZSP_EIO, "checkpoint in %s holds another parameter list", dir);
-            return ZSP_OK;
-        }
-        std::vector<HostShards> old;
-        if ((st = read_all_ranks(P, dir, nd_old, &old, step)) != ZSP_OK) return st;
-        reshard_rank(P, nd_old, old, rank, master, m, v, work);
+        OldCheckpoint old;
+        if ((st = open_old(P, dir, nd_old, std::vector<int32_t>{rank}, &old, step)) != ZSP_OK)
+            return st;
+        reshard_range(P, old.L, rank, old.master, 0, P->S, master);
+        reshard_range(P, old.L, rank, old.m, 0, P->S, m);
+        reshard_range(P, old.L, rank, old.v, 0, P->S, v);
+        reshard_range(P, old.L, rank, old.work, 0, P->S, work);
     } catch (const std::bad_alloc&) {
         return set_error(ZSP_ENOMEM, "out of host memory reading the checkpoint");
     }
@@ -533,89 +552,35 @@ zsp_status zsp_checkpoint_load(zsp_plan* P, int32_t rank_or_all, const char* dir
     CkptStaging* stg = nullptr;
     if ((st = get_staging(P, lanes, &stg)) != ZSP_OK) return st;
     try {
-        if (nd_old == P->nd) {
-            // pass 1: every file whole and consistent before any device write
-            std::vector<int64_t> steps(size_t(n), 0);
-            st = run_lanes(n, lanes, -1, [&](int i, int lane, std::string* m) {
-                std::vector<int64_t> numel;
-                int64_t S = 0;
-                const CkptStatus cs =
-                    ckpt_verify_rank(dir, P->nd, ranks[size_t(i)], &numel, &S, &steps[size_t(i)],
-                                     stg->lanes[size_t(lane)].buf[0], kChunk, m);
-                if (cs != CkptStatus::Ok) return ZSP_EIO;
-                if (!same_model(P, numel, S, P->S)) {
-                    *m = std::string("checkpoint in ") + dir + " holds another parameter list";
-                    return ZSP_EIO;
-                }
-                return ZSP_OK;
-            });
-            if (st != ZSP_OK) return st;
-            for (int i = 1; i < n; ++i)
-                if (steps[size_t(i)] != steps[0])
-                    return set_error(ZSP_EIO, "checkpoint in %s mixes steps %lld and %lld", dir,
-                                     (long long)steps[0], (long long)steps[size_t(i)]);
-            *step = steps[0];
-            // pass 2: stream the files into the device state
-            if ((st = follow_caller(stg, lanes, static_cast<hipStream_t>(stream))) != ZSP_OK)
-                return st;
-            return run_lanes(n, lanes, P->device, [&](int i, int lane, std::string* m) {
-                Lane& L = stg->lanes[size_t(lane)];
-                const int32_t r = ranks[size_t(i)];
-                DevSink sink(L, P, rank_base(P, r));
-                std::vector<int64_t> numel;
-                int64_t S = 0, st_r = 0;
-                const CkptStatus cs = ckpt_stream_rank(dir, P->nd, r, &numel, &S, &st_r, sink, m);
-                const hipError_t e = hipStreamSynchronize(L.stream);
-                if (cs != CkptStatus::Ok) return ZSP_EIO;
-                if (e != hipSuccess) {
-                    *m = hip_text(e, "host-to-device copy");
-                    return ZSP_EHIP;
-                }
-                return ZSP_OK;
-            });
-        }
-        // another rank count: read every old file, then cut each new shard
-        std::vector<HostShards> old;
-        if ((st = read_all_ranks(P, dir, nd_old, &old, step)) != ZSP_OK) return st;
+        // check and map the files needed, then cut each of the plan's shards
+        // into the pinned chunks, a chunk at a time
+        OldCheckpoint old;
+        if ((st = open_old(P, dir, nd_old, ranks, &old, step)) != ZSP_OK) return st;
         if ((st = follow_caller(stg, lanes, static_cast<hipStream_t>(stream))) != ZSP_OK)
             return st;
         return run_lanes(n, lanes, P->device, [&](int i, int lane, std::string* m) {
             Lane& L = stg->lanes[size_t(lane)];
             const int32_t r = ranks[size_t(i)];
-            HostShards h;
-            h.master.resize(size_t(P->S));
-            h.m.resize(size_t(P->S));
-            h.v.resize(size_t(P->S));
-            h.work.resize(size_t(P->S));
-            reshard_rank(P, nd_old, old, r, h.master.data(), h.m.data(), h.v.data(),
-                         h.work.data());
-            HostPayload src(h.master.data(), h.m.data(), h.v.data(), h.work.data(), P->S);
             DevSink sink(L, P, rank_base(P, r));
-            std::string why;
-            bool ok = sink.begin(P->S, &why);
-            while (ok) {  // host payload -> pinned chunk -> device
-                const void* data = nullptr;
-                size_t len = 0;
-                ok = src.next(&data, &len, &why);
-                if (!ok || len == 0) break;
-                const char* p = static_cast<const char*>(data);
-                while (ok && len > 0) {
+            bool ok = sink.begin(P->S, m);
+            for (int a = 0; a < 4 && ok; ++a) {  // master, m, v, work: payload order
+                const size_t esz = a < 3 ? sizeof(float) : sizeof(uint16_t);
+                for (int64_t e = 0; ok && e < P->S;) {
                     void* buf = nullptr;
                     size_t cap = 0;
-                    ok = sink.buffer(&buf, &cap, &why);
+                    ok = sink.buffer(&buf, &cap, m);
                     if (!ok) break;
-                    const size_t c = std::min(cap, len);
-                    std::memcpy(buf, p, c);
-                    ok = sink.commit(c, &why);
-                    p += c;
-                    len -= c;
+                    const int64_t cnt = int64_t(cap / esz);
+                    if (a == 0) reshard_range(P, old.L, r, old.master, e, e + cnt, (float*)buf);
+                    if (a == 1) reshard_range(P, old.L, r, old.m, e, e + cnt, (float*)buf);
+                    if (a == 2) reshard_range(P, old.L, r, old.v, e, e + cnt, (float*)buf);
+                    if (a == 3) reshard_range(P, old.L, r, old.work, e, e + cnt, (uint16_t*)buf);
+                    ok = sink.commit(size_t(cnt) * esz, m);
+                    e += cnt;
                 }
             }
             const hipError_t e = hipStreamSynchronize(L.stream);
-            if (!ok) {
-                *m = why;
-                return ZSP_EHIP;
-            }
+            if (!ok) return ZSP_EHIP;
             if (e != hipSuccess) {
                 *m = hip_text(e, "host-to-device copy");
                 return ZSP_EHIP;
