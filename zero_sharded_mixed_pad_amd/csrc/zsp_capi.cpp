@@ -169,6 +169,7 @@ zsp_status zsp_partition(const int64_t* numel, int32_t n_params, int32_t n_d, zs
         P->full_off.assign(n_params + 1, 0);
         P->shard_off.assign(n_params + 1, 0);
         P->flat_off.assign(n_params + 1, 0);
+        P->piece_off.assign(n_params + 1, 0);
         const int64_t kMax = int64_t(1) << 60;
         for (int32_t t = 0; t < n_params; ++t) {
             const int64_t n = numel[t];
@@ -186,6 +187,9 @@ zsp_status zsp_partition(const int64_t* numel, int32_t n_params, int32_t n_d, zs
             P->full_off[t + 1] = P->full_off[t] + n + pad;
             P->shard_off[t + 1] = P->shard_off[t] + P->shard_len[t];
             P->flat_off[t + 1] = P->flat_off[t] + n;
+            // ranks holding real elements of t: one gather piece each
+            const int64_t s_t = P->shard_len[t];
+            P->piece_off[t + 1] = P->piece_off[t] + (n == 0 ? 0 : (n + s_t - 1) / s_t);
         }
         P->S = P->shard_off[n_params];
         P->total_padded = P->full_off[n_params];
@@ -423,6 +427,8 @@ zsp_status zsp::gather_range(zsp_plan* P, int32_t first_param, int32_t n_params,
             : src == ZSP_SRC_MASTER ? static_cast<const void*>(P->master)
                                     : static_cast<const void*>(P->acc);
     L.out = out;
+    const int64_t pieces = P->piece_off[first_param + n_params] - P->piece_off[first_param];
+    L.short_pieces = pieces > 0 && count < pieces * zsp::kShortPiece;
     hipError_t e = zsp::launch_gather(L, src == ZSP_SRC_WORK ? ZSP_BF16 : ZSP_F32, stream);
     if (e != hipSuccess) return fail_hip(e, "gather launch");
     return ZSP_OK;

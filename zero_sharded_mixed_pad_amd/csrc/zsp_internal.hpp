@@ -110,7 +110,12 @@ struct GatherLaunch {
     int64_t count = 0;    // elements to write
     const void* src = nullptr;
     void* out = nullptr;
+    bool short_pieces = false;  // pieces average under kShortPiece elements
 };
+
+// Below this average piece length (elements) a gather takes its short-piece
+// form: shared boundary lines make up a few percent of the bytes or more.
+constexpr int64_t kShortPiece = 4096;
 
 // Launch one E-space operation; dtype is the gradient / parameter dtype.
 hipError_t launch_shard_op(const ShardLaunch& L, ShardOp op, zsp_dtype dtype,

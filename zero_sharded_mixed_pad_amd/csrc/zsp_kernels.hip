@@ -59,6 +59,7 @@ constexpr int kHalf = kTile / 2;  // second quad of a lane is this far on
 // *_a2 / *_a4 typedefs (they are the same type as the aligned vector).
 __device__ __forceinline__ u32x2 ldnt_x2_a2(const u32x2_a2* p) { return __builtin_nontemporal_load(p); }
 __device__ __forceinline__ u32x4 ldnt_x4_a2(const u32x4_a2* p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ u32x4 ld_x4_a2(const u32x4_a2* p) { return *p; }
 __device__ __forceinline__ u32x4 ldnt_x4_a4(const u32x4_a4* p) { return __builtin_nontemporal_load(p); }
 __device__ __forceinline__ f32x4 ldnt_f32x4(const f32x4* p) { return __builtin_nontemporal_load(p); }
 __device__ __forceinline__ void stnt(f32x4* p, f32x4 v) { __builtin_nontemporal_store(v, p); }
@@ -600,14 +601,35 @@ struct GatherShape {
 // register selects: one scalar round trip, like a single-piece tile.
 constexpr int kPick = 8;
 
+// Gathers over short pieces (many parameters of a few thousand elements):
+// a piece starts at any element offset, so its first and last cache lines
+// are shared with the neighbouring pieces, which neighbouring tiles read.
+// Such launches load their sources with ordinary (L2-allocating) loads and
+// give each XCD runs of kXcdRun consecutive tiles (workgroup b runs on XCD
+// b % 8), so a shared line is fetched once into that XCD's L2. Long pieces
+// keep non-temporal loads and the plain order: each line is read once.
+constexpr int kXcdRun = 16;
+
+template <bool SHORT>
+__device__ __forceinline__ u32x4 ld_src(const u32x4_a2* p) {
+    if constexpr (SHORT) return ld_x4_a2(p);
+    else return ldnt_x4_a2(p);
+}
+
 // out[k] = src[K + delta(piece of K)], K = k_first + k, k < count.
-template <typename T>
+template <typename T, bool SHORT>
 __global__ __launch_bounds__(kWaveLanes) void gather_kernel(const GatherArgs a) {
     using S = GatherShape<T>;
     __shared__ int64_t s_k0[kStage + 1];
     __shared__ int64_t s_delta[kStage];
     const int lane = threadIdx.x;
-    const int64_t kw = int64_t(blockIdx.x) * kTile;  // local start of the wave's tile
+    int64_t tile = blockIdx.x;
+    if constexpr (SHORT) {
+        const int64_t x = tile % 8, i = tile / 8;
+        tile = ((i / kXcdRun) * 8 + x) * kXcdRun + (i % kXcdRun);
+        if (tile * kTile >= a.count) return;  // the grid is rounded up to 8 runs
+    }
+    const int64_t kw = tile * kTile;  // local start of the wave's tile
     const int64_t kw_last = a.k_first + min(kw + kTile, a.count) - 1;
     const int lo = a.tile[(a.k_first + kw) / kTile];
     const int hi = a.tile[kw_last / kTile + 1];
@@ -627,7 +649,7 @@ __global__ __launch_bounds__(kWaveLanes) void gather_kernel(const GatherArgs a) 
             for (int h = 0; h < S::kGroups; ++h) {
                 const uint32_t o = h * S::kStride + uint32_t(lane) * S::kLaneStep;
                 stnt(reinterpret_cast<u32x4*>(ob + o),
-                     ldnt_x4_a2(reinterpret_cast<const u32x4_a2*>(sb + o)));
+                     ld_src<SHORT>(reinterpret_cast<const u32x4_a2*>(sb + o)));
             }
             return;
         }
@@ -660,7 +682,7 @@ __global__ __launch_bounds__(kWaveLanes) void gather_kernel(const GatherArgs a) 
             pick(K, next, d);
             if (k + S::kGroup <= a.count && K + S::kGroup <= next) {
                 stnt(reinterpret_cast<u32x4*>(out + k),
-                     ldnt_x4_a2(reinterpret_cast<const u32x4_a2*>(src + K + d)));
+                     ld_src<SHORT>(reinterpret_cast<const u32x4_a2*>(src + K + d)));
             } else {
                 // Crosses a piece boundary or the end: each element picks its
                 // own piece; every load is issued unconditionally.
@@ -701,7 +723,7 @@ __global__ __launch_bounds__(kWaveLanes) void gather_kernel(const GatherArgs a) 
         int64_t d = delta[q];
         if (k + S::kGroup <= a.count && K + S::kGroup <= next) {
             // src may sit at any element offset; out + k is 16-byte aligned.
-            const u32x4 x = ldnt_x4_a2(reinterpret_cast<const u32x4_a2*>(src + K + d));
+            const u32x4 x = ld_src<SHORT>(reinterpret_cast<const u32x4_a2*>(src + K + d));
             stnt(reinterpret_cast<u32x4*>(out + k), x);
         } else {
             for (int i = 0; i < S::kGroup; ++i) {
@@ -793,14 +815,22 @@ hipError_t launch_gather(const GatherLaunch& L, zsp_dtype dtype, hipStream_t str
     a.count = L.count;
     a.src = L.src;
     a.out = L.out;
-    const int64_t blocks = (L.count + kTile - 1) / kTile;  // one wave per 512 outputs
+    const int64_t tiles = (L.count + kTile - 1) / kTile;  // one wave per 512 outputs
+    const int64_t runs = 8 * kXcdRun;
+    const int64_t blocks = L.short_pieces ? (tiles + runs - 1) / runs * runs : tiles;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-    if (dtype == ZSP_BF16)
-        hipLaunchKernelGGL(gather_kernel<uint16_t>, dim3(static_cast<uint32_t>(blocks)),
-                           dim3(kWaveLanes), 0, stream, a);
-    else
-        hipLaunchKernelGGL(gather_kernel<float>, dim3(static_cast<uint32_t>(blocks)),
-                           dim3(kWaveLanes), 0, stream, a);
+    const dim3 grid(static_cast<uint32_t>(blocks)), block(kWaveLanes);
+    if (dtype == ZSP_BF16) {
+        if (L.short_pieces)
+            hipLaunchKernelGGL((gather_kernel<uint16_t, true>), grid, block, 0, stream, a);
+        else
+            hipLaunchKernelGGL((gather_kernel<uint16_t, false>), grid, block, 0, stream, a);
+    } else {
+        if (L.short_pieces)
+            hipLaunchKernelGGL((gather_kernel<float, true>), grid, block, 0, stream, a);
+        else
+            hipLaunchKernelGGL((gather_kernel<float, false>), grid, block, 0, stream, a);
+    }
     return hipGetLastError();
 }
 
