@@ -80,6 +80,8 @@ def parse():
                          "in a fresh directory under DIR, check the bits, print one JSON line")
     ap.add_argument("--stage", type=int, choices=[1, 2, 3], default=3,
                     help="ZeRO stage whose step schedule runs (3: the partitioned hot path)")
+    ap.add_argument("--split", action="store_true",
+                    help="unfused update: reduce into the accumulator, then Adam from it")
     ap.add_argument("--prefetch", action="store_true",
                     help="instead of the step: time forward+backward passes of a Llama-7B "
                          "decoder stack through the per-layer gather schedule at several "
@@ -108,13 +110,13 @@ class Runner:
     With micro-batches, stages 2 and 3 reduce per micro-batch and accumulate
     the reduced slices; stage 1 all-reduces once per step."""
 
-    def __init__(self, w, device, stage=3):
+    def __init__(self, w, device, stage=3, split=False):
         import torch
         import zero_sharded_mixed_pad_amd as zsp
         from zero_sharded_mixed_pad_amd import synth
 
         self.torch, self.zsp, self.synth = torch, zsp, synth
-        self.w, self.dev, self.stage = w, device, stage
+        self.w, self.dev, self.stage, self.split = w, device, stage, split
         if stage < 3 and w.rank_local >= 0:
             raise ValueError("stages 1 and 2 gather every rank's shard; the workload holds one")
         self.plan = zsp.partition(w.numel, w.n_d)
@@ -126,7 +128,7 @@ class Runner:
         self.m = torch.empty(n_state, dtype=f32, device=device)
         self.v = torch.empty(n_state, dtype=f32, device=device)
         self.work = torch.empty(n_state, dtype=bf16, device=device)
-        need_acc = w.micro_batches > 1 or stage == 1
+        need_acc = w.micro_batches > 1 or stage == 1 or split
         self.acc = torch.empty(n_state, dtype=f32, device=device) if need_acc else None
         # stage 1: every rank's full fp32 gradient after the all-reduce
         self.grad_replica = (torch.empty(self.plan.total_numel, dtype=f32, device=device)
@@ -196,7 +198,12 @@ class Runner:
                 self._timed("gather", lambda first=first, n=n, out=out: p.gather_many(
                     first, n, out, "work"), record)
             return
-        if w.micro_batches > 1:
+        if self.split:  # unfused: reduce into the accumulator, then Adam from it
+            for mb in range(w.micro_batches):
+                self._timed("reduce", lambda mb=mb: p.reduce_shard(
+                    self.rank, self.grads, layout=self.layout, accumulate=mb > 0), record)
+            self._timed("adam", lambda: p.adam_step(self.rank, **hp), record)
+        elif w.micro_batches > 1:
             for mb in range(w.micro_batches - 1):
                 self._timed("reduce", lambda mb=mb: p.reduce_shard(
                     self.rank, self.grads, layout=self.layout, accumulate=mb > 0), record)
@@ -217,9 +224,13 @@ class Runner:
         gathers = sum(g[3] for g in self.gather_groups)
         if self.stage == 1:
             return self.bytes_reduce_first + self.bytes_gather_acc + self.bytes_adam + gathers
-        b = self.bytes_fused
-        if w.micro_batches > 1:
-            b += self.bytes_reduce_first + (w.micro_batches - 2) * self.bytes_reduce_acc
+        if self.split:
+            b = (self.bytes_reduce_first + (w.micro_batches - 1) * self.bytes_reduce_acc
+                 + self.bytes_adam)
+        else:
+            b = self.bytes_fused
+            if w.micro_batches > 1:
+                b += self.bytes_reduce_first + (w.micro_batches - 2) * self.bytes_reduce_acc
         b += (2 if self.stage == 3 else 1) * gathers
         return b
 
@@ -236,6 +247,8 @@ class Runner:
             elif kind == "reduce":
                 if self.stage == 1:
                     nb = [self.bytes_reduce_first]
+                elif self.split:
+                    nb = [self.bytes_reduce_first] + [self.bytes_reduce_acc] * (w.micro_batches - 1)
                 else:
                     nb = [self.bytes_reduce_first] + [self.bytes_reduce_acc] * (w.micro_batches - 2)
                 nbytes = sum(nb) / len(nb)
@@ -624,7 +637,7 @@ def main():
         traffic_from(args.traffic_from[0], args.traffic_from[1], args.workload)
         return 0
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU: this build has no multi-GPU path "
+        print(f"bench.py runs on one GPU: the library has no multi-GPU path "
               f"(asked for --gpus {args.gpus}).", file=sys.stderr)
         return 2
 
@@ -645,7 +658,7 @@ def main():
         print(json.dumps({"mode": "prefetch", "steps": args.steps, "warmup": args.warmup,
                           **res}), flush=True)
         return 0
-    r = Runner(w, device, args.stage)
+    r = Runner(w, device, args.stage, args.split)
     if args.checkpoint:
         res = checkpoint_bench(r, args.checkpoint)
         print(json.dumps({"mode": "checkpoint", "workload": w.name, "n_d": w.n_d, **res}),
