@@ -157,16 +157,30 @@ CkptStatus open_and_read_header(const char* dir, int32_t nd, int32_t rank, Reade
         *err = "cannot open " + *path + ": " + std::strerror(errno);
         return CkptStatus::Missing;
     }
+    struct stat sb;
+    const bool sized = fstat(fileno(r->f), &sb) == 0;
     char magic[8];
     int64_t hdr[5];
     r->get(magic, sizeof(magic));
     r->get(hdr, sizeof(hdr));
-    if (!r->ok || std::memcmp(magic, kMagic, 8) != 0 || hdr[0] != nd || hdr[1] != rank ||
-        hdr[2] < 1 || hdr[2] > (int64_t(1) << 31) || hdr[3] < 0 || hdr[3] > (int64_t(1) << 40)) {
+    if (!sized || !r->ok || std::memcmp(magic, kMagic, 8) != 0 || hdr[0] != nd ||
+        hdr[1] != rank || hdr[2] < 1 || hdr[2] > (int64_t(1) << 31) || hdr[3] < 0 ||
+        hdr[3] > (int64_t(1) << 40)) {
         std::fclose(r->f);
         r->f = nullptr;
         *err = *path + ": not a shard file of rank " + std::to_string(rank) + " of " +
                std::to_string(nd);
+        return CkptStatus::Corrupt;
+    }
+    // The header fixes the file's length; check it before sizing anything
+    // from the header (the bounds above keep this sum far from overflow).
+    const int64_t want = int64_t(sizeof(kMagic)) + int64_t(sizeof(hdr)) + 8 * hdr[2] +
+                         ckpt_payload_bytes(hdr[3]) + int64_t(sizeof(uint64_t));
+    if (int64_t(sb.st_size) != want) {
+        std::fclose(r->f);
+        r->f = nullptr;
+        *err = *path + ": truncated or corrupt (" + std::to_string(sb.st_size) +
+               " bytes, its header needs " + std::to_string(want) + ")";
         return CkptStatus::Corrupt;
     }
     numel->resize(size_t(hdr[2]));
