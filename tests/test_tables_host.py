@@ -2,7 +2,8 @@
 (CPU only): pieces ordered and non-empty, every gradient / parameter /
 gather source range inside its buffer, and each tile-table entry naming the
 piece that holds the tile's first element. Built from the library's own host
-code with g++ and driven over small edge cases and the full workloads."""
+code with g++ (AddressSanitizer and UBSan on) and driven over small edge
+cases and the full workloads."""
 import os
 import subprocess
 
@@ -17,7 +18,8 @@ CSRC = os.path.join(ROOT, "zero_sharded_mixed_pad_amd", "csrc")
 @pytest.fixture(scope="module")
 def checker(tmp_path_factory):
     exe = str(tmp_path_factory.mktemp("tables") / "table_check")
-    subprocess.run(["g++", "-std=c++17", "-O1", "-D__HIP_PLATFORM_AMD__",
+    subprocess.run(["g++", "-std=c++17", "-O1", "-g", "-fsanitize=address,undefined",
+                    "-fno-sanitize-recover=undefined", "-D__HIP_PLATFORM_AMD__",
                     "-I", "/opt/rocm/include", "-I", os.path.join(ROOT, "include"), "-I", CSRC,
                     os.path.join(ROOT, "tests", "table_check.cpp"),
                     os.path.join(CSRC, "zsp_layout.cpp"), "-o", exe], check=True)
@@ -26,7 +28,9 @@ def checker(tmp_path_factory):
 
 def run(exe, numels, nd, rank):
     inp = f"{nd} {rank} {len(numels)} " + " ".join(str(n) for n in numels)
-    res = subprocess.run([exe], input=inp.encode(), stdout=subprocess.PIPE, timeout=600)
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:verify_asan_link_order=0")
+    res = subprocess.run([exe], input=inp.encode(), stdout=subprocess.PIPE,
+                         stderr=subprocess.STDOUT, timeout=600, env=env)
     out = res.stdout.decode()
     assert res.returncode == 0 and out.startswith("ok"), out
 
