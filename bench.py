@@ -460,6 +460,15 @@ def prefetch_bench(args, device):
 # ---------------------------------------------------------------------------
 
 def cpu_baseline(runner, target_s):
+    """The oracle as it stands, timed on the host on a bounded sample of the
+    workload: one virtual rank's reduce over the N_d gradient buffers + Adam +
+    cast, plus a share of the parameter gathers. Measured twice for about
+    target_s each: on one thread, and on one thread per host core of the
+    process's CPU share (at most 16), each thread updating its own copy of a
+    rank's state (the ranks are independent; the oracle's C calls release
+    Python's lock)."""
+    import threading
+
     import numpy as np
     import torch
     import oracle
@@ -474,45 +483,73 @@ def cpu_baseline(runner, target_s):
             return t.view(torch.int16).numpy().view(np.uint16)
         return t.numpy()
 
-    j = w.rank_local if w.rank_local >= 0 else 0
     S = runner.plan.S
-    base = 0 if w.rank_local >= 0 else j * S
     grads = [host(g) for g in runner.grads]
-    master = host(runner.master[base:base + S]).copy()
-    m = host(runner.m[base:base + S]).copy()
-    v = host(runner.v[base:base + S]).copy()
-    work = host(runner.work[base:base + S]).copy()
     all_work = host(runner.work) if w.rank_local < 0 else None
     layout = oracle.GRADS_SHARD if w.rank_local >= 0 else oracle.GRADS_FULL
     L = oracle.Layout(w.numel, nd)
-    valid = int(sum(max(0, min(int(L.shard_len[t]), int(L.numel[t]) - j * int(L.shard_len[t])))
-                    for t in range(L.T)))
     gb = 2 if w.grad_dtype == torch.bfloat16 else 4
-    fused_bytes = valid * (nd * gb + 26)
-    gather_bytes = L.total_numel * 4 if all_work is not None else 0
 
-    done_bytes, t0, passes = 0, time.perf_counter(), 0
-    while True:
-        red = oracle.reduce(w.numel, nd, j, grads, layout)
-        oracle.adam(w.numel, nd, j, master, m, v, work, red, w.lr, w.beta1, w.beta2, w.eps,
-                    passes + 1)
-        done_bytes += fused_bytes
-        if all_work is not None:
-            for t in range(L.T):
+    def rank_state(j):
+        base = 0 if w.rank_local >= 0 else j * S
+        return [host(x[base:base + S]).copy() for x in (runner.master, runner.m, runner.v,
+                                                         runner.work)]
+
+    def valid_of(j):
+        return int(sum(max(0, min(int(L.shard_len[t]), int(L.numel[t]) - j * int(L.shard_len[t])))
+                       for t in range(L.T)))
+
+    def worker(j, gather_ids, out):
+        master, m, v, work = rank_state(j)
+        fused_bytes = valid_of(j) * (nd * gb + 26)
+        gather_bytes = sum(int(L.numel[t]) * 4 for t in gather_ids)
+        done, passes, t0 = 0, 0, time.perf_counter()
+        while True:
+            red = oracle.reduce(w.numel, nd, j, grads, layout)
+            oracle.adam(w.numel, nd, j, master, m, v, work, red, w.lr, w.beta1, w.beta2, w.eps,
+                        passes + 1)
+            for t in gather_ids:
                 oracle.gather(w.numel, nd, t, all_work)
-            done_bytes += gather_bytes
-        passes += 1
+            done += fused_bytes + gather_bytes
+            passes += 1
+            el = time.perf_counter() - t0
+            if el >= target_s or el * (passes + 1) / passes > 3 * target_s:
+                break
+        out.append((done, passes))
+
+    def run(threads):
+        ranks = [(w.rank_local if w.rank_local >= 0 else i % nd) for i in range(threads)]
+        gathers = [[t for t in range(L.T) if t % threads == i] if all_work is not None else []
+                   for i in range(threads)]
+        outs = [[] for _ in range(threads)]
+        ts = [threading.Thread(target=worker, args=(ranks[i], gathers[i], outs[i]))
+              for i in range(threads)]
+        t0 = time.perf_counter()
+        for t in ts:
+            t.start()
+        for t in ts:
+            t.join()
         el = time.perf_counter() - t0
-        if el >= target_s or el * (passes + 1) / passes > 3 * target_s:
-            break
-    el = time.perf_counter() - t0
-    what = (f"rank {j}'s reduce over {nd} gradient buffers + Adam + cast on its "
-            f"{valid:,}-element shard")
-    if all_work is not None:
-        what += f", plus one gather of all {L.T} parameters"
-    return {"value": round(done_bytes / el / 1e9, 3), "unit": "GB/s", "cores": 1,
-            "kind": "oracle", "seconds": round(el, 2),
-            "sample": f"{passes} pass(es) of {what} (single-threaded C oracle)"}
+        return sum(o[0][0] for o in outs) / el / 1e9, el, min(o[0][1] for o in outs)
+
+    one, el1, p1 = run(1)
+    try:
+        share = len(os.sched_getaffinity(0))
+    except AttributeError:
+        share = os.cpu_count() or 1
+    threads = max(1, min(16, share))
+    many, eln, pn = run(threads) if threads > 1 else (one, el1, p1)
+    what = (f"each thread: one virtual rank's reduce over {nd} gradient buffers + Adam + cast "
+            f"on its shard (rank-local: copies of rank {w.rank_local}'s)"
+            if w.rank_local >= 0 else
+            f"each thread: one virtual rank's reduce over {nd} gradient buffers + Adam + cast "
+            f"on its shard (thread i takes rank i mod {nd}, its own state copy), plus the "
+            f"gathers of its share of the {L.T} parameters")
+    return {"value": round(many, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "seconds": round(eln, 2),
+            "sample": f"{what}; at least {pn} pass(es) per thread (C oracle, unchanged)",
+            "single_core": {"value": round(one, 3), "cores": 1, "seconds": round(el1, 2),
+                            "passes": p1}}
 
 
 # ---------------------------------------------------------------------------
