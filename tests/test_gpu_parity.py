@@ -170,6 +170,8 @@ CASES = [
     ([3] * 40 + [1000], 64),
     ([77777], 1),
     ([300, 7, 5000], 256),
+    ([1003, 64, 5, 0, 3 * 4096 + 1], 40),   # ranks in batches of 16 with a partial batch
+    ([97, 12345, 7, 2048], 100),
     (synth.small_tensor_sizes(count=300, lo=8, hi=3000, seed=5), 8),
 ]
 
