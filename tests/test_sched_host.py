@@ -88,3 +88,23 @@ def test_calls_before_bind_fail_without_device_work():
     zsp.zsp_sched_destroy(s)
     zsp.zsp_sched_destroy(None)
     p.destroy()
+
+
+def test_destroying_the_plan_destroys_its_schedules():
+    p = zsp.partition(NUMELS, 4)
+    s = zsp.Schedule(p, [(0, 3)], [0, 0], 1)
+    p.destroy()
+    for call in (lambda: s.acquire(0), lambda: s.release(0), s.reset):
+        try:
+            call()
+        except zsp.ZspError as e:
+            assert e.status == binding.ESTATE
+        else:
+            raise AssertionError("a schedule of a destroyed plan must refuse calls")
+    s.destroy()   # again: a no-op
+    try:
+        zsp.Schedule(p, [(0, 3)], [0], 0)
+    except zsp.ZspError as e:
+        assert e.status == binding.ESTATE
+    else:
+        raise AssertionError("no schedule on a destroyed plan")

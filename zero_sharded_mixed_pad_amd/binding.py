@@ -7,6 +7,7 @@ libzsp.so is missing, importing this module raises.
 """
 import ctypes
 import os
+import weakref
 
 import torch
 
@@ -315,17 +316,25 @@ class Schedule:
         self.groups = [(int(f), int(c)) for f, c in groups]
         self.order = [int(g) for g in order]
         self.dtype = torch.bfloat16 if source == "work" else torch.float32
+        if plan._h is None:
+            raise ZspError(ESTATE, "the plan is destroyed")
         self._h, self.arena_bytes = zsp_sched_create(plan._h, self.groups, self.order, depth,
                                                      source)
         self.info = zsp_sched_info(self._h)
         self.arena = None
+        plan._schedules.add(self)
+
+    def _live(self):
+        if self._h is None:
+            raise ZspError(ESTATE, "the schedule is destroyed (or its plan is)")
+        return self._h
 
     def bind(self, arena, gather_stream):
-        zsp_sched_bind(self._h, arena, gather_stream)
+        zsp_sched_bind(self._live(), arena, gather_stream)
         self.arena = arena
 
     def acquire(self, position, stream=None):
-        addr = zsp_sched_acquire(self._h, position, stream)
+        addr = zsp_sched_acquire(self._live(), position, stream)
         off = addr - self.arena.data_ptr()
         first, count = self.groups[self.order[position]]
         esz = torch.finfo(self.dtype).bits // 8
@@ -338,10 +347,10 @@ class Schedule:
         return views
 
     def release(self, position, stream=None):
-        zsp_sched_release(self._h, position, stream)
+        zsp_sched_release(self._live(), position, stream)
 
     def reset(self):
-        zsp_sched_reset(self._h)
+        zsp_sched_reset(self._live())
 
     def destroy(self):
         if self._h:
@@ -371,12 +380,15 @@ class Plan:
         self.model_state_bytes_per_rank = info["model_state_bytes_per_rank"]
         self._bound = None
         self._bound_rank = None
+        self._schedules = weakref.WeakSet()   # destroyed before the plan
 
     @property
     def handle(self):
         return self._h
 
     def destroy(self):
+        for sched in list(self._schedules):
+            sched.destroy()
         if self._h is not None and self._h.value:
             zsp_destroy(self._h)
         self._h = None
