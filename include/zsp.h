@@ -54,7 +54,8 @@
  *   recent failure. Values are not checked: NaN and Inf propagate.
  *
  * Threads
- *   Calls on one plan must not overlap in time (they share its binding).
+ *   Calls on one plan must not overlap in time (they share its binding and
+ *   its checkpoint staging); a schedule's calls count as calls on its plan.
  *   Different plans are independent.
  */
 #ifndef ZSP_H
