@@ -183,6 +183,28 @@ zsp_status zsp_reduce_adam_step(zsp_plan* plan, int32_t rank_or_all,
                                 float beta1, float beta2, float eps, int64_t step,
                                 void* stream);
 
+/* The three calls above restricted to the parameters [first_param,
+ * first_param + n_params): only those parameters' slots of each rank the
+ * call names are read or written; every other slot, the accumulator's
+ * included, is untouched. This is the reduce-scatter of one layer during
+ * backward ([ZD] section 6: gradient reduce-scatters appear during backward;
+ * [ZS3]: after a layer's backward its gradients go to the ranks owning
+ * them), or the update of one layer. grads[] are the same whole-model
+ * buffers as above. Each rank's slots of a parameter range are one
+ * contiguous span, so the call is one launch per rank (one launch for every
+ * parameter). ZSP_ERANGE if the range is empty or outside [0, n_params). */
+zsp_status zsp_reduce_shard_params(zsp_plan* plan, int32_t rank_or_all, int32_t first_param,
+                                   int32_t n_params, const void* const* grads, zsp_dtype dtype,
+                                   zsp_grad_layout layout, int32_t accumulate, void* stream);
+zsp_status zsp_adam_step_params(zsp_plan* plan, int32_t rank_or_all, int32_t first_param,
+                                int32_t n_params, float lr, float beta1, float beta2, float eps,
+                                int64_t step, void* stream);
+zsp_status zsp_reduce_adam_step_params(zsp_plan* plan, int32_t rank_or_all, int32_t first_param,
+                                       int32_t n_params, const void* const* grads,
+                                       zsp_dtype dtype, zsp_grad_layout layout, int32_t use_acc,
+                                       float lr, float beta1, float beta2, float eps,
+                                       int64_t step, void* stream);
+
 /* gather(param_id) -- AllGather of a full parameter just before compute
  * ([ZD] section 3; [ZS3] on-demand fetch, step 2; [ZST] "Stage 3
  * partitions parameters"). Writes numel[param_id] elements to `out`, pad

@@ -51,6 +51,10 @@ def _load():
         "zsp_adam_step": (i32, [vp, i32, f32, f32, f32, f32, i64, vp]),
         "zsp_reduce_adam_step": (i32, [vp, i32, vpp, i32, i32, i32, f32, f32, f32, f32, i64,
                                        vp]),
+        "zsp_reduce_shard_params": (i32, [vp, i32, i32, i32, vpp, i32, i32, i32, vp]),
+        "zsp_adam_step_params": (i32, [vp, i32, i32, i32, f32, f32, f32, f32, i64, vp]),
+        "zsp_reduce_adam_step_params": (i32, [vp, i32, i32, i32, vpp, i32, i32, i32, f32, f32,
+                                              f32, f32, i64, vp]),
         "zsp_gather": (i32, [vp, i32, i32, vp, vp]),
         "zsp_gather_many": (i32, [vp, i32, i32, i32, vp, vp]),
         "zsp_checkpoint_write_host": (i32, [vp, i32, ctypes.c_char_p, i64, vp, vp, vp, vp]),
@@ -196,6 +200,27 @@ def zsp_reduce_adam_step(h, n_d, rank, grads, lr, beta1, beta2, eps, step, layou
     _check(lib.zsp_reduce_adam_step(h, int(rank), arr, code, _LAYOUTS[layout],
                                     int(bool(use_acc)), float(lr), float(beta1), float(beta2),
                                     float(eps), int(step), _stream(stream)))
+
+
+def zsp_reduce_shard_params(h, n_d, rank, first, n, grads, layout="full", accumulate=False,
+                            stream=None, min_elems=0):
+    arr, code = _grad_array(grads, n_d, min_elems)
+    _check(lib.zsp_reduce_shard_params(h, int(rank), int(first), int(n), arr, code,
+                                       _LAYOUTS[layout], int(bool(accumulate)), _stream(stream)))
+
+
+def zsp_adam_step_params(h, rank, first, n, lr, beta1, beta2, eps, step, stream=None):
+    _check(lib.zsp_adam_step_params(h, int(rank), int(first), int(n), float(lr), float(beta1),
+                                    float(beta2), float(eps), int(step), _stream(stream)))
+
+
+def zsp_reduce_adam_step_params(h, n_d, rank, first, n, grads, lr, beta1, beta2, eps, step,
+                                layout="full", use_acc=False, stream=None, min_elems=0):
+    arr, code = _grad_array(grads, n_d, min_elems)
+    _check(lib.zsp_reduce_adam_step_params(h, int(rank), int(first), int(n), arr, code,
+                                           _LAYOUTS[layout], int(bool(use_acc)), float(lr),
+                                           float(beta1), float(beta2), float(eps), int(step),
+                                           _stream(stream)))
 
 
 def zsp_gather(h, param_id, out, source="work", stream=None):
@@ -441,6 +466,19 @@ class Plan:
                          use_acc=False, stream=None):
         zsp_reduce_adam_step(self._h, self.n_d, rank, grads, lr, beta1, beta2, eps, step,
                              layout, use_acc, stream, self._grad_elems(layout))
+
+    def reduce_shard_params(self, rank, first, n, grads, layout="full", accumulate=False,
+                            stream=None):
+        zsp_reduce_shard_params(self._h, self.n_d, rank, first, n, grads, layout, accumulate,
+                                stream, self._grad_elems(layout))
+
+    def adam_step_params(self, rank, first, n, lr, beta1, beta2, eps, step, stream=None):
+        zsp_adam_step_params(self._h, rank, first, n, lr, beta1, beta2, eps, step, stream)
+
+    def reduce_adam_step_params(self, rank, first, n, grads, lr, beta1, beta2, eps, step,
+                                layout="full", use_acc=False, stream=None):
+        zsp_reduce_adam_step_params(self._h, self.n_d, rank, first, n, grads, lr, beta1, beta2,
+                                    eps, step, layout, use_acc, stream, self._grad_elems(layout))
 
     def gather(self, param_id, out, source="work", stream=None):
         if 0 <= param_id < len(self.numel):

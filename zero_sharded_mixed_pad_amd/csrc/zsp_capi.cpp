@@ -8,6 +8,8 @@
 #include <cstring>
 #include <new>
 #include <string>
+#include <utility>
+#include <vector>
 
 #include "zsp_entry.hpp"
 #include "zsp_internal.hpp"
@@ -336,62 +338,133 @@ zsp_status zsp_load_params(zsp_plan* P, const void* flat_params, zsp_dtype dtype
     return ZSP_OK;
 }
 
-zsp_status zsp_reduce_shard(zsp_plan* P, int32_t rank_or_all, const void* const* grads,
-                            zsp_dtype dtype, zsp_grad_layout layout, int32_t accumulate,
-                            void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The state spans a call on parameters [first, first + n) covers: for each
+// rank it acts on, that rank's slots of those parameters, one contiguous
+// span of the shard index space. Every parameter gives a single span over
+// the whole bound range.
+zsp_status param_spans(const zsp_plan* P, int32_t rank_or_all, int32_t first, int32_t n,
+                       std::vector<std::pair<int64_t, int64_t>>* spans) {
+    int64_t b, e;
+    zsp_status st = rank_range(P, rank_or_all, &b, &e);
+    if (st != ZSP_OK) return st;
+    if (n < 1 || first < 0 || first > P->T - n)
+        return fail(ZSP_ERANGE, "parameters [%d, %d+%d) outside [0, %d)", first, first, n, P->T);
+    spans->clear();
+    if (first == 0 && n == P->T) {
+        spans->emplace_back(b, e);
+        return ZSP_OK;
+    }
+    const int64_t lo = P->shard_off[size_t(first)], hi = P->shard_off[size_t(first + n)];
+    for (int64_t base = b; base < e; base += P->S) spans->emplace_back(base + lo, base + hi);
+    return ZSP_OK;
+}
+
+zsp_status launch_spans(zsp::ShardLaunch L, const std::vector<std::pair<int64_t, int64_t>>& spans,
+                        zsp::ShardOp op, zsp_dtype dtype, void* stream, const char* what) {
+    for (const auto& sp : spans) {
+        L.e_begin = sp.first;
+        L.e_end = sp.second;
+        const hipError_t e = zsp::launch_shard_op(L, op, dtype, static_cast<hipStream_t>(stream));
+        if (e != hipSuccess) return fail_hip(e, what);
+    }
+    return ZSP_OK;
+}
+
+zsp_status reduce_params(zsp_plan* P, int32_t rank_or_all, int32_t first, int32_t n,
+                         const void* const* grads, zsp_dtype dtype, zsp_grad_layout layout,
+                         int32_t accumulate, void* stream) {
     zsp_status st = check_bound(P);
     if (st != ZSP_OK) return st;
     if (!P->acc) return fail(ZSP_ESTATE, "reduce_shard needs a bound grad_acc");
-    int64_t b, en;
-    if ((st = rank_range(P, rank_or_all, &b, &en)) != ZSP_OK) return st;
+    std::vector<std::pair<int64_t, int64_t>> spans;
+    if ((st = param_spans(P, rank_or_all, first, n, &spans)) != ZSP_OK) return st;
     if ((st = check_grads(P, grads, dtype, layout)) != ZSP_OK) return st;
     zsp::ShardLaunch L = base_launch(P);
-    L.e_begin = b;
-    L.e_end = en;
     L.grads = grads;
     L.shard_layout = layout == ZSP_GRADS_SHARD;
-    hipError_t e = zsp::launch_shard_op(L, accumulate ? zsp::OP_REDUCE_ACC : zsp::OP_REDUCE_SET,
-                                        dtype, static_cast<hipStream_t>(stream));
-    if (e != hipSuccess) return fail_hip(e, "reduce launch");
-    return ZSP_OK;
+    return launch_spans(L, spans, accumulate ? zsp::OP_REDUCE_ACC : zsp::OP_REDUCE_SET, dtype,
+                        stream, "reduce launch");
+}
+
+zsp_status adam_params(zsp_plan* P, int32_t rank_or_all, int32_t first, int32_t n, float lr,
+                       float beta1, float beta2, float eps, int64_t step, void* stream) {
+    zsp_status st = check_bound(P);
+    if (st != ZSP_OK) return st;
+    if (!P->acc) return fail(ZSP_ESTATE, "adam_step reads grad_acc, which is not bound");
+    std::vector<std::pair<int64_t, int64_t>> spans;
+    if ((st = param_spans(P, rank_or_all, first, n, &spans)) != ZSP_OK) return st;
+    zsp::ShardLaunch L = base_launch(P);
+    if ((st = adam_scalars(lr, beta1, beta2, eps, step, &L.hp)) != ZSP_OK) return st;
+    return launch_spans(L, spans, zsp::OP_ADAM, ZSP_F32, stream, "adam launch");
+}
+
+zsp_status reduce_adam_params(zsp_plan* P, int32_t rank_or_all, int32_t first, int32_t n,
+                              const void* const* grads, zsp_dtype dtype, zsp_grad_layout layout,
+                              int32_t use_acc, float lr, float beta1, float beta2, float eps,
+                              int64_t step, void* stream) {
+    zsp_status st = check_bound(P);
+    if (st != ZSP_OK) return st;
+    if (use_acc && !P->acc) return fail(ZSP_ESTATE, "use_acc needs a bound grad_acc");
+    std::vector<std::pair<int64_t, int64_t>> spans;
+    if ((st = param_spans(P, rank_or_all, first, n, &spans)) != ZSP_OK) return st;
+    if ((st = check_grads(P, grads, dtype, layout)) != ZSP_OK) return st;
+    zsp::ShardLaunch L = base_launch(P);
+    if ((st = adam_scalars(lr, beta1, beta2, eps, step, &L.hp)) != ZSP_OK) return st;
+    L.grads = grads;
+    L.shard_layout = layout == ZSP_GRADS_SHARD;
+    return launch_spans(L, spans, use_acc ? zsp::OP_FUSED_ACC : zsp::OP_FUSED, dtype, stream,
+                        "fused reduce+adam launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+zsp_status zsp_reduce_shard(zsp_plan* P, int32_t rank_or_all, const void* const* grads,
+                            zsp_dtype dtype, zsp_grad_layout layout, int32_t accumulate,
+                            void* stream) {
+    return reduce_params(P, rank_or_all, 0, P ? P->T : 0, grads, dtype, layout, accumulate,
+                         stream);
+}
+
+zsp_status zsp_reduce_shard_params(zsp_plan* P, int32_t rank_or_all, int32_t first_param,
+                                   int32_t n_params, const void* const* grads, zsp_dtype dtype,
+                                   zsp_grad_layout layout, int32_t accumulate, void* stream) {
+    return reduce_params(P, rank_or_all, first_param, n_params, grads, dtype, layout,
+                         accumulate, stream);
 }
 
 zsp_status zsp_adam_step(zsp_plan* P, int32_t rank_or_all, float lr, float beta1, float beta2,
                          float eps, int64_t step, void* stream) {
-    zsp_status st = check_bound(P);
-    if (st != ZSP_OK) return st;
-    if (!P->acc) return fail(ZSP_ESTATE, "adam_step reads grad_acc, which is not bound");
-    int64_t b, en;
-    if ((st = rank_range(P, rank_or_all, &b, &en)) != ZSP_OK) return st;
-    zsp::ShardLaunch L = base_launch(P);
-    if ((st = adam_scalars(lr, beta1, beta2, eps, step, &L.hp)) != ZSP_OK) return st;
-    L.e_begin = b;
-    L.e_end = en;
-    hipError_t e = zsp::launch_shard_op(L, zsp::OP_ADAM, ZSP_F32, static_cast<hipStream_t>(stream));
-    if (e != hipSuccess) return fail_hip(e, "adam launch");
-    return ZSP_OK;
+    return adam_params(P, rank_or_all, 0, P ? P->T : 0, lr, beta1, beta2, eps, step, stream);
+}
+
+zsp_status zsp_adam_step_params(zsp_plan* P, int32_t rank_or_all, int32_t first_param,
+                                int32_t n_params, float lr, float beta1, float beta2, float eps,
+                                int64_t step, void* stream) {
+    return adam_params(P, rank_or_all, first_param, n_params, lr, beta1, beta2, eps, step,
+                       stream);
 }
 
 zsp_status zsp_reduce_adam_step(zsp_plan* P, int32_t rank_or_all, const void* const* grads,
                                 zsp_dtype dtype, zsp_grad_layout layout, int32_t use_acc,
                                 float lr, float beta1, float beta2, float eps, int64_t step,
                                 void* stream) {
-    zsp_status st = check_bound(P);
-    if (st != ZSP_OK) return st;
-    if (use_acc && !P->acc) return fail(ZSP_ESTATE, "use_acc needs a bound grad_acc");
-    int64_t b, en;
-    if ((st = rank_range(P, rank_or_all, &b, &en)) != ZSP_OK) return st;
-    if ((st = check_grads(P, grads, dtype, layout)) != ZSP_OK) return st;
-    zsp::ShardLaunch L = base_launch(P);
-    if ((st = adam_scalars(lr, beta1, beta2, eps, step, &L.hp)) != ZSP_OK) return st;
-    L.e_begin = b;
-    L.e_end = en;
-    L.grads = grads;
-    L.shard_layout = layout == ZSP_GRADS_SHARD;
-    hipError_t e = zsp::launch_shard_op(L, use_acc ? zsp::OP_FUSED_ACC : zsp::OP_FUSED, dtype,
-                                        static_cast<hipStream_t>(stream));
-    if (e != hipSuccess) return fail_hip(e, "fused reduce+adam launch");
-    return ZSP_OK;
+    return reduce_adam_params(P, rank_or_all, 0, P ? P->T : 0, grads, dtype, layout, use_acc,
+                              lr, beta1, beta2, eps, step, stream);
+}
+
+zsp_status zsp_reduce_adam_step_params(zsp_plan* P, int32_t rank_or_all, int32_t first_param,
+                                       int32_t n_params, const void* const* grads,
+                                       zsp_dtype dtype, zsp_grad_layout layout, int32_t use_acc,
+                                       float lr, float beta1, float beta2, float eps,
+                                       int64_t step, void* stream) {
+    return reduce_adam_params(P, rank_or_all, first_param, n_params, grads, dtype, layout,
+                              use_acc, lr, beta1, beta2, eps, step, stream);
 }
 
 zsp_status zsp_gather_many(zsp_plan* P, int32_t first_param, int32_t n_params, zsp_source src,
