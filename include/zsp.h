@@ -32,10 +32,13 @@
  *
  * Memory and ownership
  *   The caller allocates and owns every device buffer (parameters, gradients,
- *   optimizer state, accumulator, gather outputs). A plan owns only its host
- *   tables and the device copies of its offset tables, which it allocates in
- *   zsp_bind_state and frees in zsp_destroy. No call after zsp_bind_state
- *   allocates memory.
+ *   optimizer state, accumulator, gather outputs, schedule arenas). A plan
+ *   owns its host tables, the device copies of its offset tables (allocated
+ *   in zsp_bind_state) and, from its first checkpoint save or load, the
+ *   checkpoint staging (pinned host chunks, streams, events); zsp_destroy
+ *   frees them. The hot-path calls (reduce, Adam, gather, schedule acquire
+ *   and release) allocate nothing; checkpoint calls also use host memory
+ *   for their own duration.
  *   Every device pointer must be 16-byte aligned (torch allocations are).
  *   State arrays bound for all ranks hold nd*S elements, rank r at
  *   [r*S, (r+1)*S); bound for one rank j they hold that rank's S elements.
