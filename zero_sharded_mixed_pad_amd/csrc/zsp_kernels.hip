@@ -12,8 +12,9 @@
 //    (1 KiB for fp32 state, 512 B for bf16). Giving a lane 8 contiguous
 //    elements instead makes each fp32 instruction touch every other 16 bytes
 //    of a 2 KiB run, which measured ~5% slower.
-//  * Every stream is touched once per launch, so all global loads and stores
-//    carry the non-temporal hint; that measured a further ~5%.
+//  * Every stream is touched once per launch, so global loads and stores
+//    carry the non-temporal hint; that measured a further ~5%. The one
+//    exception is the gather over short pieces (below).
 //  * The optimizer state of both quads is loaded before the gradients so the
 //    state's latency overlaps the rank loop.
 //  * The tile's parameter comes from a per-tile table: wave-uniform, so the
@@ -23,11 +24,13 @@
 //  * Gradient and parameter sources may sit at any 2-byte offset relative to
 //    the quads (each parameter is padded on its own, so slices do not line
 //    up). gfx9 global memory serves unaligned vector loads, so the fast path
-//    stays one vector load per quad; only quads that cross a parameter or pad
-//    boundary take the per-element path.
+//    stays one vector load per quad. Quads that cross a parameter or pad
+//    boundary keep vector state access and mask per element; only quads at
+//    the edge of a launch's range go element by element.
 //  * The reduce over N_d ranks keeps each lane's 8 sums in registers and adds
 //    rank r's values strictly after rank r-1's (fixed order, bit-exact); the
-//    ranks are loaded 8 at a time, so 16 loads per lane are in flight.
+//    ranks are loaded 8 at a time (16 at a time for more than 16 ranks), so
+//    16 (32) loads per lane are in flight.
 //  * Floating point: built with -ffp-contract=off; division and square root
 //    are the default correctly rounded expansions; bf16 narrowing is the
 //    hardware round-to-nearest-even convert (v_cvt_pk_bf16_f32).
