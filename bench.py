@@ -15,8 +15,18 @@ count what the method must move per real (non-pad) element:
   gather                   2*w (read shard, write full) per unpadded element
 with g, w the gradient and parameter element sizes in bytes.
 
-Prints one JSON line. `--rocprof-summary DIR` instead turns rocprofv3 output
-into the text summaries kept under profiles/.
+Prints one JSON line: the metric, a roofline object for the dominant kernel
+(HIP-event time, peak, and HBM traffic from stored PMC counters when they
+match the kernels' source) and the CPU oracle's figure on a bounded sample.
+
+Other modes, each printing its own JSON line:
+  --stage 1|2   the step in the ZeRO stage-1 or stage-2 schedule
+  --split       reduce into the accumulator, then Adam (unfused update)
+  --prefetch    forward + backward over a Llama-7B stack through the
+                per-layer gather schedule; hidden fraction of gather time
+  --checkpoint DIR   sharded checkpoint save / load / reshard-load timings
+  --rocprof-summary DIR, --traffic-from F W   turn rocprofv3 output into the
+                text and JSON summaries kept under profiles/
 """
 import argparse
 import csv
