@@ -38,7 +38,11 @@
  *   checkpoint staging (pinned host chunks, streams, events); zsp_destroy
  *   frees them. The hot-path calls (reduce, Adam, gather, schedule acquire
  *   and release) allocate nothing; checkpoint calls also use host memory
- *   for their own duration.
+ *   for their own duration. The reduce, Adam and gather calls only check
+ *   arguments and launch kernels (no host wait, no memset), so they can be
+ *   captured into a HIP graph; Adam's scalars (lr, betas, eps and the step's
+ *   bias corrections) are kernel arguments, so a replay repeats the step it
+ *   was captured with.
  *   Every device pointer must be 16-byte aligned (torch allocations are).
  *   State arrays bound for all ranks hold nd*S elements, rank r at
  *   [r*S, (r+1)*S); bound for one rank j they hold that rank's S elements.

@@ -1,0 +1,57 @@
+"""The hot-path calls under HIP graph capture: no allocation, no host
+synchronisation and no memset node inside zsp_reduce_adam_step,
+zsp_reduce_shard, zsp_adam_step or zsp_gather_many, so a caller can capture
+one step and replay it. Captured once, replayed three times with eager work
+and host synchronisations between the replays; after every replay the state
+and the gathered parameters equal those of the same calls made eagerly on a
+twin plan. The Adam step's scalars are kernel arguments, so a replay repeats
+the step number it was captured with (the eager twin does the same)."""
+import pytest
+import torch
+
+import zero_sharded_mixed_pad_amd as zsp
+
+from test_gpu_parity import HP, Mirror, assert_bits, dev, np_of
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("numels,nd", [([1003, 64, 5, 0, 3 * 4096 + 1], 4),
+                                       ([4096 * 3, 11008 * 2, 4096, 4096], 8)])
+def test_capture_and_replay_matches_eager(numels, nd):
+    A, B = Mirror(numels, nd), Mirror(numels, nd)
+    grads = [g.to(dev()) for g in A.grads(torch.bfloat16, "graph", poison=False)]
+    n_out = max(A.L.total_numel, 8)
+    out_a = torch.empty(n_out, dtype=torch.bfloat16, device=dev())
+    out_b = torch.empty(n_out, dtype=torch.bfloat16, device=dev())
+    T = len(numels)
+    torch.cuda.synchronize()
+
+    def step(M, out, stream):
+        M.plan.reduce_shard(zsp.ALL_RANKS, grads, accumulate=False, stream=stream)
+        M.plan.adam_step(zsp.ALL_RANKS, step=3, stream=stream, **HP)
+        M.plan.reduce_adam_step(zsp.ALL_RANKS, grads, step=4, use_acc=True, stream=stream, **HP)
+        M.plan.gather_many(0, T, out[:A.L.total_numel], "work", stream=stream)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            step(A, out_a, s)
+    torch.cuda.synchronize()
+    # capture does not run the work: A is still at its copy-in state
+    assert_bits(np_of(A.g_master[:A.n]), np_of(B.g_master[:B.n]), "capture ran nothing")
+    scratch = torch.empty(1 << 20, device=dev())
+    for rep in range(3):
+        g.replay()
+        step(B, out_b, torch.cuda.current_stream())
+        scratch.uniform_()                       # eager work between replays
+        torch.cuda.synchronize()
+        for name, a, b in (("master", A.g_master, B.g_master), ("m", A.g_m, B.g_m),
+                           ("v", A.g_v, B.g_v), ("work", A.g_work, B.g_work),
+                           ("acc", A.g_acc, B.g_acc)):
+            assert_bits(np_of(a[:A.n]), np_of(b[:B.n]), f"replay {rep}: {name}")
+        assert_bits(np_of(out_a[:A.L.total_numel]), np_of(out_b[:B.L.total_numel]),
+                    f"replay {rep}: gathered parameters")
+    del g
