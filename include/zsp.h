@@ -326,9 +326,9 @@ zsp_status zsp_checkpoint_read_host(const zsp_plan* plan, int32_t rank, const ch
 /* Save the bound state of one rank or of every bound rank
  * (ZSP_ALL_RANKS) to `dir`. The copies follow everything already enqueued
  * on `stream` (an event taken on it orders the library's own copy streams);
- * returns after the files are written. Up to 8 files are written at once,
- * through pinned host chunks the plan keeps until zsp_destroy (about 32 MiB
- * per file in flight). */
+ * returns after the files are written. Up to 16 files are written at once,
+ * through pinned host chunks the plan keeps until zsp_destroy (32 MiB per
+ * file in flight, 512 MiB at most). */
 zsp_status zsp_checkpoint_save(zsp_plan* plan, int32_t rank_or_all, const char* dir,
                                int64_t step, void* stream);
 

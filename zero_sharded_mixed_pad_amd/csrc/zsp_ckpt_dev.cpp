@@ -4,7 +4,7 @@
 // is restored from its own file; a restart under another rank count
 // reshuffles the shards; the safe point is between steps).
 //
-// Device state moves through a small set of lanes, each with its own stream
+// Device state moves through up to 16 lanes, each with its own stream
 // (default priority), two pinned chunks and two events, kept by the plan
 // between calls. A lane handles one rank file at a time, and lanes run on
 // separate host threads, so files are written or read in parallel:
@@ -41,7 +41,7 @@ namespace zsp {
 
 namespace {
 
-constexpr int kLanes = 8;                      // files in flight at once
+constexpr int kLanes = 16;                     // files in flight at once
 constexpr size_t kChunk = size_t(16) << 20;    // bytes per pinned chunk
 
 }  // namespace
