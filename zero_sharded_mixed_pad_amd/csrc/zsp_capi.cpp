@@ -131,8 +131,6 @@ size_t bytes_of(const std::vector<T>& v) {
 
 size_t round_up(size_t x) { return (x + 255) & ~size_t(255); }
 
-
-
 }  // namespace
 
 namespace zsp {

@@ -245,19 +245,12 @@ class DevSource : public PayloadSource {
 // filled in payload order (master, m, v, work), each array whole.
 class DevSink {
   public:
-    DevSink(Lane& lane, const zsp_plan* P, int64_t base) : lane_(lane), S_(P->S) {
+    DevSink(Lane& lane, const zsp_plan* P, int64_t base) : lane_(lane) {
         dst_[0] = reinterpret_cast<char*>(P->master + base);
         dst_[1] = reinterpret_cast<char*>(P->m + base);
         dst_[2] = reinterpret_cast<char*>(P->v + base);
         dst_[3] = reinterpret_cast<char*>(P->work + base);
         for (int i = 0; i < 4; ++i) len_[i] = size_t(P->S) * (i < 3 ? 4 : 2);
-    }
-    bool begin(int64_t S, std::string* err) {
-        if (S != S_) {
-            *err = "holds another parameter list";
-            return false;
-        }
-        return true;
     }
     // A chunk for the next bytes, at most *cap of them (never past an array).
     bool buffer(void** data, size_t* cap, std::string* err) {
@@ -299,7 +292,6 @@ class DevSink {
 
   private:
     Lane& lane_;
-    int64_t S_;
     char* dst_[4];
     size_t len_[4];
     int seg_ = 0;
@@ -562,7 +554,7 @@ zsp_status zsp_checkpoint_load(zsp_plan* P, int32_t rank_or_all, const char* dir
             Lane& L = stg->lanes[size_t(lane)];
             const int32_t r = ranks[size_t(i)];
             DevSink sink(L, P, rank_base(P, r));
-            bool ok = sink.begin(P->S, m);
+            bool ok = true;
             for (int a = 0; a < 4 && ok; ++a) {  // master, m, v, work: payload order
                 const size_t esz = a < 3 ? sizeof(float) : sizeof(uint16_t);
                 for (int64_t e = 0; ok && e < P->S;) {
