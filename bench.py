@@ -469,6 +469,25 @@ def prefetch_bench(args, device):
 # CPU baseline: the oracle, as it stands, on a bounded sample
 # ---------------------------------------------------------------------------
 
+def cpu_model():
+    """The host CPU's model name as /proc/cpuinfo reports it, or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def software():
+    """Versions the measurement ran on."""
+    import torch
+    return {"torch": torch.__version__, "hip": torch.version.hip,
+            "gpu": torch.cuda.get_device_name(0) if torch.cuda.is_available() else None}
+
+
 def cpu_baseline(runner, target_s):
     """The oracle as it stands, timed on the host on a bounded sample of the
     workload: one virtual rank's reduce over the N_d gradient buffers + Adam +
@@ -556,7 +575,7 @@ def cpu_baseline(runner, target_s):
             f"on its shard (thread i takes rank i mod {nd}, its own state copy), plus the "
             f"gathers of its share of the {L.T} parameters")
     return {"value": round(many, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "seconds": round(eln, 2),
+            "cpu_model": cpu_model(), "seconds": round(eln, 2),
             "sample": f"{what}; at least {pn} pass(es) per thread (C oracle, unchanged)",
             "single_core": {"value": round(one, 3), "cores": 1, "seconds": round(el1, 2),
                             "passes": p1}}
@@ -779,7 +798,7 @@ def main():
                    "bytes_per_step": int(step_bytes), "cache_flush": bool(flush),
                    "wall_ms_per_step": round(wall * 1e3 / args.steps, 4)},
         "roofline": roof, "cpu_baseline": cpu, "kernels": ks,
-        "kernel_source_hash": kernel_source_hash(),
+        "kernel_source_hash": kernel_source_hash(), "software": software(),
     }
     print(json.dumps(line), flush=True)
     return 0
