@@ -61,9 +61,15 @@
  *   recent failure. Values are not checked: NaN and Inf propagate.
  *
  * Threads
- *   Calls on one plan must not overlap in time (they share its binding and
- *   its checkpoint staging); a schedule's calls count as calls on its plan.
- *   Different plans are independent.
+ *   The reduce, Adam and gather calls (whole-model and _params forms) and
+ *   zsp_load_params only read the plan: several threads may issue them on
+ *   one plan at once, e.g. one thread per rank, each on its own stream (work
+ *   that writes the same state at the same time is the caller's race, as
+ *   for any two kernels). zsp_bind_state, the checkpoint calls and
+ *   zsp_destroy change the plan and must not overlap any other call on it.
+ *   A schedule's calls must not overlap one another; other schedules and
+ *   the read-only calls above may run beside them. Different plans are
+ *   independent.
  */
 #ifndef ZSP_H
 #define ZSP_H
