@@ -269,7 +269,10 @@ class Runner:
             else:
                 nbytes = sum(g[3] for g in self.gather_groups) / len(self.gather_groups)
             gbps = nbytes / avg_s / 1e9
+            srt = sorted(ms)
+            med = (srt[(len(srt) - 1) // 2] + srt[len(srt) // 2]) / 2
             out[kind] = {"launches": len(ms), "avg_us": round(avg_s * 1e6, 2),
+                         "median_us": round(med * 1e3, 2),
                          "min_us": round(min(ms) * 1e3, 2), "bytes_per_launch": int(nbytes),
                          "GBps": round(gbps, 1), "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4)}
         return out
