@@ -68,6 +68,17 @@ MUTANTS = [
      "if (dropped > 0x8000u) kept += 1u;", ADAM),
     ("bf16 ties rounded away",
      "(dropped == 0x8000u && (kept & 1u))", "(dropped == 0x8000u)", ADAM),
+    ("reduce drops the last rank",
+     "for (int32_t r = 1; r < nd; ++r) acc = acc + g[r];",
+     "for (int32_t r = 1; r < nd - 1; ++r) acc = acc + g[r];", REDUCE),
+    ("reduce reads pad slots", "if (k >= numel[t]) { out[e] = 0.0f; continue; }", "", REDUCE),
+    ("gather forgets the rank's base",
+     "int64_t idx = r * L.S + L.shard_off[t] + (k - r * s);",
+     "int64_t idx = L.shard_off[t] + (k - r * s);", LAYOUT),
+    ("shard offsets skip a slot", "shard_off[t + 1] = shard_off[t] + shard_len[t];",
+     "shard_off[t + 1] = shard_off[t] + shard_len[t] + 1;", LAYOUT),
+    ("bf16 cast leaves NaN unquieted",
+     "return (uint16_t)((u >> 16) | 0x0040u);", "return (uint16_t)(u >> 16);", ADAM),
     ("adam updates pad slots",
      "if (k >= numel[t]) continue;\n            int64_t e = L.shard_off[t] + i;\n            adam_one",
      "int64_t e = L.shard_off[t] + i;\n            adam_one", ADAM),
