@@ -75,8 +75,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time for the oracle baseline sample")
     ap.add_argument("--flush", choices=["auto", "on", "off"], default="auto",
-                    help="overwrite a 1 GiB buffer before each step so a small working set "
-                         "is not served from the 256 MB Infinity Cache")
+                    help="read a 1 GiB buffer before each step so a small working set is "
+                         "not served from the 256 MB Infinity Cache (auto: fused step under "
+                         "2 GB); gathers under 1 GB are also timed cold, after such a read")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run plain 2 GiB device copies (PMC byte-count calibration)")
     ap.add_argument("--rocprof-summary", metavar="DIR", default=None)
@@ -179,7 +180,8 @@ class Runner:
                 out = torch.empty(cnt, dtype=bf16, device=device)
                 self.gather_groups.append((first, n, out, cnt * 4))
         self.step_no = 0
-        self.ev = {"fused": [], "reduce": [], "gather": [], "adam": [], "gather_acc": []}
+        self.ev = {"fused": [], "reduce": [], "gather": [], "adam": [], "gather_acc": [],
+                   "gather_cold": []}
 
     def _event(self):
         return self.torch.cuda.Event(enable_timing=True)
@@ -228,6 +230,16 @@ class Runner:
             for first, n, out, _b in self.gather_groups:
                 self._timed("gather", lambda first=first, n=n, out=out: p.gather_many(
                     first, n, out, "work"), record)
+
+    def cold_gathers(self, flush, reps):
+        """Each gather group again, `reps` times, each time right after
+        `flush` has evicted the caches: a gather under 1 GB can otherwise
+        read what the step just wrote from the 256 MB Infinity Cache."""
+        for _ in range(reps):
+            for first, n, out, _b in self.gather_groups:
+                flush()
+                self._timed("gather_cold", lambda first=first, n=n, out=out:
+                            self.plan.gather_many(first, n, out, "work"), True)
 
     def step_bytes(self):
         w = self.w
@@ -734,18 +746,25 @@ def main():
               flush=True)
         return 0
     flush = args.flush == "on" or (args.flush == "auto" and r.bytes_fused < 2e9)
-    scratch = torch.empty(1 << 30, dtype=torch.uint8, device=device) if flush else None
+    # Cache flush: a reduction that reads 1 GiB, four times the Infinity
+    # Cache, evicting the working set without leaving dirty lines behind (a
+    # flush that writes would make the timed kernel pay their write-back).
+    scratch = torch.ones(1 << 28, dtype=torch.float32, device=device)
+    sink = torch.empty((), dtype=torch.float32, device=device)
+
+    def evict():
+        torch.sum(scratch, dim=0, out=sink)
 
     for _ in range(args.warmup):
         if flush:
-            scratch.fill_(1)
+            evict()
         r.step()
     torch.cuda.synchronize()
     step_events = []
     t0 = time.perf_counter()
     for _ in range(args.steps):
         if flush:
-            scratch.fill_(1)
+            evict()
         a = torch.cuda.Event(enable_timing=True)
         b = torch.cuda.Event(enable_timing=True)
         a.record()
@@ -760,6 +779,9 @@ def main():
     ms_per_step = event_ms if flush else wall * 1e3 / args.steps
     step_bytes = r.step_bytes()
     value = step_bytes / (ms_per_step / 1e3) / 1e9
+    if not flush and any(g[3] < 1e9 for g in r.gather_groups):
+        r.cold_gathers(evict, args.steps)
+        torch.cuda.synchronize()
     ks = r.kernel_stats()
 
     if args.calibrate_copy:
