@@ -1,0 +1,78 @@
+"""Seeded random cases beyond the hand-picked ones: random parameter lists
+(empty, tiny, smaller than N_d, ragged, a few tiles long), random rank counts
+up to 64, both gradient dtypes and layouts, with or without an accumulated
+micro-batch, on all ranks or one; every step and a gather of a random run of
+parameters must match the oracle bit for bit."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import zero_sharded_mixed_pad_amd as zsp
+
+from test_gpu_parity import HP, Mirror, assert_bits, dev, np_of
+
+pytestmark = pytest.mark.gpu
+
+ND_CHOICES = [1, 2, 3, 4, 5, 7, 8, 9, 13, 16, 31, 40, 64]
+
+
+def random_numels(rng):
+    kinds = rng.integers(0, 4, size=int(rng.integers(1, 13)))
+    out = []
+    for k in kinds:
+        if k == 0:
+            out.append(int(rng.integers(0, 8)))           # empty or below N_d
+        elif k == 1:
+            out.append(int(rng.integers(8, 700)))         # within a tile
+        elif k == 2:
+            out.append(int(rng.integers(700, 6000)))      # a few tiles
+        else:
+            out.append(int(rng.integers(6000, 40000)))    # many tiles
+    return out
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_case(seed):
+    rng = np.random.default_rng(20261202 + seed)
+    numels = random_numels(rng)
+    nd = int(rng.choice(ND_CHOICES))
+    gdtype = torch.float32 if rng.integers(0, 4) == 0 else torch.bfloat16
+    pdtype = torch.float32 if gdtype == torch.float32 else torch.bfloat16
+    layout = "shard" if rng.integers(0, 3) == 0 else "full"
+    use_acc = bool(rng.integers(0, 2))
+    rank = -1 if rng.integers(0, 3) else int(rng.integers(0, nd))
+    what = (f"seed {seed}: numels {numels}, N_d {nd}, grads {gdtype}, {layout} layout, "
+            f"use_acc {use_acc}, rank {rank}")
+    print(f"\n[random] {what}", flush=True)
+    M = Mirror(numels, nd, pdtype, seed=seed)
+    d = dev()
+    ranks = M.ranks if rank < 0 else [rank]
+    for step in (1, 2):
+        if use_acc:
+            g0 = M.grads(gdtype, ("rand-acc", seed, step), layout=layout)
+            M.plan.reduce_shard(rank, [g.to(d) for g in g0], layout=layout)
+            for j in ranks:
+                M.o_acc[M.o_slice(j)] = M.o_reduce(j, g0, layout)
+        grads = M.grads(gdtype, ("rand", seed, step), layout=layout)
+        M.plan.reduce_adam_step(rank, [g.to(d) for g in grads], step=step, layout=layout,
+                                use_acc=use_acc, **HP)
+        for j in ranks:
+            g = M.o_reduce(j, grads, layout)
+            if use_acc:
+                acc = M.o_acc[M.o_slice(j)].copy()
+                oracle.accumulate(acc, g)
+                g = acc
+            M.o_adam(j, g, step)
+        assert M.check_state(f"{what}, step {step}") == 0, what
+    # a random run of consecutive parameters, gathered in one launch
+    T = len(numels)
+    first = int(rng.integers(0, T))
+    n = int(rng.integers(1, T - first + 1))
+    total = sum(numels[first:first + n])
+    out = torch.empty(max(total, 1), dtype=torch.bfloat16, device=d)
+    M.plan.gather_many(first, n, out[:total], "work")
+    torch.cuda.synchronize()
+    want = [oracle.gather(numels, nd, t, M.o_work) for t in range(first, first + n)]
+    want = np.concatenate(want) if want else np.zeros(0, np.uint16)
+    assert_bits(np_of(out[:total]), want, f"{what}: gather of [{first}, {first + n})")
