@@ -76,3 +76,57 @@ def test_random_case(seed):
     want = [oracle.gather(numels, nd, t, M.o_work) for t in range(first, first + n)]
     want = np.concatenate(want) if want else np.zeros(0, np.uint16)
     assert_bits(np_of(out[:total]), want, f"{what}: gather of [{first}, {first + n})")
+
+
+def random_groups(rng, T):
+    """T parameters cut into consecutive non-empty groups at random points."""
+    cuts = sorted(set(int(c) for c in rng.integers(1, T, size=int(rng.integers(0, T)))))
+    edges = [0] + cuts + [T]
+    return [(a, b - a) for a, b in zip(edges[:-1], edges[1:])]
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_groups_update_and_schedule(seed):
+    """Per-group fused updates in a random order cover the model and equal the
+    oracle's whole update; then a schedule over the same groups, with a random
+    order of positions and depth, hands every position its layer."""
+    rng = np.random.default_rng(7_000 + seed)
+    numels = random_numels(rng)
+    T = len(numels)
+    nd = int(rng.choice(ND_CHOICES))
+    layout = "shard" if rng.integers(0, 3) == 0 else "full"
+    groups = random_groups(rng, T)
+    what = f"seed {seed}: numels {numels}, N_d {nd}, {layout} layout, groups {groups}"
+    print(f"\n[random groups] {what}", flush=True)
+    M = Mirror(numels, nd, seed=100 + seed)
+    d = dev()
+    for step in (1, 2):
+        grads = M.grads(torch.bfloat16, ("rand-groups", seed, step), layout=layout)
+        gdev = [g.to(d) for g in grads]
+        for gi in rng.permutation(len(groups)):
+            first, n = groups[int(gi)]
+            M.plan.reduce_adam_step_params(-1, first, n, gdev, step=step, layout=layout, **HP)
+        for j in M.ranks:
+            M.o_adam(j, M.o_reduce(j, grads, layout), step)
+        assert M.check_state(f"{what}, step {step}") == 0, what
+
+    order = [int(g) for g in rng.integers(0, len(groups), size=int(rng.integers(1, 12)))]
+    depth = int(rng.integers(0, 4))
+    s = zsp.Schedule(M.plan, groups, order, depth)
+    arena = torch.empty(s.arena_bytes, dtype=torch.uint8, device=d)
+    cs, gs = torch.cuda.Stream(), torch.cuda.Stream()
+    s.bind(arena, gs if s.info["depth"] > 0 else None)
+    torch.cuda.synchronize()
+    caps = []
+    with torch.cuda.stream(cs):
+        for p in range(len(order)):
+            views = s.acquire(p, cs)
+            caps.append([v.clone() for v in views])
+            s.release(p, cs)
+    torch.cuda.synchronize()
+    for p, g in enumerate(order):
+        first, n = groups[g]
+        for i, t in enumerate(range(first, first + n)):
+            assert_bits(np_of(caps[p][i]), oracle.gather(numels, nd, t, M.o_work),
+                        f"{what}: schedule depth {depth}, position {p}, parameter {t}")
+    s.destroy()
