@@ -12,8 +12,10 @@
 //   float    master[S], m[S], v[S]
 //   uint16   work[S]
 //   uint64   XXH64 (seed 0) of every byte above
-// Files are written to a temporary name and renamed, so a crash mid-write
-// never leaves a truncated file under the final name.
+// Files are written to a temporary name and renamed, so a process that dies
+// mid-write never leaves a short file under the final name. The data is not
+// forced to disk before the rename; a file cut short by a system crash fails
+// the length and checksum checks of every read.
 #include <dirent.h>
 #include <fcntl.h>
 #include <sys/mman.h>
