@@ -144,3 +144,30 @@ def test_bind_argument_errors_before_device_use():
     bad[4] = ctypes.c_void_p(256 + 8)                               # grad_acc misaligned
     assert lib.zsp_bind_state(h, -1, *bad) == binding.EINVAL
     plan.destroy()
+
+
+try:
+    from hypothesis import given, settings, strategies as st
+except ImportError:  # the property test below needs hypothesis
+    given = None
+
+
+if given is not None:
+    @settings(max_examples=300, deadline=None)
+    @given(numels=st.lists(st.one_of(st.integers(0, 9), st.integers(0, 5000),
+                                     st.integers(0, 10 ** 12)), min_size=1, max_size=40),
+           nd=st.integers(1, 256))
+    def test_layout_queries_match_oracle_on_random_lists(numels, nd):
+        """The library's layout queries equal the oracle's tables for random
+        parameter lists (sizes from empty to 10^12 elements, any rank count
+        the library accepts)."""
+        plan = zsp.partition(numels, nd)
+        L = oracle.Layout(numels, nd)
+        info = plan.info()
+        assert (info["shard_elems"], info["total_padded"], info["total_numel"]) == (
+            L.S, L.total_padded, L.total_numel)
+        for t in range(len(numels)):
+            d = plan.tensor(t)
+            assert (d["pad"], d["shard_len"], d["full_off"], d["shard_off"], d["flat_off"]) == (
+                L.pad[t], L.shard_len[t], L.full_off[t], L.shard_off[t], L.flat_off[t])
+        plan.destroy()
