@@ -131,6 +131,15 @@ size_t bytes_of(const std::vector<T>& v) {
 
 size_t round_up(size_t x) { return (x + 255) & ~size_t(255); }
 
+// Whether a shard launch over parameters [first, first + n) meets its pieces
+// (one per rank and parameter with slots) every few thousand elements or
+// less: such launches have many tiles at piece boundaries.
+bool short_pieces(const zsp_plan* P, int32_t first, int32_t n) {
+    const int64_t pieces = P->slot_off[size_t(first + n)] - P->slot_off[size_t(first)];
+    const int64_t elems = P->shard_off[size_t(first + n)] - P->shard_off[size_t(first)];
+    return pieces > 0 && elems < pieces * zsp::kShortPiece;
+}
+
 }  // namespace
 
 namespace zsp {
@@ -170,6 +179,7 @@ zsp_status zsp_partition(const int64_t* numel, int32_t n_params, int32_t n_d, zs
         P->shard_off.assign(n_params + 1, 0);
         P->flat_off.assign(n_params + 1, 0);
         P->piece_off.assign(n_params + 1, 0);
+        P->slot_off.assign(n_params + 1, 0);
         const int64_t kMax = int64_t(1) << 60;
         for (int32_t t = 0; t < n_params; ++t) {
             const int64_t n = numel[t];
@@ -190,6 +200,7 @@ zsp_status zsp_partition(const int64_t* numel, int32_t n_params, int32_t n_d, zs
             // ranks holding real elements of t: one gather piece each
             const int64_t s_t = P->shard_len[t];
             P->piece_off[t + 1] = P->piece_off[t] + (n == 0 ? 0 : (n + s_t - 1) / s_t);
+            P->slot_off[t + 1] = P->slot_off[t] + (s_t > 0 ? 1 : 0);
         }
         P->S = P->shard_off[n_params];
         P->total_padded = P->full_off[n_params];
@@ -331,6 +342,7 @@ zsp_status zsp_load_params(zsp_plan* P, const void* flat_params, zsp_dtype dtype
     L.e_begin = 0;
     L.e_end = P->shard.total;
     L.src = flat_params;
+    L.short_pieces = short_pieces(P, 0, P->T);
     hipError_t e = zsp::launch_shard_op(L, zsp::OP_COPYIN, dtype, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail_hip(e, "copy-in launch");
     return ZSP_OK;
@@ -384,6 +396,7 @@ zsp_status reduce_params(zsp_plan* P, int32_t rank_or_all, int32_t first, int32_
     zsp::ShardLaunch L = base_launch(P);
     L.grads = grads;
     L.shard_layout = layout == ZSP_GRADS_SHARD;
+    L.short_pieces = short_pieces(P, first, n);
     return launch_spans(L, spans, accumulate ? zsp::OP_REDUCE_ACC : zsp::OP_REDUCE_SET, dtype,
                         stream, "reduce launch");
 }
@@ -397,6 +410,7 @@ zsp_status adam_params(zsp_plan* P, int32_t rank_or_all, int32_t first, int32_t 
     if ((st = param_spans(P, rank_or_all, first, n, &spans)) != ZSP_OK) return st;
     zsp::ShardLaunch L = base_launch(P);
     if ((st = adam_scalars(lr, beta1, beta2, eps, step, &L.hp)) != ZSP_OK) return st;
+    L.short_pieces = short_pieces(P, first, n);
     return launch_spans(L, spans, zsp::OP_ADAM, ZSP_F32, stream, "adam launch");
 }
 
@@ -414,6 +428,7 @@ zsp_status reduce_adam_params(zsp_plan* P, int32_t rank_or_all, int32_t first, i
     if ((st = adam_scalars(lr, beta1, beta2, eps, step, &L.hp)) != ZSP_OK) return st;
     L.grads = grads;
     L.shard_layout = layout == ZSP_GRADS_SHARD;
+    L.short_pieces = short_pieces(P, first, n);
     return launch_spans(L, spans, use_acc ? zsp::OP_FUSED_ACC : zsp::OP_FUSED, dtype, stream,
                         "fused reduce+adam launch");
 }

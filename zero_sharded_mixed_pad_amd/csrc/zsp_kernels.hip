@@ -7,6 +7,10 @@
 //  * One wavefront per workgroup, owning one 512-element tile of the index
 //    space. Small workgroups keep more, shorter-lived waves in flight, which
 //    measured faster than 256-thread groups for these streams.
+//  * Heavy shard launches cap the workgroups resident per CU (4 to 10,
+//    through the LDS each reserves): fewer waves, each with 14-24 KiB of
+//    loads in flight, let HBM serve the mixed read/write streams faster
+//    than a full CU does. See shard_lds_pad.
 //  * Lane l owns two 4-element quads of the tile, at 4*l and 256 + 4*l, so
 //    every load and store instruction of the wave covers one contiguous run
 //    (1 KiB for fp32 state, 512 B for bf16). Giving a lane 8 contiguous
@@ -36,6 +40,7 @@
 //    hardware round-to-nearest-even convert (v_cvt_pk_bf16_f32).
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstddef>
 #include <type_traits>
 
@@ -749,6 +754,59 @@ __global__ __launch_bounds__(kWaveLanes) void gather_kernel(const GatherArgs a) 
     }
 }
 
+// Resident waves. With every CU full of shard waves, each touching a dozen
+// streams, HBM serves the mix of reads and writes less efficiently than with
+// fewer waves resident, as long as each wave has enough bytes in flight.
+// The cap is set through the LDS each workgroup reserves (its piece tables
+// plus padding), at totals measured on MI355X (160 KiB of LDS per CU) by the
+// bytes a launch reads per element: 40 or more (the fused step at 16 ranks
+// with its accumulator) 40960 bytes, 4 workgroups per CU; 24 or more (the
+// fused step at 8 ranks, the reduce at 16) 28160, 5 per CU; launches over
+// short pieces, whose boundary tiles need more waves to hide their latency,
+// 16384. Lighter launches (the reduce at 8 ranks, Adam alone: 16 bytes per
+// element) ran slower capped and keep every wave, as do launches of more
+// than 16 ranks, launches too small to fill the chip several times, and
+// the copy-in.
+constexpr size_t kLdsTunedPerCu = 163840;
+constexpr size_t kLdsHeavy = 40960;
+constexpr size_t kLdsMedium = 28160;
+constexpr size_t kLdsShortPieces = 16384;
+constexpr int kHeavyBytes = 40;
+constexpr int kMediumBytes = 24;
+constexpr int64_t kCapMinTiles = 8192;
+
+size_t device_lds_per_cu() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    int v = cache[dev].load(std::memory_order_relaxed);
+    if (v == 0) {
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) !=
+            hipSuccess)
+            v = -1;
+        cache[dev].store(v, std::memory_order_relaxed);
+    }
+    return v > 0 ? size_t(v) : 0;
+}
+
+// Dynamic LDS that brings a shard workgroup to the reservation above, or 0.
+template <int OP, typename GT, int CAP>
+size_t shard_lds_pad(const ShardLaunch& L, int64_t blocks) {
+    if constexpr (CAP > 16 || OP == OP_COPYIN) {
+        return 0;
+    } else {
+        if (blocks < kCapMinTiles || device_lds_per_cu() != kLdsTunedPerCu) return 0;
+        const int grad = uses_grads(OP) ? L.nd * int(sizeof(GT)) : 0;
+        const int bytes = grad + (is_adam(OP) ? 12 : 0) + (reads_acc(OP) ? 4 : 0);
+        if (bytes < kMediumBytes) return 0;
+        const size_t total = L.short_pieces        ? kLdsShortPieces
+                             : bytes >= kHeavyBytes ? kLdsHeavy
+                                                    : kLdsMedium;
+        const size_t tables = kStage * (sizeof(int64_t) + sizeof(PieceInfo));
+        return total > tables ? total - tables : 0;
+    }
+}
+
 template <int OP, typename GT, int CAP>
 hipError_t launch_t(const ShardLaunch& L, hipStream_t stream) {
     ShardArgs<CAP> a{};
@@ -774,8 +832,9 @@ hipError_t launch_t(const ShardLaunch& L, hipStream_t stream) {
     const int64_t blocks = tile_end - a.tile_first;  // one wave per tile
     if (blocks <= 0) return hipSuccess;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+    const size_t lds_pad = shard_lds_pad<OP, GT, CAP>(L, blocks);
     hipLaunchKernelGGL((shard_kernel<OP, GT, CAP>), dim3(static_cast<uint32_t>(blocks)),
-                       dim3(kWaveLanes), 0, stream, a);
+                       dim3(kWaveLanes), lds_pad, stream, a);
     return hipGetLastError();
 }
 

@@ -19,6 +19,7 @@ struct zsp_plan {
     int32_t nd = 0;
     std::vector<int64_t> numel, pad, shard_len, full_off, shard_off, flat_off;
     std::vector<int64_t> piece_off;  // gather pieces (rank runs) before parameter t
+    std::vector<int64_t> slot_off;   // parameters with shard_len > 0 before parameter t
     int64_t S = 0;
     int64_t total_padded = 0;
     int64_t total_numel = 0;
