@@ -7,8 +7,8 @@
 //  * One wavefront per workgroup, owning one 512-element tile of the index
 //    space. Small workgroups keep more, shorter-lived waves in flight, which
 //    measured faster than 256-thread groups for these streams.
-//  * Heavy shard launches cap the workgroups resident per CU (4 to 10,
-//    through the LDS each reserves): fewer waves, each with 14-24 KiB of
+//  * Large shard launches cap the workgroups resident per CU (4 to 10,
+//    through the LDS each reserves): fewer waves, each with 8-24 KiB of
 //    loads in flight, let HBM serve the mixed read/write streams faster
 //    than a full CU does. See shard_lds_pad.
 //  * Lane l owns two 4-element quads of the tile, at 4*l and 256 + 4*l, so
@@ -761,18 +761,19 @@ __global__ __launch_bounds__(kWaveLanes) void gather_kernel(const GatherArgs a) 
 // plus padding), at totals measured on MI355X (160 KiB of LDS per CU) by the
 // bytes a launch reads per element: 40 or more (the fused step at 16 ranks
 // with its accumulator) 40960 bytes, 4 workgroups per CU; 24 or more (the
-// fused step at 8 ranks, the reduce at 16) 28160, 5 per CU; launches over
-// short pieces, whose boundary tiles need more waves to hide their latency,
-// 16384. Lighter launches (the reduce at 8 ranks, Adam alone: 16 bytes per
-// element) ran slower capped and keep every wave, as do launches of more
-// than 16 ranks, launches too small to fill the chip several times, and
-// the copy-in.
+// fused step at 8 ranks, the reduce at 16) 28160, 5 per CU; 16 or more (the
+// reduce at 8 ranks, Adam alone) 20480, about 8 per CU; launches over short
+// pieces, whose boundary tiles need more waves to hide their latency, 16384.
+// Lighter launches, launches of more than 16 ranks, launches too small to
+// fill the chip several times, and the copy-in keep every wave.
 constexpr size_t kLdsTunedPerCu = 163840;
 constexpr size_t kLdsHeavy = 40960;
 constexpr size_t kLdsMedium = 28160;
+constexpr size_t kLdsLight = 20480;
 constexpr size_t kLdsShortPieces = 16384;
 constexpr int kHeavyBytes = 40;
 constexpr int kMediumBytes = 24;
+constexpr int kLightBytes = 16;
 constexpr int64_t kCapMinTiles = 8192;
 
 size_t device_lds_per_cu() {
@@ -798,10 +799,11 @@ size_t shard_lds_pad(const ShardLaunch& L, int64_t blocks) {
         if (blocks < kCapMinTiles || device_lds_per_cu() != kLdsTunedPerCu) return 0;
         const int grad = uses_grads(OP) ? L.nd * int(sizeof(GT)) : 0;
         const int bytes = grad + (is_adam(OP) ? 12 : 0) + (reads_acc(OP) ? 4 : 0);
-        if (bytes < kMediumBytes) return 0;
-        const size_t total = L.short_pieces        ? kLdsShortPieces
-                             : bytes >= kHeavyBytes ? kLdsHeavy
-                                                    : kLdsMedium;
+        if (bytes < kLightBytes) return 0;
+        const size_t total = L.short_pieces         ? kLdsShortPieces
+                             : bytes >= kHeavyBytes  ? kLdsHeavy
+                             : bytes >= kMediumBytes ? kLdsMedium
+                                                     : kLdsLight;
         const size_t tables = kStage * (sizeof(int64_t) + sizeof(PieceInfo));
         return total > tables ? total - tables : 0;
     }
