@@ -3,6 +3,7 @@
 // every property the kernels' indexing relies on, so that no kernel can
 // address memory outside its buffers. Input on stdin: nd rank T numel...
 // (rank -1 = all ranks). Prints "ok" or the first violated property.
+#include <algorithm>
 #include <cstdio>
 #include <vector>
 
@@ -79,6 +80,18 @@ int main() {
         }
         if (nq > 0 && hg.k0[0] != 0) return bad("first gather piece", hg.k0[0], 0);
         if (check_tiles(hg.k0, hg.tile, hg.total)) return 1;
+        // tile_delta[g]: the piece delta exactly when the full tile g lies
+        // in one piece, else the marker
+        const int64_t gt = hg.total == 0 ? 0 : (hg.total + kTile - 1) / kTile;
+        if (int64_t(hg.tile_delta.size()) != gt) return bad("tile_delta size", hg.tile_delta.size(), gt);
+        for (int64_t g = 0; g < gt; ++g) {
+            const int64_t a = g * kTile, b = a + kTile;
+            const int64_t p = int64_t(std::upper_bound(hg.k0.begin(), hg.k0.end() - 1, a) -
+                                      hg.k0.begin()) - 1;
+            const bool one = b <= hg.total && b <= hg.k0[p + 1];
+            const int64_t want = one ? hg.delta[p] : kNoTileDelta;
+            if (hg.tile_delta[g] != want) return bad("tile_delta", g, hg.tile_delta[g]);
+        }
     }
     std::printf("ok %lld pieces\n", (long long)np);
     return 0;

@@ -173,6 +173,7 @@ CASES = [
     ([77777], 1),
     ([300, 7, 5000], 256),
     ([1003, 64, 5, 0, 3 * 4096 + 1], 40),   # ranks in batches of 16 with a partial batch
+    ([300 * 1001, 7, 200 * 513 + 3, 65536], 4),   # long pieces, unaligned parameter starts
     ([97, 12345, 7, 2048], 100),
     (synth.small_tensor_sizes(count=300, lo=8, hi=3000, seed=5), 8),
 ]
@@ -209,16 +210,26 @@ def test_gather_roundtrip_and_oracle(numels, nd):
             assert_bits(np_of(out[:nt]), oracle.gather(numels, nd, t, M.o_work), f"gather {t}")
 
 
-def test_gather_many_subranges():
-    numels = synth.small_tensor_sizes(count=200, lo=5, hi=2000, seed=9)
-    nd = 8
+# Short pieces take the gather's short-piece form; long ones its default form,
+# whose launches starting on a 512-element boundary look up one delta per tile.
+SUBRANGE_LAYOUTS = {
+    "short": (synth.small_tensor_sizes(count=200, lo=5, hi=2000, seed=9), 8),
+    "long": ([512 * 300, 4096 * 37 + 5, 100003, 77, 262144 + 13, 512 * 64, 9000], 8),
+}
+
+
+@pytest.mark.parametrize("which", list(SUBRANGE_LAYOUTS))
+def test_gather_many_subranges(which):
+    numels, nd = SUBRANGE_LAYOUTS[which]
     M = Mirror(numels, nd)
     L = M.L
     rng = np.random.default_rng(0)
     d = dev()
+    ranges = [(0, L.T), (1, L.T), (1, 2)]
     for _ in range(20):
         a = int(rng.integers(0, L.T))
-        b = int(rng.integers(a + 1, L.T + 1))
+        ranges.append((a, int(rng.integers(a + 1, L.T + 1))))
+    for a, b in ranges:
         cnt = int(L.flat_off[b] - L.flat_off[a])
         out = torch.empty(max(cnt, 8), dtype=torch.bfloat16, device=d)
         M.plan.gather_many(a, b - a, out, "work")

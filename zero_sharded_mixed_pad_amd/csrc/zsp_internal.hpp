@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime_api.h>
 
+#include <climits>
 #include <cstdint>
 #include <vector>
 
@@ -53,10 +54,14 @@ struct GatherTable {
     const int64_t* k0 = nullptr;
     const int64_t* delta = nullptr;
     const int32_t* tile = nullptr;
+    // per tile g: the delta of its piece when all kTile elements of the tile
+    // lie in one piece, else kNoTileDelta (one lookup for the common tile)
+    const int64_t* tile_delta = nullptr;
     int64_t nq = 0;
     int64_t ntile = 0;
     int64_t total = 0;
 };
+constexpr int64_t kNoTileDelta = INT64_MIN;
 
 // Host-side tables before upload.
 struct HostShardTable {
@@ -70,6 +75,7 @@ struct HostGatherTable {
     std::vector<int64_t> k0;
     std::vector<int64_t> delta;
     std::vector<int32_t> tile;
+    std::vector<int64_t> tile_delta;
     int64_t total = 0;
 };
 
@@ -112,6 +118,10 @@ struct GatherLaunch {
     const void* src = nullptr;
     void* out = nullptr;
     bool short_pieces = false;  // pieces average under kShortPiece elements
+    // tab.tile_delta offset to the launch's first tile when k_first is a
+    // multiple of kTile (local tile t is then global tile k_first/kTile + t),
+    // else NULL
+    const int64_t* tile_delta = nullptr;
 };
 
 // Below this average piece length (elements) a gather takes its short-piece

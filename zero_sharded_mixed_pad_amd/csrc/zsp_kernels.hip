@@ -594,6 +594,7 @@ struct GatherArgs {
     const int64_t* k0;
     const int64_t* delta;
     const int32_t* tile;
+    const int64_t* tile_delta;  // per local tile, or NULL (k_first not tile-aligned)
     int64_t k_first, count;
     const void* src;
     void* out;
@@ -643,12 +644,30 @@ __global__ __launch_bounds__(kWaveLanes) void gather_kernel(const GatherArgs a) 
         if (tile * kTile >= a.count) return;  // the grid is rounded up to 8 runs
     }
     const int64_t kw = tile * kTile;  // local start of the wave's tile
+    const T* src = static_cast<const T*>(a.src);
+    T* out = static_cast<T*>(a.out);
+    if (!SHORT && a.tile_delta && kw + kTile <= a.count) {
+        // Long pieces, tile-aligned launch: one scalar load says whether the
+        // whole tile is one run of one rank's slice, and gives that run's
+        // delta, a round trip ahead of the data instead of two. Short-piece
+        // launches, where many tiles miss, go straight to the bracket below.
+        const int64_t d = a.tile_delta[tile];
+        if (d != kNoTileDelta) {
+            const T* sb = src + (a.k_first + kw + d);
+            T* ob = out + kw;
+#pragma unroll
+            for (int h = 0; h < S::kGroups; ++h) {
+                const uint32_t o = h * S::kStride + uint32_t(lane) * S::kLaneStep;
+                stnt(reinterpret_cast<u32x4*>(ob + o),
+                     ld_src<SHORT>(reinterpret_cast<const u32x4_a2*>(sb + o)));
+            }
+            return;
+        }
+    }
     const int64_t kw_last = a.k_first + min(kw + kTile, a.count) - 1;
     const int lo = a.tile[(a.k_first + kw) / kTile];
     const int hi = a.tile[kw_last / kTile + 1];
     const int n = hi - lo + 1;
-    const T* src = static_cast<const T*>(a.src);
-    T* out = static_cast<T*>(a.out);
     const int64_t* k0 = a.k0 + lo;
     const int64_t* delta = a.delta + lo;
     if (n == 1) {
@@ -880,6 +899,7 @@ hipError_t launch_gather(const GatherLaunch& L, zsp_dtype dtype, hipStream_t str
     a.k0 = L.tab.k0;
     a.delta = L.tab.delta;
     a.tile = L.tab.tile;
+    a.tile_delta = L.tile_delta;
     a.k_first = L.k_first;
     a.count = L.count;
     a.src = L.src;

@@ -91,6 +91,14 @@ void build_gather_table(const std::vector<int64_t>& numel,
     out.total = flat_off[T];
     out.k0.push_back(out.total);
     build_tile_index(out.k0, out.total, out.tile);
+    // One lookup for a tile inside one piece: its piece's delta. A full tile
+    // g lies in piece p = tile[g] when p's run reaches (g+1)*kTile.
+    const int64_t ntile = out.tile.empty() ? 0 : int64_t(out.tile.size()) - 1;
+    out.tile_delta.assign(size_t(ntile), kNoTileDelta);
+    for (int64_t g = 0; g < ntile; ++g) {
+        const int32_t p = out.tile[size_t(g)];
+        if ((g + 1) * kTile <= out.k0[size_t(p) + 1]) out.tile_delta[size_t(g)] = out.delta[size_t(p)];
+    }
 }
 
 }  // namespace zsp
