@@ -5,10 +5,11 @@
 // chosen by measurement on MI355X:
 //
 //  * One wavefront per workgroup, owning one 512-element tile of the index
-//    space. Small workgroups keep more, shorter-lived waves in flight, which
-//    measured faster than 256-thread groups for these streams.
-//  * Large shard launches cap the workgroups resident per CU (4 to 10,
-//    through the LDS each reserves): fewer waves, each with 8-24 KiB of
+//    space, or one half of it (shard launches of up to 16 ranks over long
+//    pieces). Small workgroups keep more, shorter-lived waves in flight,
+//    which measured faster than 256-thread groups for these streams.
+//  * Large shard launches cap the workgroups resident per CU (7 to 16,
+//    through the LDS each reserves): fewer waves, each with 4-12 KiB of
 //    loads in flight, let HBM serve the mixed read/write streams faster
 //    than a full CU does. See shard_lds_pad.
 //  * Lane l owns two 4-element quads of the tile, at 4*l and 256 + 4*l, so
@@ -539,12 +540,16 @@ __device__ __forceinline__ void quad_one(const ShardArgs<CAP>& a, int64_t E, int
     }
 }
 
-template <int OP, typename GT, int CAP>
+// W waves per tile: W = 1, the wave takes both quads of each lane; W = 2,
+// workgroup 2i + h takes quad h (elements 256h .. 256h + 255) of tile i.
+template <int OP, typename GT, int CAP, int W>
 __global__ __launch_bounds__(kWaveLanes) void shard_kernel(const ShardArgs<CAP> a) {
+    static_assert(W == 1 || W == 2, "one or two waves per tile");
     __shared__ int64_t s_e0[kStage];
     __shared__ PieceInfo s_info[kStage];
     const int lane = threadIdx.x;
-    const int64_t tile = a.tile_first + blockIdx.x;
+    const int64_t tile = a.tile_first + blockIdx.x / W;
+    const int hw = W == 2 ? int(blockIdx.x % 2) : 0;
     const int64_t E0 = tile * kTile + int64_t(lane) * kQuad;
     // Wave-uniform bracket of the tile's pieces (scalar loads).
     const int lo = a.tile[tile];
@@ -557,11 +562,19 @@ __global__ __launch_bounds__(kWaveLanes) void shard_kernel(const ShardArgs<CAP> 
             // Every element real and in range: wave-uniform bases (scalar
             // registers) plus the lane's 32-bit offsets.
             const int64_t gbase = a.shard_layout ? T0 : T0 + pi.gdelta;
-            const int64_t Eb[2] = {T0, T0};
-            const int64_t gb[2] = {gbase, gbase};
-            const int64_t ib[2] = {T0 + pi.idelta, T0 + pi.idelta};
-            const uint32_t off[2] = {uint32_t(lane) * kQuad, uint32_t(lane) * kQuad + kHalf};
-            quads_fast<OP, GT, CAP, 2>(a, Eb, gb, ib, off);
+            if constexpr (W == 2) {
+                const int64_t Eb[1] = {T0};
+                const int64_t gb[1] = {gbase};
+                const int64_t ib[1] = {T0 + pi.idelta};
+                const uint32_t off[1] = {uint32_t(lane) * kQuad + uint32_t(hw) * uint32_t(kHalf)};
+                quads_fast<OP, GT, CAP, 1>(a, Eb, gb, ib, off);
+            } else {
+                const int64_t Eb[2] = {T0, T0};
+                const int64_t gb[2] = {gbase, gbase};
+                const int64_t ib[2] = {T0 + pi.idelta, T0 + pi.idelta};
+                const uint32_t off[2] = {uint32_t(lane) * kQuad, uint32_t(lane) * kQuad + kHalf};
+                quads_fast<OP, GT, CAP, 2>(a, Eb, gb, ib, off);
+            }
             return;
         }
     }
@@ -582,7 +595,7 @@ __global__ __launch_bounds__(kWaveLanes) void shard_kernel(const ShardArgs<CAP> 
         info = s_info;
     }
 #pragma unroll 1
-    for (int h = 0; h < 2; ++h) {
+    for (int h = hw; h < hw + 3 - W; ++h) {  // both quads, or the wave's one
         const int64_t E = E0 + h * kHalf;
         const int p = n == 1 ? 0 : find_local(e0, n, E);
         const PieceInfo pi = info[p];
@@ -777,22 +790,26 @@ __global__ __launch_bounds__(kWaveLanes) void gather_kernel(const GatherArgs a) 
 // streams, HBM serves the mix of reads and writes less efficiently than with
 // fewer waves resident, as long as each wave has enough bytes in flight.
 // The cap is set through the LDS each workgroup reserves (its piece tables
-// plus padding), at totals measured on MI355X (160 KiB of LDS per CU) by the
-// bytes a launch reads per element: 40 or more (the fused step at 16 ranks
-// with its accumulator) 40960 bytes, 4 workgroups per CU; 24 or more (the
-// fused step at 8 ranks, the reduce at 16) 28160, 5 per CU; 16 or more (the
-// reduce at 8 ranks, Adam alone) 20480, about 8 per CU; launches over short
-// pieces, whose boundary tiles need more waves to hide their latency, 16384.
-// Lighter launches, launches of more than 16 ranks, launches too small to
-// fill the chip several times, and the copy-in keep every wave.
+// plus padding), at totals measured on MI355X (160 KiB of LDS per CU).
+// Half-tile waves (launches of up to 16 ranks over long pieces), by kind and
+// by the bytes read per element: the fused step reading 40 or more (16 ranks
+// with the accumulator) 23405 bytes, 7 workgroups per CU; a lighter fused
+// step (8 ranks) 16384, 10 per CU; Adam alone 13312, 12 per CU; the reduce
+// reading 24 or more (16 ranks) 13312, 12 per CU; a lighter reduce (8 ranks)
+// 10240, 16 per CU. Whole-tile waves over short pieces, whose boundary tiles
+// need more waves to hide their latency: 16384, 10 per CU, from 16 bytes per
+// element. Lighter launches, launches of more than 16 ranks, launches too
+// small to fill the chip several times, and the copy-in keep every wave.
 constexpr size_t kLdsTunedPerCu = 163840;
-constexpr size_t kLdsHeavy = 40960;
-constexpr size_t kLdsMedium = 28160;
-constexpr size_t kLdsLight = 20480;
+constexpr size_t kLdsFusedHeavy = 23405;
+constexpr size_t kLdsFused = 16384;
+constexpr size_t kLdsAdamAlone = 13312;
+constexpr size_t kLdsReduceHeavy = 13312;
+constexpr size_t kLdsReduce = 10240;
 constexpr size_t kLdsShortPieces = 16384;
-constexpr int kHeavyBytes = 40;
-constexpr int kMediumBytes = 24;
-constexpr int kLightBytes = 16;
+constexpr int kHeavyFusedBytes = 40;
+constexpr int kHeavyReduceBytes = 24;
+constexpr int kShortCapBytes = 16;
 constexpr int64_t kCapMinTiles = 8192;
 
 size_t device_lds_per_cu() {
@@ -809,24 +826,38 @@ size_t device_lds_per_cu() {
     return v > 0 ? size_t(v) : 0;
 }
 
-// Dynamic LDS that brings a shard workgroup to the reservation above, or 0.
-template <int OP, typename GT, int CAP>
-size_t shard_lds_pad(const ShardLaunch& L, int64_t blocks) {
+// Dynamic LDS that brings a shard workgroup (W waves per tile) to the
+// reservation above, or 0.
+template <int OP, typename GT, int CAP, int W>
+size_t shard_lds_pad(const ShardLaunch& L, int64_t tiles) {
     if constexpr (CAP > 16 || OP == OP_COPYIN) {
         return 0;
     } else {
-        if (blocks < kCapMinTiles || device_lds_per_cu() != kLdsTunedPerCu) return 0;
+        if (tiles < kCapMinTiles || device_lds_per_cu() != kLdsTunedPerCu) return 0;
         const int grad = uses_grads(OP) ? L.nd * int(sizeof(GT)) : 0;
         const int bytes = grad + (is_adam(OP) ? 12 : 0) + (reads_acc(OP) ? 4 : 0);
-        if (bytes < kLightBytes) return 0;
-        const size_t total = L.short_pieces         ? kLdsShortPieces
-                             : bytes >= kHeavyBytes  ? kLdsHeavy
-                             : bytes >= kMediumBytes ? kLdsMedium
-                                                     : kLdsLight;
+        size_t total = 0;
+        if constexpr (W == 1) {
+            if (!L.short_pieces || bytes < kShortCapBytes) return 0;
+            total = kLdsShortPieces;
+        } else if constexpr (OP == OP_ADAM) {
+            total = kLdsAdamAlone;
+        } else if constexpr (is_adam(OP)) {
+            total = bytes >= kHeavyFusedBytes ? kLdsFusedHeavy : kLdsFused;
+        } else {
+            total = bytes >= kHeavyReduceBytes ? kLdsReduceHeavy : kLdsReduce;
+        }
         const size_t tables = kStage * (sizeof(int64_t) + sizeof(PieceInfo));
         return total > tables ? total - tables : 0;
     }
 }
+
+// Half-tile waves: shard launches of up to 16 ranks over long pieces (not
+// the copy-in). Measured faster there under the caps above (+6-8% on the
+// fused step, +1-6% on the reduce, +7% on Adam alone); whole-tile waves
+// stay faster over short pieces and for more ranks.
+template <int OP, int CAP>
+constexpr bool kHalfTiles = CAP <= 16 && OP != OP_COPYIN;
 
 template <int OP, typename GT, int CAP>
 hipError_t launch_t(const ShardLaunch& L, hipStream_t stream) {
@@ -850,11 +881,21 @@ hipError_t launch_t(const ShardLaunch& L, hipStream_t stream) {
     if constexpr (uses_grads(OP)) {
         for (int r = 0; r < L.nd; ++r) a.grads[r] = L.grads[r];
     }
-    const int64_t blocks = tile_end - a.tile_first;  // one wave per tile
-    if (blocks <= 0) return hipSuccess;
-    if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-    const size_t lds_pad = shard_lds_pad<OP, GT, CAP>(L, blocks);
-    hipLaunchKernelGGL((shard_kernel<OP, GT, CAP>), dim3(static_cast<uint32_t>(blocks)),
+    const int64_t tiles = tile_end - a.tile_first;
+    if (tiles <= 0) return hipSuccess;
+    if constexpr (kHalfTiles<OP, CAP>) {
+        if (!L.short_pieces) {
+            if (2 * tiles > 0x7fffffffLL) return hipErrorInvalidValue;
+            const size_t lds_pad = shard_lds_pad<OP, GT, CAP, 2>(L, tiles);
+            hipLaunchKernelGGL((shard_kernel<OP, GT, CAP, 2>),
+                               dim3(static_cast<uint32_t>(2 * tiles)), dim3(kWaveLanes), lds_pad,
+                               stream, a);
+            return hipGetLastError();
+        }
+    }
+    if (tiles > 0x7fffffffLL) return hipErrorInvalidValue;
+    const size_t lds_pad = shard_lds_pad<OP, GT, CAP, 1>(L, tiles);
+    hipLaunchKernelGGL((shard_kernel<OP, GT, CAP, 1>), dim3(static_cast<uint32_t>(tiles)),
                        dim3(kWaveLanes), lds_pad, stream, a);
     return hipGetLastError();
 }
