@@ -859,6 +859,9 @@ size_t shard_lds_pad(const ShardLaunch& L, int64_t tiles) {
 template <int OP, int CAP>
 constexpr bool kHalfTiles = CAP <= 16 && OP != OP_COPYIN;
 
+// A launch's work-items (workgroups x 64) must fit in 32 bits.
+constexpr int64_t kMaxBlocks = int64_t(UINT32_MAX) / kWaveLanes;
+
 template <int OP, typename GT, int CAP>
 hipError_t launch_t(const ShardLaunch& L, hipStream_t stream) {
     ShardArgs<CAP> a{};
@@ -884,8 +887,7 @@ hipError_t launch_t(const ShardLaunch& L, hipStream_t stream) {
     const int64_t tiles = tile_end - a.tile_first;
     if (tiles <= 0) return hipSuccess;
     if constexpr (kHalfTiles<OP, CAP>) {
-        if (!L.short_pieces) {
-            if (2 * tiles > 0x7fffffffLL) return hipErrorInvalidValue;
+        if (!L.short_pieces && 2 * tiles <= kMaxBlocks) {
             const size_t lds_pad = shard_lds_pad<OP, GT, CAP, 2>(L, tiles);
             hipLaunchKernelGGL((shard_kernel<OP, GT, CAP, 2>),
                                dim3(static_cast<uint32_t>(2 * tiles)), dim3(kWaveLanes), lds_pad,
@@ -893,7 +895,7 @@ hipError_t launch_t(const ShardLaunch& L, hipStream_t stream) {
             return hipGetLastError();
         }
     }
-    if (tiles > 0x7fffffffLL) return hipErrorInvalidValue;
+    if (tiles > kMaxBlocks) return hipErrorInvalidValue;
     const size_t lds_pad = shard_lds_pad<OP, GT, CAP, 1>(L, tiles);
     hipLaunchKernelGGL((shard_kernel<OP, GT, CAP, 1>), dim3(static_cast<uint32_t>(tiles)),
                        dim3(kWaveLanes), lds_pad, stream, a);
@@ -948,7 +950,7 @@ hipError_t launch_gather(const GatherLaunch& L, zsp_dtype dtype, hipStream_t str
     const int64_t tiles = (L.count + kTile - 1) / kTile;  // one wave per 512 outputs
     const int64_t runs = 8 * kXcdRun;
     const int64_t blocks = L.short_pieces ? (tiles + runs - 1) / runs * runs : tiles;
-    if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+    if (blocks > kMaxBlocks) return hipErrorInvalidValue;
     const dim3 grid(static_cast<uint32_t>(blocks)), block(kWaveLanes);
     if (dtype == ZSP_BF16) {
         if (L.short_pieces)
