@@ -801,6 +801,9 @@ def main():
             "kernel": ("fused reduce+Adam+cast (all ranks, one launch)" if dom == "fused"
                        else "shard reduce (all ranks, one launch)"),
             "bytes_per_launch": fused["bytes_per_launch"], "avg_launch_us": fused["avg_us"]}
+    # counter-measured HBM bytes (FETCH_SIZE + WRITE_SIZE) over the same launch time
+    roof["traffic_GBps"] = (round(roof["traffic"] / fused["avg_us"] / 1e3, 1)
+                            if roof["traffic"] and fused["avg_us"] else None)
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(r, args.cpu_seconds)

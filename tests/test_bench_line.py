@@ -46,6 +46,11 @@ def test_json_line_is_consistent():
     assert roof["frac"] == pytest.approx(roof["achieved"] / roof["peak"], abs=1e-4)
     assert roof["achieved"] == pytest.approx(
         roof["bytes_per_launch"] / roof["avg_launch_us"] / 1e3, rel=2e-3)
+    if roof["traffic"] is None:
+        assert roof["traffic_GBps"] is None
+    else:
+        assert roof["traffic_GBps"] == pytest.approx(
+            roof["traffic"] / roof["avg_launch_us"] / 1e3, rel=2e-3)
     fused = d["kernels"]["fused"]
     assert fused["launches"] == 3 and fused["min_us"] <= fused["median_us"]
     cpu = d["cpu_baseline"]
