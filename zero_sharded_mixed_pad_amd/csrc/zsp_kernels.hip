@@ -20,10 +20,11 @@
 //  * Every stream is touched once per launch, so global loads and stores
 //    carry the non-temporal hint; that measured a further ~5%. The one
 //    exception is the gather over short pieces (below).
-//  * The optimizer state of both quads is loaded before the gradients so the
-//    state's latency overlaps the rank loop.
+//  * The optimizer state of the wave's quads is loaded before the gradients
+//    so the state's latency overlaps the rank loop.
 //  * The tile's parameter comes from a per-tile table: wave-uniform, so the
-//    common single-parameter tile costs two scalar loads. A launch can span
+//    common single-parameter tile costs two scalar loads (a gather over long
+//    pieces reads one per-tile delta instead). A launch can span
 //    any number of parameters -- thousands of small ones as easily as one
 //    large one -- with no per-parameter launch.
 //  * Gradient and parameter sources may sit at any 2-byte offset relative to
@@ -32,10 +33,10 @@
 //    stays one vector load per quad. Quads that cross a parameter or pad
 //    boundary keep vector state access and mask per element; only quads at
 //    the edge of a launch's range go element by element.
-//  * The reduce over N_d ranks keeps each lane's 8 sums in registers and adds
-//    rank r's values strictly after rank r-1's (fixed order, bit-exact); the
-//    ranks are loaded 8 at a time (16 at a time for more than 16 ranks), so
-//    16 (32) loads per lane are in flight.
+//  * The reduce over N_d ranks keeps each lane's 4 or 8 sums in registers
+//    and adds rank r's values strictly after rank r-1's (fixed order,
+//    bit-exact); the ranks are loaded 8 at a time (16 at a time for more
+//    than 16 ranks), so 8 to 32 loads per lane are in flight.
 //  * Floating point: built with -ffp-contract=off; division and square root
 //    are the default correctly rounded expansions; bf16 narrowing is the
 //    hardware round-to-nearest-even convert (v_cvt_pk_bf16_f32).
@@ -579,9 +580,10 @@ __global__ __launch_bounds__(kWaveLanes) void shard_kernel(const ShardArgs<CAP> 
         }
     }
     // A tile at a piece, pad or range boundary. Several pieces: stage their
-    // table in LDS with one coalesced load and search it there. The two quads
-    // go through one call site (a loop kept rolled): each copy of the update
-    // is long, and fewer copies keep the kernel within the instruction cache.
+    // table in LDS with one coalesced load and search it there. A whole-tile
+    // wave's two quads go through one call site (a loop kept rolled): each
+    // copy of the update is long, and fewer copies keep the kernel within
+    // the instruction cache.
     const int n = hi - lo + 1;
     const int64_t* e0 = a.e0 + lo;
     const PieceInfo* info = a.info + lo;
