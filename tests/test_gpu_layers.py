@@ -15,6 +15,10 @@ from zero_sharded_mixed_pad_amd import binding
 
 from test_gpu_parity import CASES, HP, Mirror, assert_bits, dev, np_of
 
+# Long pieces (two waves per tile) over several parameters whose slots start
+# mid-tile, so per-group ranges cut tiles at both ends.
+LONG = ([300 * 1001, 7, 200 * 513 + 3, 65536, 4096 * 9 + 1], 4)
+
 pytestmark = pytest.mark.gpu
 
 
@@ -38,7 +42,7 @@ def slot_mask(M, first, n):
     return mask
 
 
-@pytest.mark.parametrize("numels,nd", CASES[:9])
+@pytest.mark.parametrize("numels,nd", CASES[:9] + [LONG])
 def test_reduce_by_groups(numels, nd):
     M = Mirror(numels, nd)
     grads = M.grads(torch.bfloat16, "layers-reduce")
@@ -56,7 +60,7 @@ def test_reduce_by_groups(numels, nd):
     assert written.all()
 
 
-@pytest.mark.parametrize("numels,nd", CASES[:9])
+@pytest.mark.parametrize("numels,nd", CASES[:9] + [LONG])
 def test_fused_update_by_groups(numels, nd):
     M = Mirror(numels, nd)
     for step in (1, 2):
@@ -69,7 +73,7 @@ def test_fused_update_by_groups(numels, nd):
         assert M.check_state(f"step {step}") == 0
 
 
-@pytest.mark.parametrize("numels,nd", CASES[:6])
+@pytest.mark.parametrize("numels,nd", CASES[:6] + [LONG])
 def test_reduce_then_adam_by_groups(numels, nd):
     M = Mirror(numels, nd)
     grads = M.grads(torch.bfloat16, "layers-acc")
