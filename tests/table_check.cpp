@@ -84,6 +84,7 @@ int main() {
         // in one piece, else the marker
         const int64_t gt = hg.total == 0 ? 0 : (hg.total + kTile - 1) / kTile;
         if (int64_t(hg.tile_delta.size()) != gt) return bad("tile_delta size", hg.tile_delta.size(), gt);
+        if (int64_t(hg.tile_pair.size()) != 3 * gt) return bad("tile_pair size", hg.tile_pair.size(), 3 * gt);
         for (int64_t g = 0; g < gt; ++g) {
             const int64_t a = g * kTile, b = a + kTile;
             const int64_t p = int64_t(std::upper_bound(hg.k0.begin(), hg.k0.end() - 1, a) -
@@ -91,6 +92,18 @@ int main() {
             const bool one = b <= hg.total && b <= hg.k0[p + 1];
             const int64_t want = one ? hg.delta[p] : kNoTileDelta;
             if (hg.tile_delta[g] != want) return bad("tile_delta", g, hg.tile_delta[g]);
+            // tile_pair: pieces holding the tile's first and last element
+            const int64_t e = std::min(b, hg.total) - 1;
+            const int64_t q = int64_t(std::upper_bound(hg.k0.begin(), hg.k0.end() - 1, e) -
+                                      hg.k0.begin()) - 1;
+            const int64_t* r = &hg.tile_pair[size_t(3 * g)];
+            if (q - p >= 2) {
+                if (r[0] != kNoTileDelta) return bad("tile_pair marker", g, r[0]);
+            } else {
+                const int64_t split = q > p ? hg.k0[q] : INT64_MAX;
+                if (r[0] != split || r[1] != hg.delta[p] || r[2] != hg.delta[q])
+                    return bad("tile_pair", g, r[0]);
+            }
         }
     }
     std::printf("ok %lld pieces\n", (long long)np);

@@ -215,6 +215,8 @@ def test_gather_roundtrip_and_oracle(numels, nd):
 SUBRANGE_LAYOUTS = {
     "short": (synth.small_tensor_sizes(count=200, lo=5, hi=2000, seed=9), 8),
     "long": ([512 * 300, 4096 * 37 + 5, 100003, 77, 262144 + 13, 512 * 64, 9000], 8),
+    # short pieces with a tile-aligned second parameter (per-tile pair records)
+    "short_aligned": ([512 * 3, 8000, 7777, 15000, 640, 20480, 3, 15000, 9, 4096], 8),
 }
 
 

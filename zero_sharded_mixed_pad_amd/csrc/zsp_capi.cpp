@@ -278,15 +278,15 @@ zsp_status zsp_bind_state(zsp_plan* P, int32_t rank_or_all, float* master, float
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
 
-    // One allocation: [e0 | info | tile | k0 | delta | gtile | gtile_delta],
-    // 256-byte aligned parts.
-    constexpr int kParts = 7;
+    // One allocation: [e0 | info | tile | k0 | delta | gtile | gtile_delta |
+    // gtile_pair], 256-byte aligned parts.
+    constexpr int kParts = 8;
     const size_t sz[kParts] = {bytes_of(hs.e0), bytes_of(hs.info),  bytes_of(hs.tile),
                                bytes_of(hg.k0), bytes_of(hg.delta), bytes_of(hg.tile),
-                               bytes_of(hg.tile_delta)};
+                               bytes_of(hg.tile_delta), bytes_of(hg.tile_pair)};
     const void* src[kParts] = {hs.e0.data(), hs.info.data(),  hs.tile.data(),
                                hg.k0.data(), hg.delta.data(), hg.tile.data(),
-                               hg.tile_delta.data()};
+                               hg.tile_delta.data(), hg.tile_pair.data()};
     size_t off[kParts], total = 0;
     for (int i = 0; i < kParts; ++i) {
         off[i] = total;
@@ -322,6 +322,7 @@ zsp_status zsp_bind_state(zsp_plan* P, int32_t rank_or_all, float* master, float
         P->gather.delta = reinterpret_cast<const int64_t*>(b + off[4]);
         P->gather.tile = reinterpret_cast<const int32_t*>(b + off[5]);
         P->gather.tile_delta = reinterpret_cast<const int64_t*>(b + off[6]);
+        P->gather.tile_pair = reinterpret_cast<const int64_t*>(b + off[7]);
         P->gather.nq = int64_t(hg.delta.size());
         P->gather.ntile = hg.tile.empty() ? 0 : int64_t(hg.tile.size()) - 1;
         P->gather.total = hg.total;
@@ -520,8 +521,10 @@ zsp_status zsp::gather_range(zsp_plan* P, int32_t first_param, int32_t n_params,
     L.out = out;
     const int64_t pieces = P->piece_off[first_param + n_params] - P->piece_off[first_param];
     L.short_pieces = pieces > 0 && count < pieces * zsp::kShortPiece;
-    if (k_first % zsp::kTile == 0 && P->gather.tile_delta)
+    if (k_first % zsp::kTile == 0 && P->gather.tile_delta) {
         L.tile_delta = P->gather.tile_delta + k_first / zsp::kTile;
+        L.tile_pair = P->gather.tile_pair + 3 * (k_first / zsp::kTile);
+    }
     hipError_t e = zsp::launch_gather(L, src == ZSP_SRC_WORK ? ZSP_BF16 : ZSP_F32, stream);
     if (e != hipSuccess) return fail_hip(e, "gather launch");
     return ZSP_OK;

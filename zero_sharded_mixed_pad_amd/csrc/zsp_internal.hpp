@@ -57,6 +57,10 @@ struct GatherTable {
     // per tile g: the delta of its piece when all kTile elements of the tile
     // lie in one piece, else kNoTileDelta (one lookup for the common tile)
     const int64_t* tile_delta = nullptr;
+    // per tile g, three values at 3g: when the tile's elements lie in at most
+    // two pieces, the start of the second (INT64_MAX if one) and the deltas
+    // of the first and second; else kNoTileDelta first (short-piece gathers)
+    const int64_t* tile_pair = nullptr;
     int64_t nq = 0;
     int64_t ntile = 0;
     int64_t total = 0;
@@ -76,6 +80,7 @@ struct HostGatherTable {
     std::vector<int64_t> delta;
     std::vector<int32_t> tile;
     std::vector<int64_t> tile_delta;
+    std::vector<int64_t> tile_pair;
     int64_t total = 0;
 };
 
@@ -122,6 +127,7 @@ struct GatherLaunch {
     // multiple of kTile (local tile t is then global tile k_first/kTile + t),
     // else NULL
     const int64_t* tile_delta = nullptr;
+    const int64_t* tile_pair = nullptr;  // tab.tile_pair likewise, or NULL
 };
 
 // Below this average piece length (elements) a gather takes its short-piece

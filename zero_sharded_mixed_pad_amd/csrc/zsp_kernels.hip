@@ -23,10 +23,11 @@
 //  * The optimizer state of the wave's quads is loaded before the gradients
 //    so the state's latency overlaps the rank loop.
 //  * The tile's parameter comes from a per-tile table: wave-uniform, so the
-//    common single-parameter tile costs two scalar loads (a gather over long
-//    pieces reads one per-tile delta instead). A launch can span
-//    any number of parameters -- thousands of small ones as easily as one
-//    large one -- with no per-parameter launch.
+//    common single-parameter tile costs two scalar loads (a tile-aligned
+//    gather reads one per-tile record instead: its piece's delta over long
+//    pieces, the split and both deltas of at most two short pieces). A
+//    launch can span any number of parameters -- thousands of small ones as
+//    easily as one large one -- with no per-parameter launch.
 //  * Gradient and parameter sources may sit at any 2-byte offset relative to
 //    the quads (each parameter is padded on its own, so slices do not line
 //    up). gfx9 global memory serves unaligned vector loads, so the fast path
@@ -610,6 +611,7 @@ struct GatherArgs {
     const int64_t* delta;
     const int32_t* tile;
     const int64_t* tile_delta;  // per local tile, or NULL (k_first not tile-aligned)
+    const int64_t* tile_pair;   // three per local tile, or NULL likewise
     int64_t k_first, count;
     const void* src;
     void* out;
@@ -675,6 +677,43 @@ __global__ __launch_bounds__(kWaveLanes) void gather_kernel(const GatherArgs a) 
                 const uint32_t o = h * S::kStride + uint32_t(lane) * S::kLaneStep;
                 stnt(reinterpret_cast<u32x4*>(ob + o),
                      ld_src<SHORT>(reinterpret_cast<const u32x4_a2*>(sb + o)));
+            }
+            return;
+        }
+    }
+    if (SHORT && a.tile_pair) {
+        // Short pieces, tile-aligned launch: one record gives the tile's (at
+        // most two) pieces: the second's start and both deltas.
+        const int64_t* rec = a.tile_pair + 3 * tile;
+        const int64_t split = rec[0];
+        if (split != kNoTileDelta) {
+            const int64_t d0 = rec[1], d1 = rec[2];
+#pragma unroll
+            for (int h = 0; h < S::kGroups; ++h) {
+                const int64_t k = kw + h * S::kStride + int64_t(lane) * S::kLaneStep;
+                if (k >= a.count) continue;
+                const int64_t K = a.k_first + k;
+                if (k + S::kGroup <= a.count && (K + S::kGroup <= split || K >= split)) {
+                    const int64_t d = K < split ? d0 : d1;
+                    stnt(reinterpret_cast<u32x4*>(out + k),
+                         ld_src<SHORT>(reinterpret_cast<const u32x4_a2*>(src + K + d)));
+                } else {
+                    // Crosses the split or the end: element by element, every
+                    // load issued (clamped to the launch's last element).
+                    T x[S::kGroup];
+#pragma unroll
+                    for (int i = 0; i < S::kGroup; ++i) {
+                        const int64_t KK = min(K + i, a.k_first + a.count - 1);
+                        x[i] = src[KK + (KK < split ? d0 : d1)];
+                    }
+                    if (k + S::kGroup <= a.count) {
+                        stnt(reinterpret_cast<u32x4*>(out + k), __builtin_bit_cast(u32x4, x));
+                    } else {
+#pragma unroll
+                        for (int i = 0; i < S::kGroup; ++i)
+                            if (k + i < a.count) out[k + i] = x[i];
+                    }
+                }
             }
             return;
         }
@@ -945,6 +984,7 @@ hipError_t launch_gather(const GatherLaunch& L, zsp_dtype dtype, hipStream_t str
     a.delta = L.tab.delta;
     a.tile = L.tab.tile;
     a.tile_delta = L.tile_delta;
+    a.tile_pair = L.tile_pair;
     a.k_first = L.k_first;
     a.count = L.count;
     a.src = L.src;

@@ -99,6 +99,23 @@ void build_gather_table(const std::vector<int64_t>& numel,
         const int32_t p = out.tile[size_t(g)];
         if ((g + 1) * kTile <= out.k0[size_t(p) + 1]) out.tile_delta[size_t(g)] = out.delta[size_t(p)];
     }
+    // Short-piece gathers: a tile within at most two pieces gets the second
+    // piece's start and both deltas, one record instead of two lookups.
+    out.tile_pair.assign(size_t(3 * ntile), 0);
+    for (int64_t g = 0; g < ntile; ++g) {
+        const int64_t p = out.tile[size_t(g)];
+        const int64_t last = std::min((g + 1) * kTile, out.total) - 1;
+        int64_t q = p;
+        while (q - p < 2 && out.k0[size_t(q) + 1] <= last) ++q;
+        int64_t* r = &out.tile_pair[size_t(3 * g)];
+        if (q - p >= 2) {
+            r[0] = kNoTileDelta;
+        } else {
+            r[0] = q > p ? out.k0[size_t(q)] : INT64_MAX;
+            r[1] = out.delta[size_t(p)];
+            r[2] = out.delta[size_t(q)];
+        }
+    }
 }
 
 }  // namespace zsp
