@@ -143,7 +143,10 @@ zsp_status zsp_plan_tensor(const zsp_plan* plan, int32_t t, int64_t* numel, int6
  *   master, m, v: fp32; work: bf16 bit patterns; grad_acc: fp32 accumulator
  *     or NULL (then accumulate/use_acc calls fail with ZSP_ESTATE).
  * Allocates the device tables (setup path; the only device allocation the
- * library makes). Rebinding replaces the previous binding. */
+ * library makes): 56 bytes per piece (one rank's slice of one parameter),
+ * 4 bytes per 512 elements of the bound state and 36 bytes per 512
+ * elements of the unpadded parameters. Rebinding replaces the previous
+ * binding. */
 zsp_status zsp_bind_state(zsp_plan* plan, int32_t rank_or_all, float* master, float* m,
                           float* v, uint16_t* work, float* grad_acc);
 
