@@ -143,8 +143,9 @@ zsp_status zsp_plan_tensor(const zsp_plan* plan, int32_t t, int64_t* numel, int6
  *   master, m, v: fp32; work: bf16 bit patterns; grad_acc: fp32 accumulator
  *     or NULL (then accumulate/use_acc calls fail with ZSP_ESTATE).
  * Allocates the device tables (setup path; the only device allocation the
- * library makes): 56 bytes per piece (one rank's slice of one parameter),
- * 4 bytes per 512 elements of the bound state and 36 bytes per 512
+ * library makes): 40 bytes per bound piece (one rank's slice of one
+ * parameter) and 4 bytes per 512 elements of the bound state; an all-rank
+ * binding adds the gather's 16 bytes per piece and 36 bytes per 512
  * elements of the unpadded parameters. Rebinding replaces the previous
  * binding. */
 zsp_status zsp_bind_state(zsp_plan* plan, int32_t rank_or_all, float* master, float* m,
