@@ -667,7 +667,7 @@ __global__ __launch_bounds__(kWaveLanes) void gather_kernel(const GatherArgs a) 
         // Long pieces, tile-aligned launch: one scalar load says whether the
         // whole tile is one run of one rank's slice, and gives that run's
         // delta, a round trip ahead of the data instead of two. Short-piece
-        // launches, where many tiles miss, go straight to the bracket below.
+        // launches read a record of their own (below).
         const int64_t d = a.tile_delta[tile];
         if (d != kNoTileDelta) {
             const T* sb = src + (a.k_first + kw + d);
