@@ -1,12 +1,14 @@
 """The library's offset tables satisfy every property its kernels index by
 (CPU only): pieces ordered and non-empty, every gradient / parameter /
-gather source range inside its buffer, and each tile-table entry naming the
-piece that holds the tile's first element. Built from the library's own host
-code with g++ (AddressSanitizer and UBSan on) and driven over small edge
-cases and the full workloads."""
+gather source range inside its buffer, each tile-table entry naming the
+piece that holds the tile's first element, and the gather's per-tile deltas
+and two-piece records matching a search of the piece starts. Built from the
+library's own host code with g++ (AddressSanitizer and UBSan on) and driven
+over small edge cases, seeded random layouts and the full workloads."""
 import os
 import subprocess
 
+import numpy as np
 import pytest
 
 from zero_sharded_mixed_pad_amd import synth
@@ -62,3 +64,18 @@ def test_decoder_stack_tables(checker):
     w = synth.llama_stack(32, 8)
     assert sum(w.numel) > 2 ** 32
     run(checker, w.numel, w.n_d, -1)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_layout_tables(checker, seed):
+    """Seeded random layouts: parameter sizes spread over five decades (zero
+    included), so tiles hold one, two or many pieces and slices start at
+    every alignment; every rank count from 1 to 70 across the seeds."""
+    rng = np.random.default_rng(1000 + seed)
+    for _ in range(8):
+        count = int(rng.integers(1, 120))
+        numels = [int(x) for x in np.floor(np.exp(rng.uniform(0, np.log(2e5), count)))]
+        numels = [0 if rng.random() < 0.05 else n for n in numels]
+        nd = int(rng.integers(1, 71))
+        for rank in (-1, int(rng.integers(0, nd))):
+            run(checker, numels, nd, rank)
