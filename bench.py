@@ -15,9 +15,14 @@ count what the method must move per real (non-pad) element:
   gather                   2*w (read shard, write full) per unpadded element
 with g, w the gradient and parameter element sizes in bytes.
 
-Prints one JSON line: the metric, a roofline object for the dominant kernel
-(HIP-event time, peak, and HBM traffic from stored PMC counters when they
-match the kernels' source) and the CPU oracle's figure on a bounded sample.
+Prints one JSON line for --workload (default: the 8192x28672 MLP at N_d = 16
+with 8 micro-batches, the largest workload; its step is seven reduce
+launches, one fused reduce+accumulate+Adam+cast launch and the gathers):
+the metric over the whole step, a roofline object for the kind of launch
+that takes the most time per step (HIP-event time, peak, and HBM traffic
+from stored PMC counters when they match the kernels' source), the CPU
+oracle's figure on a bounded sample, and, under "workloads", the same
+per-kernel figures for every other workload (--only skips them).
 
 Other modes, each printing its own JSON line:
   --stage 1|2   the step in the ZeRO stage-1 or stage-2 schedule
@@ -42,8 +47,10 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, AMD's published figure
-DEFAULT_WORKLOAD = "llama7b_layer_nd8"
+DEFAULT_WORKLOAD = "mlp8192x28672_accum_nd16"
 METRIC = "effective GB/s (and % HBM peak) of shard reduce+Adam+cast step and param gather"
+# Kinds of launch inside one step, in bench.py's event records.
+STEP_KINDS = ("reduce_set", "reduce_acc", "fused", "adam", "gather_acc", "gather")
 KERNEL_SOURCES = ["zero_sharded_mixed_pad_amd/csrc/zsp_kernels.hip",
                   "zero_sharded_mixed_pad_amd/csrc/zsp_internal.hpp"]
 
@@ -72,6 +79,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", dest="all_workloads", action="store_false",
+                    help="time only --workload (default: also every other workload, "
+                         "reported under 'workloads')")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time for the oracle baseline sample")
     ap.add_argument("--flush", choices=["auto", "on", "off"], default="auto",
@@ -180,8 +190,7 @@ class Runner:
                 out = torch.empty(cnt, dtype=bf16, device=device)
                 self.gather_groups.append((first, n, out, cnt * 4))
         self.step_no = 0
-        self.ev = {"fused": [], "reduce": [], "gather": [], "adam": [], "gather_acc": [],
-                   "gather_cold": []}
+        self.ev = {k: [] for k in STEP_KINDS + ("gather_cold",)}
 
     def _event(self):
         return self.torch.cuda.Event(enable_timing=True)
@@ -201,7 +210,7 @@ class Runner:
         self.step_no += 1
         hp = dict(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, step=self.step_no)
         if self.stage == 1:
-            self._timed("reduce", lambda: p.reduce_shard(
+            self._timed("reduce_set", lambda: p.reduce_shard(
                 self.rank, self.grads, layout=self.layout, accumulate=False), record)
             self._timed("gather_acc", lambda: p.gather_many(
                 0, len(w.numel), self.grad_replica, "acc"), record)
@@ -212,12 +221,12 @@ class Runner:
             return
         if self.split:  # unfused: reduce into the accumulator, then Adam from it
             for mb in range(w.micro_batches):
-                self._timed("reduce", lambda mb=mb: p.reduce_shard(
+                self._timed("reduce_acc" if mb > 0 else "reduce_set", lambda mb=mb: p.reduce_shard(
                     self.rank, self.grads, layout=self.layout, accumulate=mb > 0), record)
             self._timed("adam", lambda: p.adam_step(self.rank, **hp), record)
         elif w.micro_batches > 1:
             for mb in range(w.micro_batches - 1):
-                self._timed("reduce", lambda mb=mb: p.reduce_shard(
+                self._timed("reduce_acc" if mb > 0 else "reduce_set", lambda mb=mb: p.reduce_shard(
                     self.rank, self.grads, layout=self.layout, accumulate=mb > 0), record)
             self._timed("fused", lambda: p.reduce_adam_step(
                 self.rank, self.grads, layout=self.layout, use_acc=True, **hp), record)
@@ -256,38 +265,63 @@ class Runner:
         b += (2 if self.stage == 3 else 1) * gathers
         return b
 
-    def kernel_stats(self):
+    def bytes_of(self, kind):
+        """Algorithmic bytes one launch of `kind` moves."""
+        if kind == "fused":
+            return self.bytes_fused
+        if kind == "reduce_set":
+            return self.bytes_reduce_first
+        if kind == "reduce_acc":
+            return self.bytes_reduce_acc
+        if kind == "adam":
+            return self.bytes_adam
+        if kind == "gather_acc":
+            return self.bytes_gather_acc
+        return sum(g[3] for g in self.gather_groups) / len(self.gather_groups)
+
+    def trace_name(self, kind):
+        """The kernel's name in the rocprofv3 summaries (bench.py --rocprof-summary)."""
+        gdt = "bf16" if self.w.grad_dtype == self.torch.bfloat16 else "f32"
+        if kind == "fused":
+            acc = "_acc" if self.w.micro_batches > 1 and not self.split else ""
+            return f"fused_reduce_adam_cast{acc}[{gdt}]"
+        if kind in ("reduce_set", "reduce_acc"):
+            return f"{kind}[{gdt}]"
+        if kind == "adam":
+            return "adam_from_acc[f32]"
+        if kind == "gather_acc":
+            return "gather[f32]"
+        return "gather[bf16]"
+
+    def kernel_stats(self, steps):
+        """Per kind of launch: HIP-event times over the timed steps, the
+        algorithmic bytes of one launch and the rate they give; for the kinds
+        of the step, launches per step and the time per step they take."""
         out = {}
-        w = self.w
         for kind, evs in self.ev.items():
             if not evs:
                 continue
             ms = [a.elapsed_time(b) for a, b in evs]
             avg_s = sum(ms) / len(ms) / 1e3
-            if kind == "fused":
-                nbytes = self.bytes_fused
-            elif kind == "reduce":
-                if self.stage == 1:
-                    nb = [self.bytes_reduce_first]
-                elif self.split:
-                    nb = [self.bytes_reduce_first] + [self.bytes_reduce_acc] * (w.micro_batches - 1)
-                else:
-                    nb = [self.bytes_reduce_first] + [self.bytes_reduce_acc] * (w.micro_batches - 2)
-                nbytes = sum(nb) / len(nb)
-            elif kind == "adam":
-                nbytes = self.bytes_adam
-            elif kind == "gather_acc":
-                nbytes = self.bytes_gather_acc
-            else:
-                nbytes = sum(g[3] for g in self.gather_groups) / len(self.gather_groups)
+            nbytes = self.bytes_of(kind)
             gbps = nbytes / avg_s / 1e9
             srt = sorted(ms)
             med = (srt[(len(srt) - 1) // 2] + srt[len(srt) // 2]) / 2
             out[kind] = {"launches": len(ms), "avg_us": round(avg_s * 1e6, 2),
                          "median_us": round(med * 1e3, 2),
                          "min_us": round(min(ms) * 1e3, 2), "bytes_per_launch": int(nbytes),
-                         "GBps": round(gbps, 1), "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4)}
+                         "GBps": round(gbps, 1), "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
+                         "kernel": self.trace_name(kind)}
+            if kind in STEP_KINDS:
+                out[kind]["launches_per_step"] = round(len(ms) / steps, 3)
+                out[kind]["us_per_step"] = round(avg_s * 1e6 * len(ms) / steps, 2)
         return out
+
+
+def dominant_kind(ks):
+    """The kind of launch that takes the most time per step."""
+    kinds = [k for k in ks if k in STEP_KINDS]
+    return max(kinds, key=lambda k: ks[k]["us_per_step"])
 
 
 # ---------------------------------------------------------------------------
@@ -503,23 +537,35 @@ def software():
             "gpu": torch.cuda.get_device_name(0) if torch.cuda.is_available() else None}
 
 
-def cpu_baseline(runner, target_s):
-    """The oracle as it stands, timed on the host on a bounded sample of the
-    workload: one virtual rank's reduce over the N_d gradient buffers + Adam +
-    cast, plus a share of the parameter gathers. Measured twice for about
-    target_s each: on one thread, and on one thread per host core of the
-    process's CPU share (at most 16), each thread updating its own copy of a
-    rank's state (the ranks are independent; the oracle's C calls release
-    Python's lock)."""
-    import threading
+# Rank j's real elements in the oracle sample: parameters are taken from the
+# first one on until they reach this count (or the model ends).
+CPU_SAMPLE_ELEMS = 8 << 20
 
+
+def cpu_sample(runner, limit=CPU_SAMPLE_ELEMS):
+    """Host copies of one virtual rank's share of the workload: its slices of
+    the first parameters (together at least `limit` of its real elements, or
+    every parameter), cut from the device buffers on the device so that only
+    the sample crosses to the host. A prefix of the parameter list has the
+    same per-parameter layout (pad, shard length, offsets) on its own as
+    inside the whole list, so the oracle runs on that prefix as a model of
+    its own. Returns the prefix, the rank, its gradient chunks in shard
+    layout (the slice each rank sends to it), its state, and every rank's
+    working copy of the prefix (for the gathers; None if rank-local)."""
     import numpy as np
     import torch
     import oracle
 
-    w = runner.w
-    nd = w.n_d
-    torch.cuda.synchronize()
+    w, nd = runner.w, runner.w.n_d
+    L = oracle.Layout(w.numel, nd)
+    j = w.rank_local if w.rank_local >= 0 else 0
+    b, got = 0, 0
+    while b < L.T and (b == 0 or got < limit):
+        s = int(L.shard_len[b])
+        got += max(0, min(s, int(L.numel[b]) - j * s))
+        b += 1
+    sub = [int(n) for n in w.numel[:b]]
+    Ss = int(L.shard_off[b])           # the prefix's S: shard_off is a prefix sum
 
     def host(t):
         t = t.detach().cpu()
@@ -527,33 +573,56 @@ def cpu_baseline(runner, target_s):
             return t.view(torch.int16).numpy().view(np.uint16)
         return t.numpy()
 
-    S = runner.plan.S
-    grads = [host(g) for g in runner.grads]
-    all_work = host(runner.work) if w.rank_local < 0 else None
-    layout = oracle.GRADS_SHARD if w.rank_local >= 0 else oracle.GRADS_FULL
-    L = oracle.Layout(w.numel, nd)
+    torch.cuda.synchronize()
+    grads = []
+    for g in runner.grads:
+        if w.rank_local >= 0:
+            grads.append(host(g[:Ss]))
+        else:
+            parts = [g[int(L.full_off[t]) + j * int(L.shard_len[t]):
+                       int(L.full_off[t]) + (j + 1) * int(L.shard_len[t])] for t in range(b)]
+            grads.append(host(torch.cat(parts)))
+    base = 0 if w.rank_local >= 0 else j * L.S
+    state = [host(x[base:base + Ss]).copy() for x in (runner.master, runner.m, runner.v,
+                                                       runner.work)]
+    all_work = None
+    if w.rank_local < 0:
+        all_work = host(torch.cat([runner.work[r * L.S:r * L.S + Ss] for r in range(nd)]))
+    valid = int(sum(max(0, min(int(L.shard_len[t]), int(L.numel[t]) - j * int(L.shard_len[t])))
+                    for t in range(b)))
+    return sub, j, grads, state, all_work, valid
+
+
+def cpu_baseline(runner, target_s):
+    """The oracle as it stands, timed on the host on a bounded sample of the
+    workload (cpu_sample): one virtual rank's reduce over the N_d gradient
+    chunks + Adam + cast on its slices of the first parameters, plus the
+    gathers of those parameters. Measured twice for about target_s each: on
+    one thread, and on one thread per host core of the process's CPU share
+    (at most 16), each thread updating its own copy of the rank's state (the
+    oracle's C calls release Python's lock)."""
+    import threading
+
+    import torch
+    import oracle
+
+    w = runner.w
+    nd = w.n_d
+    sub, j, grads, state0, all_work, valid = cpu_sample(runner)
     gb = 2 if w.grad_dtype == torch.bfloat16 else 4
+    T = len(sub)
 
-    def rank_state(j):
-        base = 0 if w.rank_local >= 0 else j * S
-        return [host(x[base:base + S]).copy() for x in (runner.master, runner.m, runner.v,
-                                                         runner.work)]
-
-    def valid_of(j):
-        return int(sum(max(0, min(int(L.shard_len[t]), int(L.numel[t]) - j * int(L.shard_len[t])))
-                       for t in range(L.T)))
-
-    def worker(j, gather_ids, out):
-        master, m, v, work = rank_state(j)
-        fused_bytes = valid_of(j) * (nd * gb + 26)
-        gather_bytes = sum(int(L.numel[t]) * 4 for t in gather_ids)
+    def worker(gather_ids, out):
+        master, m, v, work = (x.copy() for x in state0)
+        fused_bytes = valid * (nd * gb + 26)
+        gather_bytes = sum(sub[t] * 4 for t in gather_ids)
         done, passes, t0 = 0, 0, time.perf_counter()
         while True:
-            red = oracle.reduce(w.numel, nd, j, grads, layout)
-            oracle.adam(w.numel, nd, j, master, m, v, work, red, w.lr, w.beta1, w.beta2, w.eps,
+            red = oracle.reduce(sub, nd, j, grads, oracle.GRADS_SHARD)
+            oracle.adam(sub, nd, j, master, m, v, work, red, w.lr, w.beta1, w.beta2, w.eps,
                         passes + 1)
             for t in gather_ids:
-                oracle.gather(w.numel, nd, t, all_work)
+                oracle.gather(sub, nd, t, all_work)
             done += fused_bytes + gather_bytes
             passes += 1
             el = time.perf_counter() - t0
@@ -562,11 +631,10 @@ def cpu_baseline(runner, target_s):
         out.append((done, passes))
 
     def run(threads):
-        ranks = [(w.rank_local if w.rank_local >= 0 else i % nd) for i in range(threads)]
-        gathers = [[t for t in range(L.T) if t % threads == i] if all_work is not None else []
+        gathers = [[t for t in range(T) if t % threads == i] if all_work is not None else []
                    for i in range(threads)]
         outs = [[] for _ in range(threads)]
-        ts = [threading.Thread(target=worker, args=(ranks[i], gathers[i], outs[i]))
+        ts = [threading.Thread(target=worker, args=(gathers[i], outs[i]))
               for i in range(threads)]
         t0 = time.perf_counter()
         for t in ts:
@@ -583,12 +651,11 @@ def cpu_baseline(runner, target_s):
         share = os.cpu_count() or 1
     threads = max(1, min(16, share))
     many, eln, pn = run(threads) if threads > 1 else (one, el1, p1)
-    what = (f"each thread: one virtual rank's reduce over {nd} gradient buffers + Adam + cast "
-            f"on its shard (rank-local: copies of rank {w.rank_local}'s)"
-            if w.rank_local >= 0 else
-            f"each thread: one virtual rank's reduce over {nd} gradient buffers + Adam + cast "
-            f"on its shard (thread i takes rank i mod {nd}, its own state copy), plus the "
-            f"gathers of its share of the {L.T} parameters")
+    what = (f"each thread: virtual rank {j}'s reduce over {nd} gradient chunks + Adam + cast "
+            f"on its own copy of rank {j}'s state, for parameters 0..{T - 1} of {len(w.numel)} "
+            f"({valid} of the rank's real elements)"
+            + ("" if all_work is None else
+               f", plus the gathers of its share of those {T} parameters"))
     return {"value": round(many, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "cpu_model": cpu_model(), "seconds": round(eln, 2),
             "sample": f"{what}; at least {pn} pass(es) per thread (C oracle, unchanged)",
@@ -694,9 +761,10 @@ def traffic_from(fetch_dir, write_dir, workload):
     print(json.dumps(out, indent=1))
 
 
-def load_traffic(workload):
-    """Measured HBM bytes per fused launch from the committed counter summary,
-    if it was taken on the current kernel source."""
+def load_traffic(workload, kernel):
+    """Measured HBM bytes per launch of `kernel` (its name in the rocprofv3
+    summaries) from the committed counter summary of `workload`, if it was
+    taken on the current kernel source; else None."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(path):
         return None
@@ -704,57 +772,19 @@ def load_traffic(workload):
         d = json.load(f)
     if d.get("kernel_source_hash") != kernel_source_hash():
         return None
-    return d.get("fused_bytes_per_launch")
+    k = d.get("kernels", {}).get(kernel)
+    return k["bytes_per_launch"] if k else None
 
 
 # ---------------------------------------------------------------------------
 
-def main():
-    args = parse()
-    if args.rocprof_summary:
-        rocprof_summary(args.rocprof_summary, args.summary_out)
-        return 0
-    if args.traffic_from:
-        traffic_from(args.traffic_from[0], args.traffic_from[1], args.workload)
-        return 0
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU: the library has no multi-GPU path "
-              f"(asked for --gpus {args.gpus}).", file=sys.stderr)
-        return 2
-
-    import __graft_entry__
-    __graft_entry__.ensure_built()
+def time_workload(w, args, device, evict, say):
+    """Build the workload's runner, run `warmup` untimed steps and time
+    `steps` steps. Returns the runner and the workload's figures."""
     import torch
-    from zero_sharded_mixed_pad_amd import synth
-
-    wl = synth.workloads()
-    if args.workload not in wl:
-        print(f"unknown workload {args.workload}; choose from {sorted(wl)}", file=sys.stderr)
-        return 2
-    w = wl[args.workload]
-    device = torch.device("cuda:0")
-    torch.cuda.set_device(device)
-    if args.prefetch:
-        res = prefetch_bench(args, device)
-        print(json.dumps({"mode": "prefetch", "steps": args.steps, "warmup": args.warmup,
-                          **res}), flush=True)
-        return 0
+    say(f"[bench] {w.name}: setting up")
     r = Runner(w, device, args.stage, args.split)
-    if args.checkpoint:
-        res = checkpoint_bench(r, args.checkpoint)
-        print(json.dumps({"mode": "checkpoint", "workload": w.name, "n_d": w.n_d, **res}),
-              flush=True)
-        return 0
     flush = args.flush == "on" or (args.flush == "auto" and r.bytes_fused < 2e9)
-    # Cache flush: a reduction that reads 1 GiB, four times the Infinity
-    # Cache, evicting the working set without leaving dirty lines behind (a
-    # flush that writes would make the timed kernel pay their write-back).
-    scratch = torch.ones(1 << 28, dtype=torch.float32, device=device)
-    sink = torch.empty((), dtype=torch.float32, device=device)
-
-    def evict():
-        torch.sum(scratch, dim=0, out=sink)
-
     for _ in range(args.warmup):
         if flush:
             evict()
@@ -782,7 +812,86 @@ def main():
     if not flush and any(g[3] < 1e9 for g in r.gather_groups):
         r.cold_gathers(evict, args.steps)
         torch.cuda.synchronize()
-    ks = r.kernel_stats()
+    ks = r.kernel_stats(args.steps)
+    dom = dominant_kind(ks)
+    fig = {"ms_per_step": round(ms_per_step, 4), "GBps": round(value, 1),
+           "frac_hbm_peak": round(value / HBM_PEAK_GBPS, 4), "bytes_per_step": int(step_bytes),
+           "wall_ms_per_step": round(wall * 1e3 / args.steps, 4), "cache_flush": bool(flush),
+           "dominant": dom, "kernels": ks}
+    say(f"[bench] {w.name}: {ms_per_step:.3f} ms/step, {value:.1f} GB/s; dominant {dom} "
+        f"{ks[dom]['GBps']} GB/s ({ks[dom]['frac_hbm_peak']})")
+    return r, fig
+
+
+def roofline(r, w, fig):
+    """Roofline object for the kind of launch that takes the most time per
+    step, with the whole step's fraction of peak beside it."""
+    ks, dom = fig["kernels"], fig["dominant"]
+    k = ks[dom]
+    name = r.trace_name(dom)
+    roof = {"bound": "hbm", "achieved": k["GBps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(k["GBps"] / HBM_PEAK_GBPS, 4),
+            "traffic": load_traffic(w.name, name),
+            "kernel": name, "kind": dom,
+            "launches_per_step": k["launches_per_step"],
+            "bytes_per_launch": k["bytes_per_launch"], "avg_launch_us": k["avg_us"],
+            "step_frac": fig["frac_hbm_peak"]}
+    # counter-measured HBM bytes (FETCH_SIZE + WRITE_SIZE) over the same launch time
+    roof["traffic_GBps"] = (round(roof["traffic"] / k["avg_us"] / 1e3, 1)
+                            if roof["traffic"] and k["avg_us"] else None)
+    return roof
+
+
+def main():
+    args = parse()
+    if args.rocprof_summary:
+        rocprof_summary(args.rocprof_summary, args.summary_out)
+        return 0
+    if args.traffic_from:
+        traffic_from(args.traffic_from[0], args.traffic_from[1], args.workload)
+        return 0
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU: the library has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}).", file=sys.stderr)
+        return 2
+
+    import __graft_entry__
+    __graft_entry__.ensure_built()
+    import torch
+    from zero_sharded_mixed_pad_amd import synth
+
+    def say(msg):
+        print(msg, file=sys.stderr, flush=True)
+
+    wl = synth.workloads()
+    if args.workload not in wl:
+        print(f"unknown workload {args.workload}; choose from {sorted(wl)}", file=sys.stderr)
+        return 2
+    w = wl[args.workload]
+    device = torch.device("cuda:0")
+    torch.cuda.set_device(device)
+    if args.prefetch:
+        res = prefetch_bench(args, device)
+        print(json.dumps({"mode": "prefetch", "steps": args.steps, "warmup": args.warmup,
+                          **res}), flush=True)
+        return 0
+    if args.checkpoint:
+        r = Runner(w, device, args.stage, args.split)
+        res = checkpoint_bench(r, args.checkpoint)
+        print(json.dumps({"mode": "checkpoint", "workload": w.name, "n_d": w.n_d, **res}),
+              flush=True)
+        return 0
+    # Cache flush: a reduction that reads 1 GiB, four times the Infinity
+    # Cache, evicting the working set without leaving dirty lines behind (a
+    # flush that writes would make the timed kernel pay their write-back).
+    scratch = torch.ones(1 << 28, dtype=torch.float32, device=device)
+    sink = torch.empty((), dtype=torch.float32, device=device)
+
+    def evict():
+        torch.sum(scratch, dim=0, out=sink)
+
+    r, fig = time_workload(w, args, device, evict, say)
+    roof = roofline(r, w, fig)
 
     if args.calibrate_copy:
         src = torch.empty(1 << 30, dtype=torch.bfloat16, device=device)
@@ -791,41 +900,49 @@ def main():
         for _ in range(3):
             dst.copy_(src)
         torch.cuda.synchronize()
+        del src, dst
 
-    # the dominant kernel: the fused step, or (stage 1) the unfused reduce
-    dom = "fused" if "fused" in ks else "reduce"
-    fused = ks[dom]
-    roof = {"bound": "hbm", "achieved": fused["GBps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-            "frac": round(fused["GBps"] / HBM_PEAK_GBPS, 4),
-            "traffic": load_traffic(w.name) if dom == "fused" else None,
-            "kernel": ("fused reduce+Adam+cast (all ranks, one launch)" if dom == "fused"
-                       else "shard reduce (all ranks, one launch)"),
-            "bytes_per_launch": fused["bytes_per_launch"], "avg_launch_us": fused["avg_us"]}
-    # counter-measured HBM bytes (FETCH_SIZE + WRITE_SIZE) over the same launch time
-    roof["traffic_GBps"] = (round(roof["traffic"] / fused["avg_us"] / 1e3, 1)
-                            if roof["traffic"] and fused["avg_us"] else None)
     cpu = None
     if not args.no_cpu_baseline:
+        say("[bench] CPU oracle baseline")
         cpu = cpu_baseline(r, args.cpu_seconds)
-        cpu["value_vs_gpu_ratio"] = round(value / cpu["value"], 1) if cpu["value"] else None
+        cpu["value_vs_gpu_ratio"] = round(fig["GBps"] / cpu["value"], 1) if cpu["value"] else None
 
     gdt = "bf16" if w.grad_dtype == torch.bfloat16 else "f32"
     pdt = "bf16" if w.param_dtype == torch.bfloat16 else "f32"
+    config = {"workload": w.name, "n_d": w.n_d, "params": len(w.numel),
+              "elements": sum(w.numel), "param_dtype": pdt, "grad_dtype": gdt,
+              "state": "fp32 master, m, v + bf16 working copy",
+              "micro_batches": w.micro_batches,
+              "rank_local": w.rank_local if w.rank_local >= 0 else None,
+              "zero_stage": args.stage,
+              "gathers_per_step": (2 if args.stage == 3 else 1) * len(r.gather_groups),
+              "bytes_per_step": fig["bytes_per_step"], "cache_flush": fig["cache_flush"],
+              "wall_ms_per_step": fig["wall_ms_per_step"]}
+    ks = fig["kernels"]
+    del r
+    torch.cuda.empty_cache()
+
+    # The other workloads, each timed the same way (per-kernel figures only).
+    workloads = {w.name: {k: v for k, v in fig.items()}}
+    if args.all_workloads:
+        for name, ow in wl.items():
+            if name == w.name:
+                continue
+            ro, ofig = time_workload(ow, args, device, evict, say)
+            ofig["roofline_frac"] = round(ofig["kernels"][ofig["dominant"]]["frac_hbm_peak"], 4)
+            workloads[name] = ofig
+            del ro
+            torch.cuda.empty_cache()
+    workloads[w.name]["roofline_frac"] = roof["frac"]
+
     line = {
-        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "metric": METRIC, "value": fig["GBps"], "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": fig["ms_per_step"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic (seeded normal gradients and parameters, resident in HBM)",
-        "config": {"workload": w.name, "n_d": w.n_d, "params": len(w.numel),
-                   "elements": sum(w.numel), "param_dtype": pdt, "grad_dtype": gdt,
-                   "state": "fp32 master, m, v + bf16 working copy",
-                   "micro_batches": w.micro_batches,
-                   "rank_local": w.rank_local if w.rank_local >= 0 else None,
-                   "zero_stage": args.stage,
-                   "gathers_per_step": (2 if args.stage == 3 else 1) * len(r.gather_groups),
-                   "bytes_per_step": int(step_bytes), "cache_flush": bool(flush),
-                   "wall_ms_per_step": round(wall * 1e3 / args.steps, 4)},
-        "roofline": roof, "cpu_baseline": cpu, "kernels": ks,
+        "config": config, "roofline": roof, "cpu_baseline": cpu, "kernels": ks,
+        "workloads": workloads,
         "kernel_source_hash": kernel_source_hash(), "software": software(),
     }
     print(json.dumps(line), flush=True)

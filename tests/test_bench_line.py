@@ -27,7 +27,7 @@ def test_more_than_one_gpu_is_refused():
 def test_json_line_is_consistent():
     print("[bench] fp32 1000x1003, 3 steps, 1 s of oracle", flush=True)
     res = run_bench("--workload", "fp32_1000x1003_nd4", "--steps", "3", "--warmup", "1",
-                    "--cpu-seconds", "1")
+                    "--cpu-seconds", "1", "--only")
     assert res.returncode == 0, res.stderr.decode()[-2000:]
     lines = [l for l in res.stdout.decode().splitlines() if l.strip()]
     assert len(lines) == 1, lines
@@ -53,6 +53,12 @@ def test_json_line_is_consistent():
             roof["traffic"] / roof["avg_launch_us"] / 1e3, rel=2e-3)
     fused = d["kernels"]["fused"]
     assert fused["launches"] == 3 and fused["min_us"] <= fused["median_us"]
+    # the roofline names the kind of launch with the most time per step
+    ks = d["kernels"]
+    step_kinds = [k for k in ks if "us_per_step" in ks[k]]
+    assert roof["kind"] == max(step_kinds, key=lambda k: ks[k]["us_per_step"])
+    assert roof["step_frac"] == pytest.approx(d["value"] / roof["peak"], abs=2e-4)
+    assert list(d["workloads"]) == ["fp32_1000x1003_nd4"]
     cpu = d["cpu_baseline"]
     assert cpu["kind"] == "oracle" and cpu["unit"] == "GB/s" and cpu["value"] > 0
     assert cpu["cores"] >= 1 and cpu["single_core"]["cores"] == 1
