@@ -190,7 +190,8 @@ class Runner:
                 out = torch.empty(cnt, dtype=bf16, device=device)
                 self.gather_groups.append((first, n, out, cnt * 4))
         self.step_no = 0
-        self.ev = {k: [] for k in STEP_KINDS + ("gather_cold",)}
+        self.ev = {k: [] for k in STEP_KINDS + ("gather_cold", "gather_list",
+                                                 "gather_list_cold")}
 
     def _event(self):
         return self.torch.cuda.Event(enable_timing=True)
@@ -212,11 +213,11 @@ class Runner:
         if self.stage == 1:
             self._timed("reduce_set", lambda: p.reduce_shard(
                 self.rank, self.grads, layout=self.layout, accumulate=False), record)
-            self._timed("gather_acc", lambda: p.gather_many(
+            self._timed("gather_acc", lambda: p.gather_range(
                 0, len(w.numel), self.grad_replica, "acc"), record)
             self._timed("adam", lambda: p.adam_step(self.rank, **hp), record)
             for first, n, out, _b in self.gather_groups:
-                self._timed("gather", lambda first=first, n=n, out=out: p.gather_many(
+                self._timed("gather", lambda first=first, n=n, out=out: p.gather_range(
                     first, n, out, "work"), record)
             return
         if self.split:  # unfused: reduce into the accumulator, then Adam from it
@@ -237,7 +238,7 @@ class Runner:
         # after the update
         for _ in range(2 if self.stage == 3 else 1):
             for first, n, out, _b in self.gather_groups:
-                self._timed("gather", lambda first=first, n=n, out=out: p.gather_many(
+                self._timed("gather", lambda first=first, n=n, out=out: p.gather_range(
                     first, n, out, "work"), record)
 
     def cold_gathers(self, flush, reps):
@@ -248,7 +249,24 @@ class Runner:
             for first, n, out, _b in self.gather_groups:
                 flush()
                 self._timed("gather_cold", lambda first=first, n=n, out=out:
-                            self.plan.gather_many(first, n, out, "work"), True)
+                            self.plan.gather_range(first, n, out, "work"), True)
+
+    def list_gathers(self, flush, reps):
+        """Every parameter at once through the list form (zsp_gather_many),
+        each into its own output, `reps` times; after `flush` when it is
+        given (then recorded as gather_list_cold, beside the range form's
+        gather_cold), else back to back (gather_list)."""
+        torch = self.torch
+        if not hasattr(self, "glist"):
+            outs = [torch.empty(max(n, 1), dtype=torch.bfloat16, device=self.dev)
+                    for n in self.w.numel]
+            # marshalled once: the timed calls are the library's alone
+            self.glist = self.plan.gather_list(list(range(len(self.w.numel))), outs, "work")
+        kind = "gather_list_cold" if flush else "gather_list"
+        for _ in range(reps):
+            if flush:
+                flush()
+            self._timed(kind, lambda: self.plan.gather_prepared(self.glist), True)
 
     def step_bytes(self):
         w = self.w
@@ -277,6 +295,8 @@ class Runner:
             return self.bytes_adam
         if kind == "gather_acc":
             return self.bytes_gather_acc
+        if kind.startswith("gather_list"):
+            return sum(g[3] for g in self.gather_groups)
         return sum(g[3] for g in self.gather_groups) / len(self.gather_groups)
 
     def trace_name(self, kind):
@@ -291,6 +311,9 @@ class Runner:
             return "adam_from_acc[f32]"
         if kind == "gather_acc":
             return "gather[f32]"
+        if kind.startswith("gather_list"):
+            staged = sum(1 for n in self.w.numel if n > 0) > 64
+            return f"gather_list_{'recs' if staged else 'args'}[bf16]"
         return "gather[bf16]"
 
     def kernel_stats(self, steps):
@@ -376,8 +399,8 @@ def checkpoint_bench(r, parent):
             ok = True
             for first, n, buf, _b in r.gather_groups:
                 a = torch.empty_like(buf)
-                r.plan.gather_many(first, n, a, "work")
-                p2.gather_many(first, n, buf, "work")
+                r.plan.gather_range(first, n, a, "work")
+                p2.gather_range(first, n, buf, "work")
                 ok = ok and torch.equal(a.view(torch.int16), buf.view(torch.int16))
             for src in ("master",):
                 for t_ in range(len(w.numel)):
@@ -439,7 +462,7 @@ def prefetch_bench(args, device):
     layer_elems = sum(w.numel[:9])
     cs, gs = torch.cuda.Stream(), torch.cuda.Stream()
     fixed = torch.empty(layer_elems, dtype=torch.bfloat16, device=device)
-    plan.gather_many(0, 9, fixed, "work")
+    plan.gather_range(0, 9, fixed, "work")
     fixed_views, k = [], 0
     for t in range(9):
         fixed_views.append(fixed[k:k + w.numel[t]])
@@ -680,6 +703,12 @@ def _short(name):
         return f"{_OPS[int(m.group(1))]}[{dt}]"
     if "gather_kernel" in name:
         return "gather[f32]" if ("IfE" in name or "<float>" in name) else "gather[bf16]"
+    m = re.search(r"gather_list_(args|recs)", name)
+    if m:
+        dt = "f32" if ("IfLb" in name or "<float," in name) else "bf16"
+        return f"gather_list_{m.group(1)}[{dt}]"
+    if "list_expand_kernel" in name:
+        return "gather_list_expand"
     name = re.sub(r"^void ", "", name)
     return name[:48]
 
@@ -811,6 +840,10 @@ def time_workload(w, args, device, evict, say):
     value = step_bytes / (ms_per_step / 1e3) / 1e9
     if not flush and any(g[3] < 1e9 for g in r.gather_groups):
         r.cold_gathers(evict, args.steps)
+        torch.cuda.synchronize()
+    if r.gather_groups and args.stage == 3:
+        cold = sum(g[3] for g in r.gather_groups) < 1e9
+        r.list_gathers(evict if cold else None, args.steps)
         torch.cuda.synchronize()
     ks = r.kernel_stats(args.steps)
     dom = dominant_kind(ks)

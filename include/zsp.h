@@ -34,15 +34,18 @@
  *   The caller allocates and owns every device buffer (parameters, gradients,
  *   optimizer state, accumulator, gather outputs, schedule arenas). A plan
  *   owns its host tables, the device copies of its offset tables (allocated
- *   in zsp_bind_state) and, from its first checkpoint save or load, the
- *   checkpoint staging (pinned host chunks, streams, events); zsp_destroy
- *   frees them. The hot-path calls (reduce, Adam, gather, schedule acquire
- *   and release) allocate nothing; checkpoint calls also use host memory
- *   for their own duration. The reduce, Adam and gather calls only check
- *   arguments and launch kernels (no host wait, no memset), so they can be
- *   captured into a HIP graph; Adam's scalars (lr, betas, eps and the step's
- *   bias corrections) are kernel arguments, so a replay repeats the step it
- *   was captured with.
+ *   in zsp_bind_state), the staging slots of long zsp_gather_many lists
+ *   (allocated when such a list first needs them) and, from its first
+ *   checkpoint save or load, the checkpoint staging (pinned host chunks,
+ *   streams, events); zsp_destroy frees them. The other hot-path calls
+ *   (reduce, Adam, the range and single gathers, schedule acquire and
+ *   release) allocate nothing; checkpoint calls also use host memory for
+ *   their own duration. The reduce, Adam, range and single gather calls,
+ *   and zsp_gather_many on lists of at most 64 parameters, only check
+ *   arguments and launch kernels (no host wait, no copy, no memset), so they
+ *   can be captured into a HIP graph; Adam's scalars (lr, betas, eps and the
+ *   step's bias corrections) are kernel arguments, so a replay repeats the
+ *   step it was captured with.
  *   Every device pointer must be 16-byte aligned (torch allocations are).
  *   State arrays bound for all ranks hold nd*S elements, rank r at
  *   [r*S, (r+1)*S); bound for one rank j they hold that rank's S elements.
@@ -62,10 +65,11 @@
  *
  * Threads
  *   The reduce, Adam and gather calls (whole-model and _params forms) and
- *   zsp_load_params only read the plan: several threads may issue them on
- *   one plan at once, e.g. one thread per rank, each on its own stream (work
- *   that writes the same state at the same time is the caller's race, as
- *   for any two kernels). zsp_bind_state, the checkpoint calls and
+ *   zsp_load_params only read the plan (zsp_gather_many takes the plan's
+ *   staging slots under a lock of their own): several threads may issue
+ *   them on one plan at once, e.g. one thread per rank, each on its own
+ *   stream (work that writes the same state at the same time is the
+ *   caller's race, as for any two kernels). zsp_bind_state, the checkpoint calls and
  *   zsp_destroy change the plan and must not overlap any other call on it.
  *   A schedule's calls must not overlap one another; other schedules and
  *   the read-only calls above may run beside them. Different plans are
@@ -142,12 +146,11 @@ zsp_status zsp_plan_tensor(const zsp_plan* plan, int32_t t, int64_t* numel, int6
  *     name rank j, and gathers are not possible (ZSP_ESTATE).
  *   master, m, v: fp32; work: bf16 bit patterns; grad_acc: fp32 accumulator
  *     or NULL (then accumulate/use_acc calls fail with ZSP_ESTATE).
- * Allocates the device tables (setup path; the only device allocation the
- * library makes): 40 bytes per bound piece (one rank's slice of one
- * parameter) and 4 bytes per 512 elements of the bound state; an all-rank
- * binding adds the gather's 16 bytes per piece and 36 bytes per 512
- * elements of the unpadded parameters. Rebinding replaces the previous
- * binding. */
+ * Allocates the device tables (setup path): 40 bytes per bound piece (one
+ * rank's slice of one parameter) and 4 bytes per 512 elements of the bound
+ * state; an all-rank binding adds the gather's 16 bytes per piece, 36 bytes
+ * per 512 elements of the unpadded parameters and 32 bytes per parameter.
+ * Rebinding replaces the previous binding. */
 zsp_status zsp_bind_state(zsp_plan* plan, int32_t rank_or_all, float* master, float* m,
                           float* v, uint16_t* work, float* grad_acc);
 
@@ -235,12 +238,41 @@ zsp_status zsp_reduce_adam_step_params(zsp_plan* plan, int32_t rank_or_all, int3
 zsp_status zsp_gather(zsp_plan* plan, int32_t param_id, zsp_source src, void* out,
                       void* stream);
 
-/* Batched gather of the consecutive parameters [first_param,
- * first_param + n_params) in one launch, e.g. every parameter of one layer.
- * `out` receives them back to back, unpadded: parameter t at
- * flat_off[t] - flat_off[first_param]. */
-zsp_status zsp_gather_many(zsp_plan* plan, int32_t first_param, int32_t n_params,
-                           zsp_source src, void* out, void* stream);
+/* Gather of the consecutive parameters [first_param, first_param +
+ * n_params) -- one layer's worth, e.g. -- in one launch ([ZD] section 3:
+ * each layer's parameters are all-gathered just before it runs). `out`
+ * receives them back to back, unpadded: parameter t at flat_off[t] -
+ * flat_off[first_param]. ZSP_ERANGE if the range is empty or outside
+ * [0, n_params). The per-layer schedule below uses this gather. */
+zsp_status zsp_gather_range(zsp_plan* plan, int32_t first_param, int32_t n_params,
+                            zsp_source src, void* out, void* stream);
+
+/* gather(param_id) for a list of parameters: ids[0..n) in any order
+ * (repeats allowed), parameter ids[i] into its own output outs[i]
+ * (numel[ids[i]] elements, unpadded, as zsp_gather writes them). This is
+ * the all-gather of a bucket of parameters, e.g. the module about to run
+ * ([ZD] section 3: a module's full parameters are gathered just before its
+ * forward and again before its backward; section 8: gathers go out in
+ * buckets of parameters). ids and outs are host arrays, read during the
+ * call; every outs[i] of a non-empty parameter must be a 16-byte aligned
+ * device pointer (NULL is allowed for empty ones); outputs must not
+ * overlap one another or the bound state. n = 0 does nothing.
+ *   Lists of at most 64 non-empty parameters: one launch, nothing staged.
+ *   Longer lists: their entries (16 bytes per parameter plus 4 bytes per
+ *   32768 output elements) are copied to the device through one of four
+ *   staging slots the plan keeps, then two launches. A slot is allocated
+ *   (pinned host and device memory) the first time a list needs more room
+ *   than it has -- the only allocation of any gather call -- and is refilled
+ *   only after the gathers of its previous use have run: the call waits on
+ *   the host when four staged gathers are still in flight. Each slot holds
+ *   the records of at most 2^19 tiles of 512 elements (16 MiB); longer
+ *   lists go in several pairs of launches.
+ * Errors: ZSP_ERANGE for an id outside [0, n_params) or a list of 2^31
+ * tiles or more; ZSP_EINVAL for NULL arrays with n > 0, a NULL or
+ * misaligned output, or n < 0; ZSP_ESTATE without an all-rank binding;
+ * ZSP_ENOMEM if a staging slot cannot grow. Needs an all-rank binding. */
+zsp_status zsp_gather_many(zsp_plan* plan, const int32_t* ids, int32_t n, zsp_source src,
+                           void* const* outs, void* stream);
 
 /* ---- Per-layer gather schedule with prefetch ------------------------------
  * [ZS3] on-demand fetch list (gather layer l before its computation, discard
@@ -264,7 +296,7 @@ zsp_status zsp_gather_many(zsp_plan* plan, int32_t first_param, int32_t n_params
  * n_steps - 1 act as n_steps - 1). *arena_bytes receives the device bytes
  * zsp_sched_bind needs: (D+1) slots, each the largest group's gathered size
  * (2 B per element for ZSP_SRC_WORK, 4 for ZSP_SRC_MASTER) rounded up to
- * 256 B. Every gather is zsp_gather_many's kernel. */
+ * 256 B. Every gather is zsp_gather_range's kernel. */
 zsp_status zsp_sched_create(zsp_plan* plan, int32_t n_groups, const int32_t* group_first,
                             const int32_t* group_count, int32_t n_steps, const int32_t* order,
                             int32_t depth, zsp_source src, int64_t* arena_bytes,

@@ -2,8 +2,9 @@
  * capi_demo.c -- the library driven from plain C99 through include/zsp.h
  * alone: no Python, no torch. Device memory comes from the HIP runtime's C
  * API. A small padded parameter list at N_d = 5 goes through partition, copy-in,
- * three fused reduce + Adam + cast steps over every virtual rank, and a
- * gather of every parameter; each result is compared bit for bit with the
+ * three fused reduce + Adam + cast steps over every virtual rank, a gather
+ * of every parameter into one buffer and list gathers into separate
+ * outputs; each result is compared bit for bit with the
  * CPU oracle (test infrastructure, linked only into this test program).
  * A few argument errors are checked too. Prints "capi demo ok ..." and
  * exits 0, or names the first difference and exits 1. With --host-only it
@@ -26,6 +27,7 @@
 #define ND 5
 #define T 6
 #define STEPS 3
+#define LIST_N (T + 70)
 
 static const int64_t NUMEL[T] = {1003, 64, 5, 0, 3 * 4096 + 1, 4096 * 4 + 7};
 
@@ -165,7 +167,20 @@ static int run(int host_only) {
                 return 1;
         }
     }
-    ZCK(zsp_gather_many(P, 0, T, ZSP_SRC_WORK, d_out, NULL));
+    ZCK(zsp_gather_range(P, 0, T, ZSP_SRC_WORK, d_out, NULL));
+    /* The list form: every parameter in reverse order (kernel-argument
+     * form), then 70 entries cycling through them (staged form), each into
+     * an output of its own; empty parameters take NULL. */
+    int32_t ids[LIST_N];
+    void* d_lists[LIST_N];
+    for (int i = 0; i < LIST_N; ++i) {
+        ids[i] = i < T ? T - 1 - i : (int32_t)((7 * i) % T);
+        d_lists[i] = NULL;
+        if (NUMEL[ids[i]] > 0)
+            HIPCK(hipMalloc(&d_lists[i], sizeof(uint16_t) * (size_t)NUMEL[ids[i]]));
+    }
+    ZCK(zsp_gather_many(P, ids, T, ZSP_SRC_WORK, d_lists, NULL));
+    ZCK(zsp_gather_many(P, ids + T, LIST_N - T, ZSP_SRC_WORK, d_lists + T, NULL));
     HIPCK(hipDeviceSynchronize());
     HIPCK(hipMemcpy(h_master, d_master, sizeof(float) * n_state, hipMemcpyDeviceToHost));
     HIPCK(hipMemcpy(h_m, d_m, sizeof(float) * n_state, hipMemcpyDeviceToHost));
@@ -180,6 +195,15 @@ static int run(int host_only) {
                     same(h_v, o_v, sizeof(float) * n_state, "v") +
                     same(h_work, o_work, sizeof(uint16_t) * n_state, "work") +
                     same(gathered, o_gathered, sizeof(uint16_t) * numel, "gather");
+    for (int i = 0; i < LIST_N; ++i) {
+        const int t = ids[i];
+        if (!d_lists[i]) continue;
+        HIPCK(hipMemcpy(gathered, d_lists[i], sizeof(uint16_t) * (size_t)NUMEL[t],
+                        hipMemcpyDeviceToHost));
+        bad_count += same(gathered, o_gathered + o_flat[t], sizeof(uint16_t) * (size_t)NUMEL[t],
+                          i < T ? "list gather (arguments)" : "list gather (staged)");
+        hipFree(d_lists[i]);
+    }
     zsp_destroy(P);
     hipFree(d_master);
     hipFree(d_m);
@@ -195,8 +219,8 @@ static int run(int host_only) {
     free(o_master); free(o_m); free(o_v); free(o_work); free(o_red);
     free(params); free(gathered); free(o_gathered);
     if (bad_count) return 1;
-    printf("capi demo ok: %d parameters, N_d = %d, S = %lld, %d fused steps + gather, "
-           "bit-exact\n", T, ND, (long long)S, STEPS);
+    printf("capi demo ok: %d parameters, N_d = %d, S = %lld, %d fused steps + range and "
+           "list gathers, bit-exact\n", T, ND, (long long)S, STEPS);
     return 0;
 }
 

@@ -119,8 +119,11 @@ def test_unbound_calls_fail_before_touching_a_device():
                                     1, null) == binding.ESTATE
     assert lib.zsp_gather(h, 0, binding.SRC_WORK, ctypes.c_void_p(256), null) == binding.ESTATE
     assert lib.zsp_gather(h, 9, binding.SRC_WORK, ctypes.c_void_p(256), null) == binding.ERANGE
-    assert lib.zsp_gather_many(h, 0, 1, binding.SRC_WORK, ctypes.c_void_p(256),
-                               null) == binding.ESTATE
+    assert lib.zsp_gather_range(h, 0, 1, binding.SRC_WORK, ctypes.c_void_p(256),
+                                null) == binding.ESTATE
+    ids = (ctypes.c_int32 * 2)(1, 0)
+    outs = (ctypes.c_void_p * 2)(256, 512)
+    assert lib.zsp_gather_many(h, ids, 2, binding.SRC_WORK, outs, null) == binding.ESTATE
     assert "bind" in zsp.last_error()
     assert lib.zsp_reduce_shard(None, -1, grads, 1, 0, 0, null) == binding.EINVAL
     plan.destroy()

@@ -84,7 +84,7 @@ def test_load_reshards(tmp_path, nd_old, nd_new):
         assert_bits(g, w, f"resharded {nd_old}->{nd_new}: {name}")
     # the resharded state gathers back to the same parameters
     out = torch.empty(B.L.total_numel, dtype=torch.float32, device="cuda")
-    B.plan.gather_many(0, len(NUMELS), out, "master")
+    B.plan.gather_range(0, len(NUMELS), out, "master")
     torch.cuda.synchronize()
     assert_bits(np_of(out), regathered(old[0]), "gather after reshard")
 

@@ -1,6 +1,6 @@
 """The hot-path calls under HIP graph capture: no allocation, no host
 synchronisation and no memset node inside zsp_reduce_adam_step,
-zsp_reduce_shard, zsp_adam_step or zsp_gather_many, so a caller can capture
+zsp_reduce_shard, zsp_adam_step or zsp_gather_range, so a caller can capture
 one step and replay it. Captured once, replayed three times with eager work
 and host synchronisations between the replays; after every replay the state
 and the gathered parameters equal those of the same calls made eagerly on a
@@ -31,7 +31,7 @@ def test_capture_and_replay_matches_eager(numels, nd):
         M.plan.reduce_shard(zsp.ALL_RANKS, grads, accumulate=False, stream=stream)
         M.plan.adam_step(zsp.ALL_RANKS, step=3, stream=stream, **HP)
         M.plan.reduce_adam_step(zsp.ALL_RANKS, grads, step=4, use_acc=True, stream=stream, **HP)
-        M.plan.gather_many(0, T, out[:A.L.total_numel], "work", stream=stream)
+        M.plan.gather_range(0, T, out[:A.L.total_numel], "work", stream=stream)
 
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())

@@ -194,13 +194,13 @@ def test_gather_roundtrip_and_oracle(numels, nd):
         L = M.L
         allw = torch.empty(max(L.total_numel, 8), dtype=torch.bfloat16, device=d)
         allm = torch.empty(max(L.total_numel, 8), dtype=torch.float32, device=d)
-        M.plan.gather_many(0, L.T, allw, "work")
-        M.plan.gather_many(0, L.T, allm, "master")
+        M.plan.gather_range(0, L.T, allw, "work")
+        M.plan.gather_range(0, L.T, allm, "master")
         torch.cuda.synchronize()
         flat32 = M.flat.float()
         assert torch.equal(allm[:L.total_numel].cpu(), flat32), "gather(partition(x)) != x"
         want_w = np.concatenate([oracle.gather(numels, nd, t, M.o_work) for t in range(L.T)])
-        assert_bits(np_of(allw[:L.total_numel]), want_w, "gather_many/work")
+        assert_bits(np_of(allw[:L.total_numel]), want_w, "gather_range/work")
         # single-tensor gathers into fresh buffers
         for t in range(L.T):
             nt = int(L.numel[t])
@@ -221,7 +221,7 @@ SUBRANGE_LAYOUTS = {
 
 
 @pytest.mark.parametrize("which", list(SUBRANGE_LAYOUTS))
-def test_gather_many_subranges(which):
+def test_gather_range_subranges(which):
     numels, nd = SUBRANGE_LAYOUTS[which]
     M = Mirror(numels, nd)
     L = M.L
@@ -234,10 +234,10 @@ def test_gather_many_subranges(which):
     for a, b in ranges:
         cnt = int(L.flat_off[b] - L.flat_off[a])
         out = torch.empty(max(cnt, 8), dtype=torch.bfloat16, device=d)
-        M.plan.gather_many(a, b - a, out, "work")
+        M.plan.gather_range(a, b - a, out, "work")
         torch.cuda.synchronize()
         want = np.concatenate([oracle.gather(numels, nd, t, M.o_work) for t in range(a, b)])
-        assert_bits(np_of(out[:cnt]), want, f"gather_many[{a},{b})")
+        assert_bits(np_of(out[:cnt]), want, f"gather_range[{a},{b})")
 
 
 @pytest.mark.parametrize("numels,nd", CASES)
@@ -369,7 +369,54 @@ def test_special_values():
     M.plan.reduce_adam_step(zsp.ALL_RANKS, [g.to(dev()) for g in grads], step=1, **HP)
     for j in M.ranks:
         M.o_adam(j, M.o_reduce(j, grads), 1)
-    M.check_state("special values")
+    assert M.check_state("special values") == 0
+    # NaN results of the arithmetic: positions are compared above; report
+    # how their bit patterns compare
+    got = np_of(M.g_master[:M.n]).view(np.uint32)
+    want = M.o_master.view(np.uint32)
+    nan = np.isnan(M.o_master)
+    pairs = sorted(set(zip(got[nan].tolist(), want[nan].tolist())))
+    print(f"[special values] {int(nan.sum())} NaN results; (gpu, oracle) bit pairs: "
+          f"{[(hex(a), hex(b)) for a, b in pairs[:8]]}", flush=True)
+
+
+# fp32 bit patterns of every kind of special value: NaNs (quiet and
+# signalling, both signs, payload bits high and low), infinities, signed
+# zeros, subnormals, rounding ties to both sides, the largest finite values
+# and values that round up to infinity.
+SPECIAL_F32 = np.array([
+    0x7fc00000, 0xffc00000, 0x7f800001, 0xff800001, 0x7fa00000, 0x7fc12345, 0xffe54321,
+    0x7fbfffff, 0xffffffff, 0x7ff0000f, 0x7f800000, 0xff800000, 0x00000000, 0x80000000,
+    0x00000001, 0x807fffff, 0x00008000, 0x00018000, 0x3f808000, 0x3f818000, 0x3f80ffff,
+    0x7f7fffff, 0xff7fffff, 0x7f7f8000, 0x7f7f7fff, 0x3f7fffff, 0x33800000, 0x00400000,
+    0x3f800000, 0xbf800000], np.uint32)
+
+
+def test_copyin_cast_special_values():
+    """fp32 parameters holding the special values above go through the
+    copy-in: the master keeps their bits and the bf16 working copy equals the
+    oracle's cast bit for bit, NaN payloads and signs included (the cast
+    keeps a NaN's sign and leading payload bits and sets its quiet bit)."""
+    numels, nd = [SPECIAL_F32.size * 37 + 3, 11], 4
+    total = sum(numels)
+    flat = np.resize(SPECIAL_F32, total).astype(np.uint32).view(np.float32)
+    o_master, o_work, _m, _v = oracle.partition(numels, nd, flat)
+    plan = zsp.partition(numels, nd)
+    d = dev()
+    n = nd * plan.S
+    st = [torch.empty(n, dtype=torch.float32, device=d) for _ in range(3)]
+    st.append(torch.empty(n, dtype=torch.bfloat16, device=d))
+    plan.bind_state(zsp.ALL_RANKS, *st)
+    plan.load_params(torch.from_numpy(flat.copy()).to(d))
+    torch.cuda.synchronize()
+    assert_bits(np_of(st[0]), o_master, "copy-in master (special values)")
+    assert_bits(np_of(st[3]), o_work, "copy-in work (special values)")
+    # and back through the fp32 gather: every bit pattern comes back
+    out = torch.empty(total, dtype=torch.float32, device=d)
+    plan.gather_range(0, len(numels), out, "master")
+    torch.cuda.synchronize()
+    assert_bits(np_of(out), flat.copy(), "gather of special values")
+    plan.destroy()
 
 
 def test_gpu_argument_errors():
@@ -390,7 +437,7 @@ def test_gpu_argument_errors():
     with pytest.raises(ValueError):
         M.plan.reduce_adam_step(zsp.ALL_RANKS, grads[:3], step=1, **HP)
     with pytest.raises(zsp.ZspError) as e:
-        M.plan.gather_many(1, 2, torch.empty(2000, dtype=torch.bfloat16, device=d))
+        M.plan.gather_range(1, 2, torch.empty(2000, dtype=torch.bfloat16, device=d))
     assert e.value.status == zsp.binding.ERANGE
     N = Mirror(numels, nd, with_acc=False)
     with pytest.raises(zsp.ZspError) as e:
@@ -420,7 +467,7 @@ def test_all_empty_plan(tmp_path):
     plan.reduce_shard(zsp.ALL_RANKS, grads, accumulate=True)
     plan.adam_step(zsp.ALL_RANKS, step=2, **HP)
     out = torch.full((8,), 3.0, dtype=torch.bfloat16, device=d)
-    plan.gather_many(0, 3, out, "work")
+    plan.gather_range(0, 3, out, "work")
     plan.gather(1, out, "work")
     s = zsp.Schedule(plan, [(0, 2), (2, 1)], [0, 1, 1, 0], 1)
     arena = torch.empty(s.arena_bytes, dtype=torch.uint8, device=d)

@@ -71,7 +71,7 @@ def test_random_case(seed):
     n = int(rng.integers(1, T - first + 1))
     total = sum(numels[first:first + n])
     out = torch.empty(max(total, 1), dtype=torch.bfloat16, device=d)
-    M.plan.gather_many(first, n, out[:total], "work")
+    M.plan.gather_range(first, n, out[:total], "work")
     torch.cuda.synchronize()
     want = [oracle.gather(numels, nd, t, M.o_work) for t in range(first, first + n)]
     want = np.concatenate(want) if want else np.zeros(0, np.uint16)

@@ -36,7 +36,7 @@ def test_acc_gather_is_the_allreduced_gradient(numels, nd):
     gdev = [g.to(dev()) for g in grads]
     M.plan.reduce_shard(zsp.ALL_RANKS, gdev, accumulate=False)
     out = torch.empty(max(M.L.total_numel, 1), dtype=torch.float32, device=dev())
-    M.plan.gather_many(0, M.L.T, out[:M.L.total_numel], "acc")
+    M.plan.gather_range(0, M.L.T, out[:M.L.total_numel], "acc")
     torch.cuda.synchronize()
     want, red = o_allreduced(M, grads)
     assert_bits(np_of(M.g_acc[:M.n]), red, "reduced slices")
@@ -60,11 +60,11 @@ def run_stage(M, stage, grads, step):
     if stage == 1:
         replica = torch.empty(max(M.L.total_numel, 1), dtype=torch.float32, device=dev())
         p.reduce_shard(zsp.ALL_RANKS, gdev, accumulate=False)
-        p.gather_many(0, M.L.T, replica[:M.L.total_numel], "acc")
+        p.gather_range(0, M.L.T, replica[:M.L.total_numel], "acc")
         p.adam_step(zsp.ALL_RANKS, step=step, **HP)
     else:
         p.reduce_adam_step(zsp.ALL_RANKS, gdev, step=step, **HP)
-    p.gather_many(0, M.L.T, full[:M.L.total_numel], "work")
+    p.gather_range(0, M.L.T, full[:M.L.total_numel], "work")
     torch.cuda.synchronize()
     return np_of(full[:M.L.total_numel])
 
@@ -92,7 +92,7 @@ def test_acc_gather_needs_an_accumulator():
     M = Mirror([1003, 64], 4, with_acc=False)
     out = torch.empty(1067, dtype=torch.float32, device=dev())
     with pytest.raises(zsp.ZspError) as e:
-        M.plan.gather_many(0, 2, out, "acc")
+        M.plan.gather_range(0, 2, out, "acc")
     assert e.value.status == binding.ESTATE
     with pytest.raises(TypeError):
-        M.plan.gather_many(0, 2, out.to(torch.bfloat16), "acc")   # fp32 only
+        M.plan.gather_range(0, 2, out.to(torch.bfloat16), "acc")   # fp32 only

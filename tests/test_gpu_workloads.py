@@ -8,7 +8,9 @@ plus the first and last element of many pieces) or a property that holds at
 any size:
   * copy-in: sampled master/work equal the parameter element the oracle's
     layout puts there; sampled pad slots are +0;
-  * gather(partition(x)) == x over every element (all-rank workloads);
+  * gather(partition(x)) == x over every element (all-rank workloads), by
+    the range form into one buffer and by the list form into one output per
+    parameter;
   * each step: sampled master, m, v, work after the step equal the oracle's
     rank-order reduce + Adam of the same inputs (bit-exact expected; the bar
     is 2 ulp / 1e-6 relative for fp32 state, 1 ulp for bf16); pad slots stay
@@ -116,15 +118,27 @@ def test_workload_full_size(name):
     # gather(partition(x)) == x over every element
     if w.rank_local < 0:
         out = torch.empty(L.total_numel, dtype=torch.float32, device=dev)
-        r.plan.gather_many(0, L.T, out, "master")
+        r.plan.gather_range(0, L.T, out, "master")
         torch.cuda.synchronize()
         assert torch.equal(out, flat.float()), "gather(partition(x)) != x (master)"
         del out
         outw = torch.empty(L.total_numel, dtype=torch.bfloat16, device=dev)
-        r.plan.gather_many(0, L.T, outw, "work")
+        r.plan.gather_range(0, L.T, outw, "work")
         torch.cuda.synchronize()
         assert torch.equal(outw, flat.to(torch.bfloat16)), "gather(partition(x)) != x (work)"
         del outw
+        # the list form: every parameter, last first, each into its own output
+        ids = list(range(L.T - 1, -1, -1))
+        outs = [torch.empty(max(int(L.numel[t]), 1), dtype=torch.bfloat16, device=dev)
+                for t in ids]
+        r.plan.gather_many(ids, outs, "work")
+        torch.cuda.synchronize()
+        fb = flat.to(torch.bfloat16)
+        got = torch.cat([o[:int(L.numel[t])] for t, o in zip(ids, outs)])
+        want = torch.cat([fb[int(L.flat_off[t]):int(L.flat_off[t + 1])] for t in ids])
+        assert torch.equal(got.view(torch.int16), want.view(torch.int16)), \
+            "list gather(partition(x)) != x (work)"
+        del outs, got, want, fb
     del flat
     torch.cuda.empty_cache()
 
@@ -220,7 +234,7 @@ def test_decoder_stack_beyond_32bit_indices():
     out32 = torch.empty(w.numel[4], dtype=torch.float32, device=dev)
     for layer in (31, 30, 17, 0):
         first = 9 * layer
-        plan.gather_many(first, 9, out, "work")
+        plan.gather_range(first, 9, out, "work")
         want = flat[int(offs[first]):int(offs[first + 9])]
         assert torch.equal(out.view(torch.int16), want.view(torch.int16)), f"layer {layer}"
         plan.gather(first + 4, out32, "master")   # W1 of the layer, fp32 master

@@ -220,3 +220,25 @@ def test_bf16_cast_matches_torch():
     ref = torch_bf16_bits(x)
     assert np.array_equal(got[finite], ref[finite])
     assert np.all(np.isnan(oracle.bf16_to_f32(got[~finite])))
+
+
+def test_bf16_cast_nan_rule():
+    """NaN inputs: the result is a quiet NaN of the same sign whose payload is
+    the input payload's leading bits -- the IEEE 754 recommendation for
+    narrowing a NaN (keep the payload as far as it fits, set the quiet bit).
+    Checked as two properties over every bf16 NaN pattern: a quiet bf16 NaN
+    widened to fp32 (bits << 16) and cast back is unchanged, and a signalling
+    one comes back quieted with sign and payload kept; then fp32 NaNs with low
+    payload bits set, which the narrowing drops."""
+    hi = np.arange(1 << 16, dtype=np.uint32)
+    nan16 = hi[((hi & 0x7f80) == 0x7f80) & ((hi & 0x007f) != 0)]
+    quiet = nan16[(nan16 & 0x0040) != 0]
+    signalling = nan16[(nan16 & 0x0040) == 0]
+    back = oracle.bf16_rne((quiet << 16).astype(np.uint32).view(np.float32))
+    assert np.array_equal(back.astype(np.uint32), quiet)
+    back = oracle.bf16_rne((signalling << 16).astype(np.uint32).view(np.float32))
+    assert np.array_equal(back.astype(np.uint32), signalling | 0x0040)
+    low = np.array([0x7f800001, 0xff800001, 0x7fc00001, 0xffffffff, 0x7fbfffff, 0x7fa0ffff],
+                   np.uint32)
+    got = oracle.bf16_rne(low.view(np.float32)).astype(np.uint32)
+    assert np.array_equal(got, (low >> 16) | 0x0040)

@@ -56,7 +56,8 @@ def _load():
         "zsp_reduce_adam_step_params": (i32, [vp, i32, i32, i32, vpp, i32, i32, i32, f32, f32,
                                               f32, f32, i64, vp]),
         "zsp_gather": (i32, [vp, i32, i32, vp, vp]),
-        "zsp_gather_many": (i32, [vp, i32, i32, i32, vp, vp]),
+        "zsp_gather_range": (i32, [vp, i32, i32, i32, vp, vp]),
+        "zsp_gather_many": (i32, [vp, i32p, i32, i32, vpp, vp]),
         "zsp_checkpoint_write_host": (i32, [vp, i32, ctypes.c_char_p, i64, vp, vp, vp, vp]),
         "zsp_checkpoint_read_host": (i32, [vp, i32, ctypes.c_char_p, i64p, vp, vp, vp, vp]),
         "zsp_checkpoint_save": (i32, [vp, i32, ctypes.c_char_p, i64, vp]),
@@ -229,11 +230,44 @@ def zsp_gather(h, param_id, out, source="work", stream=None):
     _check(lib.zsp_gather(h, int(param_id), src, _ptr(out, dt, "out"), _stream(stream)))
 
 
-def zsp_gather_many(h, first, n, out, source="work", stream=None):
+def zsp_gather_range(h, first, n, out, source="work", stream=None):
     src = _SOURCES[source]
     dt = torch.bfloat16 if src == SRC_WORK else torch.float32
-    _check(lib.zsp_gather_many(h, int(first), int(n), src, _ptr(out, dt, "out"),
-                               _stream(stream)))
+    _check(lib.zsp_gather_range(h, int(first), int(n), src, _ptr(out, dt, "out"),
+                                _stream(stream)))
+
+
+def _list_arrays(ids, outs, dt):
+    if len(ids) != len(outs):
+        raise ValueError(f"{len(ids)} ids but {len(outs)} outputs")
+    n = len(ids)
+    ids_c = (ctypes.c_int32 * max(n, 1))(*[int(i) for i in ids])
+    ptrs = [None if o is None else _ptr(o, dt, f"outs[{i}]").value for i, o in enumerate(outs)]
+    return ids_c, (ctypes.c_void_p * max(n, 1))(*ptrs), n
+
+
+def zsp_gather_many(h, ids, outs, source="work", stream=None):
+    src = _SOURCES[source]
+    dt = torch.bfloat16 if src == SRC_WORK else torch.float32
+    ids_c, outs_c, n = _list_arrays(ids, outs, dt)
+    _check(lib.zsp_gather_many(h, ids_c, n, src, outs_c, _stream(stream)))
+
+
+class GatherList:
+    """The C arrays of one zsp_gather_many call, marshalled once: a caller
+    that gathers the same bucket into the same outputs again and again (a
+    module's parameters each step) pays the per-tensor conversion once.
+    The outputs are kept alive with the object."""
+
+    def __init__(self, ids, outs, source="work"):
+        self.src = _SOURCES[source]
+        dt = torch.bfloat16 if self.src == SRC_WORK else torch.float32
+        self.ids_c, self.outs_c, self.n = _list_arrays(ids, outs, dt)
+        self.ids, self.outs = list(ids), list(outs)
+
+    def run(self, h, stream=None):
+        _check(lib.zsp_gather_many(h, self.ids_c, self.n, self.src, self.outs_c,
+                                   _stream(stream)))
 
 
 def _host_arrays(S, master, m, v, work, writable):
@@ -485,10 +519,29 @@ class Plan:
             _need(out, self.numel[param_id], "out")
         zsp_gather(self._h, param_id, out, source, stream)
 
-    def gather_many(self, first, n, out, source="work", stream=None):
+    def gather_range(self, first, n, out, source="work", stream=None):
         if 0 <= first and n >= 1 and first + n <= len(self.numel):
             _need(out, sum(self.numel[first:first + n]), "out")
-        zsp_gather_many(self._h, first, n, out, source, stream)
+        zsp_gather_range(self._h, first, n, out, source, stream)
+
+    def gather_many(self, ids, outs, source="work", stream=None):
+        """Parameter ids[i] into outs[i] (a tensor of at least its numel
+        elements; None for an empty parameter), all in one call."""
+        for i, (t, o) in enumerate(zip(ids, outs)):
+            if 0 <= t < len(self.numel):
+                _need(o, self.numel[t], f"outs[{i}]")
+        zsp_gather_many(self._h, ids, outs, source, stream)
+
+    def gather_list(self, ids, outs, source="work"):
+        """A GatherList for this plan's parameters (sizes checked once);
+        run it with gather_prepared."""
+        for i, (t, o) in enumerate(zip(ids, outs)):
+            if 0 <= t < len(self.numel):
+                _need(o, self.numel[t], f"outs[{i}]")
+        return GatherList(ids, outs, source)
+
+    def gather_prepared(self, glist, stream=None):
+        glist.run(self._h, stream)
 
     def checkpoint_save(self, rank, directory, step, stream=None):
         zsp_checkpoint_save(self._h, rank, directory, step, stream)

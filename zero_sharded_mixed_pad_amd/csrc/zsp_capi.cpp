@@ -122,6 +122,7 @@ void free_tables(zsp_plan* P) {
     P->dev_blob = nullptr;
     P->shard = zsp::ShardTable{};
     P->gather = zsp::GatherTable{};
+    P->params = nullptr;
 }
 
 template <typename T>
@@ -216,6 +217,7 @@ zsp_status zsp_partition(const int64_t* numel, int32_t n_params, int32_t n_d, zs
 void zsp_destroy(zsp_plan* plan) {
     if (!plan) return;
     zsp::staging_free(plan->staging);
+    zsp::list_staging_free(plan->lists);
     free_tables(plan);
     delete plan;
 }
@@ -262,12 +264,18 @@ zsp_status zsp_bind_state(zsp_plan* P, int32_t rank_or_all, float* master, float
 
     zsp::HostShardTable hs;
     zsp::HostGatherTable hg;
+    std::vector<zsp::ParamInfo> hp;
     try {
         zsp::build_shard_table(P->numel, P->shard_len, P->full_off, P->shard_off, P->flat_off,
                                P->S, P->nd, rank_or_all, hs);
-        if (rank_or_all == ZSP_ALL_RANKS)
+        if (rank_or_all == ZSP_ALL_RANKS) {
             zsp::build_gather_table(P->numel, P->shard_len, P->shard_off, P->flat_off, P->S,
                                     P->nd, hg);
+            hp.resize(size_t(P->T));
+            for (int32_t t = 0; t < P->T; ++t)
+                hp[size_t(t)] = zsp::ParamInfo{P->shard_off[size_t(t)], P->shard_len[size_t(t)],
+                                               P->numel[size_t(t)], 0};
+        }
     } catch (const std::bad_alloc&) {
         return fail(ZSP_ENOMEM, "out of host memory building tables");
     }
@@ -279,14 +287,14 @@ zsp_status zsp_bind_state(zsp_plan* P, int32_t rank_or_all, float* master, float
     if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
 
     // One allocation: [e0 | info | tile | k0 | delta | gtile | gtile_delta |
-    // gtile_pair], 256-byte aligned parts.
-    constexpr int kParts = 8;
+    // gtile_pair | params], 256-byte aligned parts.
+    constexpr int kParts = 9;
     const size_t sz[kParts] = {bytes_of(hs.e0), bytes_of(hs.info),  bytes_of(hs.tile),
                                bytes_of(hg.k0), bytes_of(hg.delta), bytes_of(hg.tile),
-                               bytes_of(hg.tile_delta), bytes_of(hg.tile_pair)};
+                               bytes_of(hg.tile_delta), bytes_of(hg.tile_pair), bytes_of(hp)};
     const void* src[kParts] = {hs.e0.data(), hs.info.data(),  hs.tile.data(),
                                hg.k0.data(), hg.delta.data(), hg.tile.data(),
-                               hg.tile_delta.data(), hg.tile_pair.data()};
+                               hg.tile_delta.data(), hg.tile_pair.data(), hp.data()};
     size_t off[kParts], total = 0;
     for (int i = 0; i < kParts; ++i) {
         off[i] = total;
@@ -309,6 +317,17 @@ zsp_status zsp_bind_state(zsp_plan* P, int32_t rank_or_all, float* master, float
             }
         }
     }
+    if (P->lists && dev != P->device) {
+        zsp::list_staging_free(P->lists);  // its slots live on the old device
+        P->lists = nullptr;
+    }
+    if (rank_or_all == ZSP_ALL_RANKS && !P->lists) {
+        P->lists = zsp::list_staging_new();
+        if (!P->lists) {
+            if (blob) (void)hipFree(blob);
+            return fail(ZSP_ENOMEM, "out of host memory");
+        }
+    }
     char* b = static_cast<char*>(blob);
     P->dev_blob = blob;
     P->shard.e0 = reinterpret_cast<const int64_t*>(b + off[0]);
@@ -326,6 +345,7 @@ zsp_status zsp_bind_state(zsp_plan* P, int32_t rank_or_all, float* master, float
         P->gather.nq = int64_t(hg.delta.size());
         P->gather.ntile = hg.tile.empty() ? 0 : int64_t(hg.tile.size()) - 1;
         P->gather.total = hg.total;
+        P->params = reinterpret_cast<const zsp::ParamInfo*>(b + off[8]);
     }
     P->bind_rank = rank_or_all;
     P->device = dev;
@@ -486,8 +506,8 @@ zsp_status zsp_reduce_adam_step_params(zsp_plan* P, int32_t rank_or_all, int32_t
                               use_acc, lr, beta1, beta2, eps, step, stream);
 }
 
-zsp_status zsp_gather_many(zsp_plan* P, int32_t first_param, int32_t n_params, zsp_source src,
-                           void* out, void* stream) {
+zsp_status zsp_gather_range(zsp_plan* P, int32_t first_param, int32_t n_params, zsp_source src,
+                            void* out, void* stream) {
     return zsp::gather_range(P, first_param, n_params, src, out, static_cast<hipStream_t>(stream));
 }
 
@@ -535,7 +555,7 @@ extern "C" {
 zsp_status zsp_gather(zsp_plan* P, int32_t param_id, zsp_source src, void* out, void* stream) {
     if (P && (param_id < 0 || param_id >= P->T))
         return fail(ZSP_ERANGE, "parameter %d outside [0, %d)", param_id, P->T);
-    return zsp_gather_many(P, param_id, 1, src, out, stream);
+    return zsp_gather_range(P, param_id, 1, src, out, stream);
 }
 
 

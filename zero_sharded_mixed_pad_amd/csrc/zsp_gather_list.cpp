@@ -1,0 +1,257 @@
+// zsp_gather_list.cpp -- zsp_gather_many: gather a list of parameters, in
+// any order, each into its own output, in one pass ("The ZeRO-3 Diagram
+// Most People Remember Is Wrong", section 3: a module's parameters are
+// all-gathered just before it runs; section 8: gathers go out in buckets of
+// parameters).
+//
+// A list of up to kListArgMax parameters with elements travels in the
+// kernel arguments: one launch, nothing staged. A longer list is staged:
+// its entries (output, parameter, first tile) and a coarse index (the entry
+// of every 64th tile) are written to pinned host memory and copied to the
+// device on the caller's stream; a first kernel turns them into one record
+// per tile and a second copies the tiles. The plan keeps four staging
+// slots, used in turn, each with an event recorded after its last kernel:
+// a slot is refilled only once the work of its previous use has finished
+// (the host waits for that event, which happens only with four staged
+// gathers still in flight), so calls on any streams and threads stay
+// apart. A slot grows, and is then reallocated, when a list needs more
+// room than it has.
+#include <algorithm>
+#include <cstring>
+#include <mutex>
+#include <new>
+#include <vector>
+
+#include "zsp_entry.hpp"
+#include "zsp_internal.hpp"
+#include "zsp_plan.hpp"
+
+namespace zsp {
+
+namespace {
+
+constexpr int kSlots = 4;
+// Tiles whose records one staged chunk holds (a multiple of 64): 16 MiB of
+// records, 2^28 elements.
+constexpr int64_t kRecChunk = int64_t(1) << 19;
+
+struct ListSlot {
+    void* host = nullptr;  // pinned: entries then coarse index
+    size_t host_cap = 0;
+    void* dev = nullptr;  // entries, coarse index, records
+    size_t dev_cap = 0;
+    hipEvent_t done = nullptr;
+    bool pending = false;
+};
+
+size_t round_up(size_t x) { return (x + 255) & ~size_t(255); }
+
+}  // namespace
+
+struct ListStaging {
+    std::mutex mu;
+    ListSlot slot[kSlots];
+    int next = 0;
+};
+
+ListStaging* list_staging_new() { return new (std::nothrow) ListStaging(); }
+
+void list_staging_free(ListStaging* ls) {
+    if (!ls) return;
+    for (ListSlot& s : ls->slot) {
+        if (s.pending) (void)hipEventSynchronize(s.done);
+        if (s.done) (void)hipEventDestroy(s.done);
+        if (s.host) (void)hipHostFree(s.host);
+        if (s.dev) (void)hipFree(s.dev);
+    }
+    delete ls;
+}
+
+// Checked and measured list: the entries with elements, their tiles and
+// which form the gather takes.
+struct ListPlan {
+    std::vector<int32_t> id;
+    std::vector<void*> out;
+    std::vector<int64_t> tile0;  // n+1
+    int64_t tiles = 0;
+    bool short_pieces = false;
+};
+
+zsp_status check_list(const zsp_plan* P, const int32_t* ids, int32_t n, zsp_source src,
+                      void* const* outs, ListPlan* lp) {
+    zsp_status st = check_bound(P);
+    if (st != ZSP_OK) return st;
+    if (P->bind_rank != ZSP_ALL_RANKS)
+        return set_error(ZSP_ESTATE,
+                         "gather needs every rank's shard (state bound for rank %d only)",
+                         P->bind_rank);
+    if (n < 0) return set_error(ZSP_EINVAL, "n = %d is negative", n);
+    if (n > 0 && (!ids || !outs)) return set_error(ZSP_EINVAL, "ids or outs is NULL");
+    if (src != ZSP_SRC_WORK && src != ZSP_SRC_MASTER && src != ZSP_SRC_ACC)
+        return set_error(ZSP_EINVAL, "bad source %d", src);
+    if (src == ZSP_SRC_ACC && !P->acc)
+        return set_error(ZSP_ESTATE, "gather of the accumulator, but none is bound");
+    int64_t tiles = 0, elems = 0, pieces = 0;
+    try {
+        lp->id.clear();
+        lp->out.clear();
+        lp->tile0.clear();
+        for (int32_t i = 0; i < n; ++i) {
+            const int32_t t = ids[i];
+            if (t < 0 || t >= P->T)
+                return set_error(ZSP_ERANGE, "ids[%d] = %d outside [0, %d)", i, t, P->T);
+            const int64_t numel = P->numel[size_t(t)];
+            if (numel == 0) continue;
+            if (!outs[i]) return set_error(ZSP_EINVAL, "outs[%d] is NULL", i);
+            if (reinterpret_cast<uintptr_t>(outs[i]) & 15u)
+                return set_error(ZSP_EINVAL, "outs[%d] is not 16-byte aligned", i);
+            lp->id.push_back(t);
+            lp->out.push_back(outs[i]);
+            lp->tile0.push_back(tiles);
+            tiles += (numel + kTile - 1) / kTile;
+            elems += numel;
+            pieces += P->piece_off[size_t(t) + 1] - P->piece_off[size_t(t)];
+            if (tiles > INT32_MAX)
+                return set_error(ZSP_ERANGE, "list of more than 2^31 tiles of %lld elements",
+                                 (long long)kTile);
+        }
+        lp->tile0.push_back(tiles);
+    } catch (const std::bad_alloc&) {
+        return set_error(ZSP_ENOMEM, "out of host memory");
+    }
+    lp->tiles = tiles;
+    lp->short_pieces = pieces > 0 && elems < pieces * kShortPiece;
+    return ZSP_OK;
+}
+
+ListLaunch list_base(const zsp_plan* P, zsp_source src, const ListPlan& lp) {
+    ListLaunch L;
+    L.params = P->params;
+    L.S = P->S;
+    L.src = src == ZSP_SRC_WORK     ? static_cast<const void*>(P->work)
+            : src == ZSP_SRC_MASTER ? static_cast<const void*>(P->master)
+                                    : static_cast<const void*>(P->acc);
+    L.short_pieces = lp.short_pieces;
+    L.tiles = lp.tiles;
+    return L;
+}
+
+// Sizes of a staged list: entries, coarse index, record area.
+struct StagedSizes {
+    size_t ents, coarse, recs;
+    int64_t rec_tiles;
+};
+
+StagedSizes staged_sizes(const ListPlan& lp, int64_t rec_chunk) {
+    StagedSizes z;
+    const size_t n = lp.id.size();
+    z.ents = round_up(n * sizeof(ListEntry));
+    z.coarse = round_up(size_t((lp.tiles + 63) / 64) * sizeof(int32_t));
+    z.rec_tiles = std::min(rec_chunk, (lp.tiles + 63) / 64 * 64);
+    z.recs = size_t(z.rec_tiles) * sizeof(TileRec);
+    return z;
+}
+
+// Entries, then the coarse index, into host memory at `h`.
+void pack_staged(const ListPlan& lp, char* h, const StagedSizes& z) {
+    ListEntry* e = reinterpret_cast<ListEntry*>(h);
+    const size_t n = lp.id.size();
+    for (size_t i = 0; i < n; ++i) {
+        e[i].out = lp.out[i];
+        e[i].id = lp.id[i];
+        e[i].tile0 = static_cast<int32_t>(lp.tile0[i]);
+    }
+    int32_t* c = reinterpret_cast<int32_t*>(h + z.ents);
+    const int64_t nc = (lp.tiles + 63) / 64;
+    size_t i = 0;
+    for (int64_t k = 0; k < nc; ++k) {
+        while (i + 1 < n && lp.tile0[i + 1] <= 64 * k) ++i;
+        c[k] = static_cast<int32_t>(i);
+    }
+}
+
+zsp_status launch_list(const ListLaunch& L, zsp_source src, hipStream_t stream) {
+    const hipError_t e = launch_gather_list(L, src == ZSP_SRC_WORK ? 2 : 4, stream);
+    if (e != hipSuccess) return set_hip_error(e, "list gather launch");
+    return ZSP_OK;
+}
+
+// Argument form, for lists of at most kListArgMax entries with elements.
+zsp_status gather_list_args(const zsp_plan* P, zsp_source src, const ListPlan& lp,
+                            hipStream_t stream) {
+    ListLaunch L = list_base(P, src, lp);
+    L.n_args = static_cast<int32_t>(lp.id.size());
+    for (int32_t i = 0; i < L.n_args; ++i) {
+        const size_t t = size_t(lp.id[size_t(i)]);
+        L.args[i] = ArgEntry{lp.out[size_t(i)], P->shard_off[t], P->shard_len[t], P->numel[t]};
+        L.arg_tile0[i] = static_cast<int32_t>(lp.tile0[size_t(i)]);
+    }
+    L.arg_tile0[L.n_args] = static_cast<int32_t>(lp.tiles);
+    return launch_list(L, src, stream);
+}
+
+}  // namespace zsp
+
+extern "C" zsp_status zsp_gather_many(zsp_plan* P, const int32_t* ids, int32_t n,
+                                      zsp_source src, void* const* outs, void* stream) {
+    using namespace zsp;
+    ListPlan lp;
+    zsp_status st = check_list(P, ids, n, src, outs, &lp);
+    if (st != ZSP_OK) return st;
+    const hipStream_t hs = static_cast<hipStream_t>(stream);
+    if (lp.tiles == 0) return ZSP_OK;
+    if (lp.id.size() <= size_t(kListArgMax)) return gather_list_args(P, src, lp, hs);
+
+    ListStaging& ls = *P->lists;  // made by the all-rank bind check_list asked for
+    std::lock_guard<std::mutex> lock(ls.mu);
+    ListSlot& s = ls.slot[ls.next];
+    ls.next = (ls.next + 1) % kSlots;
+    hipError_t e;
+    if (s.pending) {
+        if ((e = hipEventSynchronize(s.done)) != hipSuccess)
+            return set_hip_error(e, "waiting for a staging slot");
+        s.pending = false;
+    }
+    if (!s.done && (e = hipEventCreateWithFlags(&s.done, hipEventDisableTiming)) != hipSuccess)
+        return set_hip_error(e, "hipEventCreate");
+    const StagedSizes z = staged_sizes(lp, kRecChunk);
+    const size_t up = z.ents + z.coarse;
+    if (s.host_cap < up) {
+        if (s.host) (void)hipHostFree(s.host);
+        s.host = nullptr;
+        s.host_cap = 0;
+        if ((e = hipHostMalloc(&s.host, up)) != hipSuccess)
+            return set_error(ZSP_ENOMEM, "pinned staging of %zu bytes: %s", up,
+                             hipGetErrorString(e));
+        s.host_cap = up;
+    }
+    if (s.dev_cap < up + z.recs) {
+        if (s.dev) (void)hipFree(s.dev);
+        s.dev = nullptr;
+        s.dev_cap = 0;
+        if ((e = hipMalloc(&s.dev, up + z.recs)) != hipSuccess)
+            return set_error(ZSP_ENOMEM, "device staging of %zu bytes: %s", up + z.recs,
+                             hipGetErrorString(e));
+        s.dev_cap = up + z.recs;
+    }
+    pack_staged(lp, static_cast<char*>(s.host), z);
+    ListLaunch L = list_base(P, src, lp);
+    char* d = static_cast<char*>(s.dev);
+    L.ents = reinterpret_cast<const ListEntry*>(d);
+    L.n_ents = static_cast<int32_t>(lp.id.size());
+    L.coarse = reinterpret_cast<const int32_t*>(d + z.ents);
+    L.recs = reinterpret_cast<TileRec*>(d + up);
+    L.rec_cap = z.rec_tiles;
+    st = ZSP_OK;
+    if ((e = hipMemcpyAsync(s.dev, s.host, up, hipMemcpyHostToDevice, hs)) != hipSuccess)
+        st = set_hip_error(e, "staging copy");
+    else
+        st = launch_list(L, src, hs);
+    // Recorded even after a failed launch: the copy may be in flight.
+    if ((e = hipEventRecord(s.done, hs)) != hipSuccess) {
+        (void)hipStreamSynchronize(hs);
+        return st != ZSP_OK ? st : set_hip_error(e, "hipEventRecord");
+    }
+    s.pending = true;
+    return st;
+}

@@ -134,6 +134,77 @@ struct GatherLaunch {
 // form: shared boundary lines make up a few percent of the bytes or more.
 constexpr int64_t kShortPiece = 4096;
 
+// ---- Gather of a list of parameters into separate outputs ----------------
+// The list's outputs are cut into tiles of kTile elements, each tile inside
+// one output; the tiles of the list are numbered 0, 1, ... in list order.
+
+// Device table, one record per parameter (all-rank bindings): where its
+// slots start in a rank's shard, its shard length and its element count.
+struct ParamInfo {
+    int64_t shard_off;
+    int64_t shard_len;
+    int64_t numel;
+    int64_t reserved;
+};
+
+// One output of a staged list, in device memory: the parameter, the output
+// and the list tile its first element falls in. Parameters without
+// elements are left out of the staged list, so tile0 strictly increases.
+struct ListEntry {
+    void* out;
+    int32_t id;
+    int32_t tile0;
+};
+
+// One output of a list short enough to travel in the kernel arguments.
+struct ArgEntry {
+    void* out;
+    int64_t shard_off;
+    int64_t shard_len;
+    int64_t numel;
+};
+constexpr int kListArgMax = 64;
+
+// Where one tile of a list gather reads and writes. Local element k of the
+// tile (k < count) goes to out[k]. Two-piece tiles (split >= 0, shard length
+// at least kTile, so the tile meets at most two ranks' slices): it comes
+// from source element base + k, plus step when k >= split. Many-piece tiles
+// (split = -shard length): from base + k + step * ((rem + k) / shard
+// length), where rem is the tile's offset into the slice it starts in;
+// count holds the element count in its low 16 bits and rem above them.
+struct TileRec {
+    void* out;
+    int64_t base;
+    int64_t step;
+    int32_t split;
+    int32_t count;
+};
+
+struct ListLaunch {
+    const ParamInfo* params = nullptr;  // plan's device table
+    int64_t S = 0;
+    const void* src = nullptr;
+    bool short_pieces = false;
+    int64_t tiles = 0;  // tiles of the whole list
+    // Argument form (tiles of every output from the arguments): n entries
+    // and their first tiles (tile0[n] = tiles).
+    int32_t n_args = 0;
+    ArgEntry args[kListArgMax];
+    int32_t arg_tile0[kListArgMax + 1];
+    // Staged form: entries and the coarse index (entry of tile 64c, for
+    // every c) in device memory, and a record area for up to rec_cap tiles;
+    // the list is processed in chunks of rec_cap tiles (a multiple of 64).
+    const ListEntry* ents = nullptr;
+    int32_t n_ents = 0;
+    const int32_t* coarse = nullptr;
+    TileRec* recs = nullptr;
+    int64_t rec_cap = 0;
+};
+
+// Launch a list gather (argument form if n_args > 0, else staged); esz is
+// the element size of src and the outputs (2: bf16, 4: fp32).
+hipError_t launch_gather_list(const ListLaunch& L, int esz, hipStream_t stream);
+
 // Launch one E-space operation; dtype is the gradient / parameter dtype.
 hipError_t launch_shard_op(const ShardLaunch& L, ShardOp op, zsp_dtype dtype,
                            hipStream_t stream);

@@ -827,6 +827,195 @@ __global__ __launch_bounds__(kWaveLanes) void gather_kernel(const GatherArgs a) 
     }
 }
 
+// ---- Gather of a list of parameters into separate outputs ------------------
+// Each wave copies one tile of kTile elements of one output. Its record
+// (TileRec) says where the tile's elements come from: a tile of a
+// parameter whose slices hold kTile elements or more meets at most two
+// ranks' slices, so two bases and a split describe it; a tile of a smaller
+// parameter meets several, and each element group finds its rank by one
+// division by the (small) shard length.
+
+// The record of local tile kw / kTile of an output of a parameter with
+// the given layout (element kw of the output is the tile's first).
+__device__ __forceinline__ TileRec make_rec(void* out, int esz, int64_t shard_off, int64_t s,
+                                            int64_t numel, int64_t S, int64_t kw) {
+    TileRec r;
+    r.out = static_cast<char*>(out) + kw * esz;
+    // the rank whose slice holds element kw (a 32-bit division when both fit)
+    const int64_t q = ((kw | s) >> 32) == 0 ? int64_t(uint32_t(kw) / uint32_t(s)) : kw / s;
+    const int64_t rem = kw - q * s;
+    r.step = S - s;
+    r.base = shard_off + kw + q * r.step;  // q*S + shard_off + (kw - q*s)
+    const int64_t cnt = min(kTile, numel - kw);
+    if (s >= kTile) {
+        r.split = static_cast<int32_t>(min(s - rem, kTile));
+        r.count = static_cast<int32_t>(cnt);
+    } else {
+        r.split = -static_cast<int32_t>(s);
+        r.count = static_cast<int32_t>(cnt | (rem << 16));
+    }
+    return r;
+}
+
+// Source offset (added to element k's own index) of local element k.
+__device__ __forceinline__ int64_t rec_delta(const TileRec& rc, int k, int rem, uint32_t s) {
+    if (rc.split >= 0) return rc.base + (k >= rc.split ? rc.step : 0);
+    return rc.base + int64_t(uint32_t(rem + k) / s) * rc.step;
+}
+
+// Copy one tile: 16-byte groups (8 bf16, or two quads of fp32 per lane).
+template <typename T, bool SHORT>
+__device__ __forceinline__ void copy_rec_tile(const TileRec& rc, const T* src, int lane) {
+    using Sh = GatherShape<T>;
+    T* out = static_cast<T*>(rc.out);
+    const bool many = rc.split < 0;
+    const int count = many ? (rc.count & 0xffff) : rc.count;
+    const int rem = many ? (rc.count >> 16) : 0;
+    const uint32_t s = many ? uint32_t(-rc.split) : 1u;
+#pragma unroll
+    for (int h = 0; h < Sh::kGroups; ++h) {
+        const int o = h * Sh::kStride + lane * Sh::kLaneStep;
+        if (o >= count) continue;
+        const bool full = o + Sh::kGroup <= count;
+        bool one;
+        if (!many) one = o + Sh::kGroup <= rc.split || o >= rc.split;
+        else one = uint32_t(rem + o) / s == uint32_t(rem + o + Sh::kGroup - 1) / s;
+        if (full && one) {
+            // out + o is 16-byte aligned; the source may sit at any element offset.
+            const int64_t d = rec_delta(rc, o, rem, s);
+            stnt(reinterpret_cast<u32x4*>(out + o),
+                 ld_src<SHORT>(reinterpret_cast<const u32x4_a2*>(src + d + o)));
+        } else {
+            // Crosses a slice boundary or the output's end: element by
+            // element, every load issued (clamped to the last element).
+            T x[Sh::kGroup];
+#pragma unroll
+            for (int i = 0; i < Sh::kGroup; ++i) {
+                const int k = min(o + i, count - 1);
+                x[i] = src[rec_delta(rc, k, rem, s) + k];
+            }
+            if (full) {
+                stnt(reinterpret_cast<u32x4*>(out + o), __builtin_bit_cast(u32x4, x));
+            } else {
+#pragma unroll
+                for (int i = 0; i < Sh::kGroup; ++i)
+                    if (o + i < count) out[o + i] = x[i];
+            }
+        }
+    }
+}
+
+// Short-piece lists give each XCD runs of kXcdRun consecutive tiles (see
+// kXcdRun); returns the tile of workgroup `blk`, or -1 past the list.
+template <bool SHORT>
+__device__ __forceinline__ int64_t list_tile(int64_t blk, int64_t tiles) {
+    if constexpr (SHORT) {
+        const int64_t x = blk % 8, i = blk / 8;
+        const int64_t t = ((i / kXcdRun) * 8 + x) * kXcdRun + (i % kXcdRun);
+        return t < tiles ? t : -1;
+    } else {
+        return blk;
+    }
+}
+
+struct ListArgArgs {
+    const void* src;
+    int64_t S;
+    int64_t tiles;
+    int32_t n;
+    int32_t esz;
+    ArgEntry ents[kListArgMax];
+    int32_t tile0[kListArgMax + 1];
+};
+
+// Argument form: the list's entries are in the kernel arguments. The wave
+// counts, with scalar loads of the entries' first tiles, the entries that
+// start after the first one at or below its tile, and reads that entry with
+// one more scalar load: the argument segment stays in the scalar cache.
+template <typename T, bool SHORT>
+__global__ __launch_bounds__(kWaveLanes) void gather_list_args(const ListArgArgs a) {
+    const int64_t b = list_tile<SHORT>(blockIdx.x, a.tiles);
+    if (b < 0) return;
+    const char* seg = (const char*)__builtin_amdgcn_kernarg_segment_ptr();
+    const int32_t* t0 = reinterpret_cast<const int32_t*>(seg + offsetof(ListArgArgs, tile0));
+    const ArgEntry* ents = reinterpret_cast<const ArgEntry*>(seg + offsetof(ListArgArgs, ents));
+    // 16 first tiles per batch of scalar loads (the array has kListArgMax + 1
+    // slots, so a batch never reads past it); tiles fit in 32 bits
+    const int32_t bb = static_cast<int32_t>(b);
+    int i = 0;
+#pragma unroll
+    for (int k0 = 0; k0 < kListArgMax; k0 += 16) {
+        if (k0 >= a.n) break;
+        int32_t v[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) v[j] = t0[k0 + j];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) i += (k0 + j >= 1 && k0 + j < a.n && v[j] <= bb) ? 1 : 0;
+    }
+    const ArgEntry e = ents[i];
+    const TileRec rc = make_rec(e.out, a.esz, e.shard_off, e.shard_len, e.numel, a.S,
+                                (b - t0[i]) * kTile);
+    copy_rec_tile<T, SHORT>(rc, static_cast<const T*>(a.src), threadIdx.x);
+}
+
+struct ListExpandArgs {
+    const ListEntry* ents;
+    const int32_t* coarse;
+    const ParamInfo* params;
+    TileRec* recs;
+    int64_t S;
+    int64_t t_begin;  // a multiple of 64
+    int64_t t_end;
+    int32_t n;
+    int32_t esz;
+};
+
+// Staged form, first kernel: the records of tiles [t_begin, t_end), 64 per
+// wave. The coarse index gives the entry of the wave's first tile; the
+// wave's 64 tiles lie in that entry and at most 63 after it (every staged
+// entry has a tile), whose first tiles the lanes load; each lane finds its
+// own entry among them by a binary search over the lanes.
+__global__ __launch_bounds__(kWaveLanes) void list_expand_kernel(const ListExpandArgs a) {
+    const int lane = threadIdx.x;
+    const int64_t b0 = a.t_begin + int64_t(blockIdx.x) * 64;
+    const int64_t b = b0 + lane;
+    const int i0 = a.coarse[b0 / 64];
+    // lane l holds window entry i0 + l (past the list: its first tile reads
+    // as unreachable)
+    const ListEntry w = a.ents[min(i0 + lane, a.n - 1)];
+    const int32_t t0 = i0 + lane < a.n ? w.tile0 : INT32_MAX;
+    int j = 0;
+    for (int st = 32; st > 0; st >>= 1) {
+        const int c = j + st;
+        const int32_t v = __shfl(t0, c < 64 ? c : 63);
+        if (c < 64 && v <= b) j = c;
+    }
+    const int32_t id = __shfl(w.id, j);
+    const int32_t tile0 = __shfl(w.tile0, j);
+    const uint64_t o = uint64_t(reinterpret_cast<uintptr_t>(w.out));
+    void* out = reinterpret_cast<void*>((uint64_t(uint32_t(__shfl(int(o >> 32), j))) << 32) |
+                                        uint32_t(__shfl(int(uint32_t(o)), j)));
+    if (b >= a.t_end) return;
+    const ParamInfo p = a.params[id];
+    const int64_t kw = (b - tile0) * kTile;
+    a.recs[b - a.t_begin] = make_rec(out, a.esz, p.shard_off, p.shard_len, p.numel, a.S, kw);
+}
+
+struct ListRecArgs {
+    const TileRec* recs;
+    const void* src;
+    int64_t tiles;  // tiles of the chunk
+};
+
+// Staged form, second kernel: one record per wave.
+template <typename T, bool SHORT>
+__global__ __launch_bounds__(kWaveLanes) void gather_list_recs(const ListRecArgs a) {
+    const int64_t b = list_tile<SHORT>(blockIdx.x, a.tiles);
+    if (b < 0) return;
+    const TileRec rc = a.recs[b];
+    copy_rec_tile<T, SHORT>(rc, static_cast<const T*>(a.src), threadIdx.x);
+}
+
 // Resident waves. With every CU full of shard waves, each touching a dozen
 // streams, HBM serves the mix of reads and writes less efficiently than with
 // fewer waves resident, as long as each wave has enough bytes in flight.
@@ -1006,6 +1195,80 @@ hipError_t launch_gather(const GatherLaunch& L, zsp_dtype dtype, hipStream_t str
             hipLaunchKernelGGL((gather_kernel<float, false>), grid, block, 0, stream, a);
     }
     return hipGetLastError();
+}
+
+namespace {
+
+// Workgroups of a list launch over `tiles` tiles.
+int64_t list_blocks(int64_t tiles, bool short_pieces) {
+    const int64_t runs = 8 * kXcdRun;
+    return short_pieces ? (tiles + runs - 1) / runs * runs : tiles;
+}
+
+template <typename T>
+hipError_t launch_list_t(const ListLaunch& L, int esz, hipStream_t stream) {
+    const dim3 block(kWaveLanes);
+    if (L.n_args > 0) {
+        ListArgArgs a{};
+        a.src = L.src;
+        a.S = L.S;
+        a.tiles = L.tiles;
+        a.n = L.n_args;
+        a.esz = esz;
+        for (int i = 0; i < L.n_args; ++i) a.ents[i] = L.args[i];
+        for (int i = 0; i <= L.n_args; ++i) a.tile0[i] = L.arg_tile0[i];
+        const int64_t blocks = list_blocks(L.tiles, L.short_pieces);
+        if (blocks > kMaxBlocks) return hipErrorInvalidValue;
+        if (L.short_pieces)
+            hipLaunchKernelGGL((gather_list_args<T, true>), dim3(uint32_t(blocks)), block, 0,
+                               stream, a);
+        else
+            hipLaunchKernelGGL((gather_list_args<T, false>), dim3(uint32_t(blocks)), block, 0,
+                               stream, a);
+        return hipGetLastError();
+    }
+    if (L.rec_cap <= 0 || L.rec_cap % 64 != 0) return hipErrorInvalidValue;
+    for (int64_t t = 0; t < L.tiles; t += L.rec_cap) {
+        const int64_t t_end = min(L.tiles, t + L.rec_cap);
+        ListExpandArgs e{};
+        e.ents = L.ents;
+        e.coarse = L.coarse;
+        e.params = L.params;
+        e.recs = L.recs;
+        e.S = L.S;
+        e.t_begin = t;
+        e.t_end = t_end;
+        e.n = L.n_ents;
+        e.esz = esz;
+        const int64_t waves = (t_end - t + 63) / 64;
+        hipLaunchKernelGGL(list_expand_kernel, dim3(uint32_t(waves)), block, 0, stream, e);
+        hipError_t err = hipGetLastError();
+        if (err != hipSuccess) return err;
+        ListRecArgs g{};
+        g.recs = L.recs;
+        g.src = L.src;
+        g.tiles = t_end - t;
+        const int64_t blocks = list_blocks(t_end - t, L.short_pieces);
+        if (blocks > kMaxBlocks) return hipErrorInvalidValue;
+        if (L.short_pieces)
+            hipLaunchKernelGGL((gather_list_recs<T, true>), dim3(uint32_t(blocks)), block, 0,
+                               stream, g);
+        else
+            hipLaunchKernelGGL((gather_list_recs<T, false>), dim3(uint32_t(blocks)), block, 0,
+                               stream, g);
+        err = hipGetLastError();
+        if (err != hipSuccess) return err;
+    }
+    return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_gather_list(const ListLaunch& L, int esz, hipStream_t stream) {
+    if (L.tiles <= 0) return hipSuccess;
+    if (esz == 2) return launch_list_t<uint16_t>(L, esz, stream);
+    if (esz == 4) return launch_list_t<float>(L, esz, stream);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace zsp

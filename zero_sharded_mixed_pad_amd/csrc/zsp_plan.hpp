@@ -12,6 +12,9 @@
 namespace zsp {
 struct CkptStaging;                    // pinned chunks, streams, events (zsp_ckpt_dev.cpp)
 void staging_free(CkptStaging* st);    // NULL is a no-op
+struct ListStaging;                    // staging slots of long list gathers (zsp_gather_list.cpp)
+ListStaging* list_staging_new();       // NULL when out of host memory
+void list_staging_free(ListStaging* ls);  // NULL is a no-op
 }  // namespace zsp
 
 struct zsp_plan {
@@ -33,9 +36,11 @@ struct zsp_plan {
     uint16_t* work = nullptr;
     float* acc = nullptr;
 
-    void* dev_blob = nullptr;  // one device allocation holding both tables
+    void* dev_blob = nullptr;  // one device allocation holding every table
     zsp::ShardTable shard;
     zsp::GatherTable gather;
+    const zsp::ParamInfo* params = nullptr;  // per parameter (all-rank bindings)
+    zsp::ListStaging* lists = nullptr;       // made at an all-rank bind
 
     zsp::CkptStaging* staging = nullptr;  // made by the first checkpoint save / load
 };
