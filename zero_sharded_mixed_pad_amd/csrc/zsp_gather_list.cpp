@@ -20,10 +20,10 @@
 #include <cstring>
 #include <mutex>
 #include <new>
-#include <vector>
 
 #include "zsp_entry.hpp"
 #include "zsp_internal.hpp"
+#include "zsp_list.hpp"
 #include "zsp_plan.hpp"
 
 namespace zsp {
@@ -44,7 +44,7 @@ struct ListSlot {
     bool pending = false;
 };
 
-size_t round_up(size_t x) { return (x + 255) & ~size_t(255); }
+size_t list_round_up(size_t x) { return (x + 255) & ~size_t(255); }
 
 }  // namespace
 
@@ -67,18 +67,8 @@ void list_staging_free(ListStaging* ls) {
     delete ls;
 }
 
-// Checked and measured list: the entries with elements, their tiles and
-// which form the gather takes.
-struct ListPlan {
-    std::vector<int32_t> id;
-    std::vector<void*> out;
-    std::vector<int64_t> tile0;  // n+1
-    int64_t tiles = 0;
-    bool short_pieces = false;
-};
-
 zsp_status check_list(const zsp_plan* P, const int32_t* ids, int32_t n, zsp_source src,
-                      void* const* outs, ListPlan* lp) {
+                      void* const* outs, ListTotals* lt) {
     zsp_status st = check_bound(P);
     if (st != ZSP_OK) return st;
     if (P->bind_rank != ZSP_ALL_RANKS)
@@ -91,83 +81,49 @@ zsp_status check_list(const zsp_plan* P, const int32_t* ids, int32_t n, zsp_sour
         return set_error(ZSP_EINVAL, "bad source %d", src);
     if (src == ZSP_SRC_ACC && !P->acc)
         return set_error(ZSP_ESTATE, "gather of the accumulator, but none is bound");
-    int64_t tiles = 0, elems = 0, pieces = 0;
-    try {
-        lp->id.clear();
-        lp->out.clear();
-        lp->tile0.clear();
-        for (int32_t i = 0; i < n; ++i) {
-            const int32_t t = ids[i];
-            if (t < 0 || t >= P->T)
-                return set_error(ZSP_ERANGE, "ids[%d] = %d outside [0, %d)", i, t, P->T);
-            const int64_t numel = P->numel[size_t(t)];
-            if (numel == 0) continue;
-            if (!outs[i]) return set_error(ZSP_EINVAL, "outs[%d] is NULL", i);
-            if (reinterpret_cast<uintptr_t>(outs[i]) & 15u)
-                return set_error(ZSP_EINVAL, "outs[%d] is not 16-byte aligned", i);
-            lp->id.push_back(t);
-            lp->out.push_back(outs[i]);
-            lp->tile0.push_back(tiles);
-            tiles += (numel + kTile - 1) / kTile;
-            elems += numel;
-            pieces += P->piece_off[size_t(t) + 1] - P->piece_off[size_t(t)];
-            if (tiles > INT32_MAX)
-                return set_error(ZSP_ERANGE, "list of more than 2^31 tiles of %lld elements",
-                                 (long long)kTile);
-        }
-        lp->tile0.push_back(tiles);
-    } catch (const std::bad_alloc&) {
-        return set_error(ZSP_ENOMEM, "out of host memory");
+    int64_t count = 0, tiles = 0, elems = 0, pieces = 0;
+    for (int32_t i = 0; i < n; ++i) {
+        const int32_t t = ids[i];
+        if (t < 0 || t >= P->T)
+            return set_error(ZSP_ERANGE, "ids[%d] = %d outside [0, %d)", i, t, P->T);
+        const int64_t numel = P->numel[size_t(t)];
+        if (numel == 0) continue;
+        if (!outs[i]) return set_error(ZSP_EINVAL, "outs[%d] is NULL", i);
+        if (reinterpret_cast<uintptr_t>(outs[i]) & 15u)
+            return set_error(ZSP_EINVAL, "outs[%d] is not 16-byte aligned", i);
+        ++count;
+        tiles += (numel + kTile - 1) / kTile;
+        elems += numel;
+        pieces += P->piece_off[size_t(t) + 1] - P->piece_off[size_t(t)];
+        if (tiles > INT32_MAX)
+            return set_error(ZSP_ERANGE, "list of more than 2^31 tiles of %lld elements",
+                             (long long)kTile);
     }
-    lp->tiles = tiles;
-    lp->short_pieces = pieces > 0 && elems < pieces * kShortPiece;
+    lt->count = count;
+    lt->tiles = tiles;
+    lt->short_pieces = pieces > 0 && elems < pieces * kShortPiece;
     return ZSP_OK;
 }
 
-ListLaunch list_base(const zsp_plan* P, zsp_source src, const ListPlan& lp) {
+ListLaunch list_base(const zsp_plan* P, zsp_source src, const ListTotals& lt) {
     ListLaunch L;
     L.params = P->params;
     L.S = P->S;
     L.src = src == ZSP_SRC_WORK     ? static_cast<const void*>(P->work)
             : src == ZSP_SRC_MASTER ? static_cast<const void*>(P->master)
                                     : static_cast<const void*>(P->acc);
-    L.short_pieces = lp.short_pieces;
-    L.tiles = lp.tiles;
+    L.short_pieces = lt.short_pieces;
+    L.tiles = lt.tiles;
     return L;
 }
 
-// Sizes of a staged list: entries, coarse index, record area.
-struct StagedSizes {
-    size_t ents, coarse, recs;
-    int64_t rec_tiles;
-};
-
-StagedSizes staged_sizes(const ListPlan& lp, int64_t rec_chunk) {
+StagedSizes staged_sizes(const ListTotals& lt, int64_t rec_chunk) {
     StagedSizes z;
-    const size_t n = lp.id.size();
-    z.ents = round_up(n * sizeof(ListEntry));
-    z.coarse = round_up(size_t((lp.tiles + 63) / 64) * sizeof(int32_t));
-    z.rec_tiles = std::min(rec_chunk, (lp.tiles + 63) / 64 * 64);
+    z.ents = list_round_up(size_t(lt.count) * sizeof(ListEntry));
+    z.coarse = list_round_up(size_t((lt.tiles + 63) / 64) * sizeof(int32_t));
+    z.rec_tiles = std::min(rec_chunk, (lt.tiles + 63) / 64 * 64);
     z.recs = size_t(z.rec_tiles) * sizeof(TileRec);
     return z;
-}
-
-// Entries, then the coarse index, into host memory at `h`.
-void pack_staged(const ListPlan& lp, char* h, const StagedSizes& z) {
-    ListEntry* e = reinterpret_cast<ListEntry*>(h);
-    const size_t n = lp.id.size();
-    for (size_t i = 0; i < n; ++i) {
-        e[i].out = lp.out[i];
-        e[i].id = lp.id[i];
-        e[i].tile0 = static_cast<int32_t>(lp.tile0[i]);
-    }
-    int32_t* c = reinterpret_cast<int32_t*>(h + z.ents);
-    const int64_t nc = (lp.tiles + 63) / 64;
-    size_t i = 0;
-    for (int64_t k = 0; k < nc; ++k) {
-        while (i + 1 < n && lp.tile0[i + 1] <= 64 * k) ++i;
-        c[k] = static_cast<int32_t>(i);
-    }
 }
 
 zsp_status launch_list(const ListLaunch& L, zsp_source src, hipStream_t stream) {
@@ -176,31 +132,46 @@ zsp_status launch_list(const ListLaunch& L, zsp_source src, hipStream_t stream) 
     return ZSP_OK;
 }
 
-// Argument form, for lists of at most kListArgMax entries with elements.
-zsp_status gather_list_args(const zsp_plan* P, zsp_source src, const ListPlan& lp,
+zsp_status gather_list_args(const zsp_plan* P, const int32_t* ids, int32_t n,
+                            void* const* outs, zsp_source src, const ListTotals& lt,
                             hipStream_t stream) {
-    ListLaunch L = list_base(P, src, lp);
-    L.n_args = static_cast<int32_t>(lp.id.size());
-    for (int32_t i = 0; i < L.n_args; ++i) {
-        const size_t t = size_t(lp.id[size_t(i)]);
-        L.args[i] = ArgEntry{lp.out[size_t(i)], P->shard_off[t], P->shard_len[t], P->numel[t]};
-        L.arg_tile0[i] = static_cast<int32_t>(lp.tile0[size_t(i)]);
-    }
-    L.arg_tile0[L.n_args] = static_cast<int32_t>(lp.tiles);
+    ListLaunch L = list_base(P, src, lt);
+    L.n_args = static_cast<int32_t>(lt.count);
+    for_each_entry(P, ids, n, outs,
+                   [&](int64_t e, int32_t id, void* out, int64_t tile0, int64_t) {
+                       const size_t t = size_t(id);
+                       L.args[e] = ArgEntry{out, P->shard_off[t], P->shard_len[t], P->numel[t]};
+                       L.arg_tile0[e] = static_cast<int32_t>(tile0);
+                   });
+    L.arg_tile0[L.n_args] = static_cast<int32_t>(lt.tiles);
     return launch_list(L, src, stream);
 }
+
+namespace {
+
+// Writes the staged upload into one contiguous host buffer.
+struct EntSink {
+    ListEntry* p;
+    void put(int64_t e, const ListEntry& v) { p[e] = v; }
+};
+struct CoarseSink {
+    int32_t* p;
+    void put(int64_t c, int32_t v) { p[c] = v; }
+};
+
+}  // namespace
 
 }  // namespace zsp
 
 extern "C" zsp_status zsp_gather_many(zsp_plan* P, const int32_t* ids, int32_t n,
                                       zsp_source src, void* const* outs, void* stream) {
     using namespace zsp;
-    ListPlan lp;
-    zsp_status st = check_list(P, ids, n, src, outs, &lp);
+    ListTotals lt;
+    zsp_status st = check_list(P, ids, n, src, outs, &lt);
     if (st != ZSP_OK) return st;
     const hipStream_t hs = static_cast<hipStream_t>(stream);
-    if (lp.tiles == 0) return ZSP_OK;
-    if (lp.id.size() <= size_t(kListArgMax)) return gather_list_args(P, src, lp, hs);
+    if (lt.tiles == 0) return ZSP_OK;
+    if (lt.count <= kListArgMax) return gather_list_args(P, ids, n, outs, src, lt, hs);
 
     ListStaging& ls = *P->lists;  // made by the all-rank bind check_list asked for
     std::lock_guard<std::mutex> lock(ls.mu);
@@ -214,7 +185,7 @@ extern "C" zsp_status zsp_gather_many(zsp_plan* P, const int32_t* ids, int32_t n
     }
     if (!s.done && (e = hipEventCreateWithFlags(&s.done, hipEventDisableTiming)) != hipSuccess)
         return set_hip_error(e, "hipEventCreate");
-    const StagedSizes z = staged_sizes(lp, kRecChunk);
+    const StagedSizes z = staged_sizes(lt, kRecChunk);
     const size_t up = z.ents + z.coarse;
     if (s.host_cap < up) {
         if (s.host) (void)hipHostFree(s.host);
@@ -234,15 +205,17 @@ extern "C" zsp_status zsp_gather_many(zsp_plan* P, const int32_t* ids, int32_t n
                              hipGetErrorString(e));
         s.dev_cap = up + z.recs;
     }
-    pack_staged(lp, static_cast<char*>(s.host), z);
-    ListLaunch L = list_base(P, src, lp);
+    char* h = static_cast<char*>(s.host);
+    EntSink es{reinterpret_cast<ListEntry*>(h)};
+    CoarseSink cs{reinterpret_cast<int32_t*>(h + z.ents)};
+    emit_staged(P, ids, n, outs, es, cs);
+    ListLaunch L = list_base(P, src, lt);
     char* d = static_cast<char*>(s.dev);
     L.ents = reinterpret_cast<const ListEntry*>(d);
-    L.n_ents = static_cast<int32_t>(lp.id.size());
+    L.n_ents = static_cast<int32_t>(lt.count);
     L.coarse = reinterpret_cast<const int32_t*>(d + z.ents);
     L.recs = reinterpret_cast<TileRec*>(d + up);
     L.rec_cap = z.rec_tiles;
-    st = ZSP_OK;
     if ((e = hipMemcpyAsync(s.dev, s.host, up, hipMemcpyHostToDevice, hs)) != hipSuccess)
         st = set_hip_error(e, "staging copy");
     else
