@@ -274,6 +274,24 @@ zsp_status zsp_gather_range(zsp_plan* plan, int32_t first_param, int32_t n_param
 zsp_status zsp_gather_many(zsp_plan* plan, const int32_t* ids, int32_t n, zsp_source src,
                            void* const* outs, void* stream);
 
+/* zsp_gather_many for callers that cannot allocate (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same
+ * arguments, checks and results, but nothing is allocated, on the device
+ * or the host. A long list (more than 64 non-empty parameters) is staged
+ * in a fixed device array the library holds on every GPU it runs on from
+ * load to process end (9.25 MiB): its entries and coarse index are copied
+ * there from a static host buffer, then the same two kernels run. Limits:
+ * at most 65536 non-empty parameters and 2^22 tiles of 512 elements (2^31
+ * elements) per call, else ZSP_ERANGE; longer lists than 2^18 tiles run in
+ * several pairs of launches. The array keeps the last call's contents and
+ * every call on a GPU shares it: calls on one stream run in order, but
+ * calls that overlap on one GPU (other streams or threads) race. The array's
+ * address is taken at an all-rank zsp_bind_state (or the first call) on
+ * each device. Lists of at most 64 non-empty parameters touch no staging
+ * at all, as in zsp_gather_many. */
+zsp_status zsp_gather_many_noalloc(zsp_plan* plan, const int32_t* ids, int32_t n,
+                                   zsp_source src, void* const* outs, void* stream);
+
 /* ---- Per-layer gather schedule with prefetch ------------------------------
  * [ZS3] on-demand fetch list (gather layer l before its computation, discard
  * after) and prefetch paragraph (gather layer l+1 while layer l computes);

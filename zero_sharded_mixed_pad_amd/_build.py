@@ -18,7 +18,7 @@ LIB = os.path.join(HERE, "libzsp.so")
 
 ARCH = "gfx950"
 SOURCES = ["zsp_kernels.hip", "zsp_capi.cpp", "zsp_layout.cpp", "zsp_gather_list.cpp",
-           "zsp_ckpt.cpp", "zsp_ckpt_dev.cpp", "zsp_sched.cpp"]
+           "zsp_noalloc.hip", "zsp_ckpt.cpp", "zsp_ckpt_dev.cpp", "zsp_sched.cpp"]
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
     "-ffp-contract=off",

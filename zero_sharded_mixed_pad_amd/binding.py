@@ -58,6 +58,7 @@ def _load():
         "zsp_gather": (i32, [vp, i32, i32, vp, vp]),
         "zsp_gather_range": (i32, [vp, i32, i32, i32, vp, vp]),
         "zsp_gather_many": (i32, [vp, i32p, i32, i32, vpp, vp]),
+        "zsp_gather_many_noalloc": (i32, [vp, i32p, i32, i32, vpp, vp]),
         "zsp_checkpoint_write_host": (i32, [vp, i32, ctypes.c_char_p, i64, vp, vp, vp, vp]),
         "zsp_checkpoint_read_host": (i32, [vp, i32, ctypes.c_char_p, i64p, vp, vp, vp, vp]),
         "zsp_checkpoint_save": (i32, [vp, i32, ctypes.c_char_p, i64, vp]),
@@ -251,6 +252,13 @@ def zsp_gather_many(h, ids, outs, source="work", stream=None):
     dt = torch.bfloat16 if src == SRC_WORK else torch.float32
     ids_c, outs_c, n = _list_arrays(ids, outs, dt)
     _check(lib.zsp_gather_many(h, ids_c, n, src, outs_c, _stream(stream)))
+
+
+def zsp_gather_many_noalloc(h, ids, outs, source="work", stream=None):
+    src = _SOURCES[source]
+    dt = torch.bfloat16 if src == SRC_WORK else torch.float32
+    ids_c, outs_c, n = _list_arrays(ids, outs, dt)
+    _check(lib.zsp_gather_many_noalloc(h, ids_c, n, src, outs_c, _stream(stream)))
 
 
 class GatherList:
@@ -531,6 +539,14 @@ class Plan:
             if 0 <= t < len(self.numel):
                 _need(o, self.numel[t], f"outs[{i}]")
         zsp_gather_many(self._h, ids, outs, source, stream)
+
+    def gather_many_noalloc(self, ids, outs, source="work", stream=None):
+        """gather_many staged through the library's fixed device array:
+        allocates nothing."""
+        for i, (t, o) in enumerate(zip(ids, outs)):
+            if 0 <= t < len(self.numel):
+                _need(o, self.numel[t], f"outs[{i}]")
+        zsp_gather_many_noalloc(self._h, ids, outs, source, stream)
 
     def gather_list(self, ids, outs, source="work"):
         """A GatherList for this plan's parameters (sizes checked once);

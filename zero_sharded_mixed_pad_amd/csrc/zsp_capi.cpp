@@ -328,6 +328,14 @@ zsp_status zsp_bind_state(zsp_plan* P, int32_t rank_or_all, float* master, float
             return fail(ZSP_ENOMEM, "out of host memory");
         }
     }
+    if (rank_or_all == ZSP_ALL_RANKS) {
+        // the no-alloc list gather's device array, located on this device now
+        const zsp_status st = zsp::noalloc_setup();
+        if (st != ZSP_OK) {
+            if (blob) (void)hipFree(blob);
+            return st;
+        }
+    }
     char* b = static_cast<char*>(blob);
     P->dev_blob = blob;
     P->shard.e0 = reinterpret_cast<const int64_t*>(b + off[0]);

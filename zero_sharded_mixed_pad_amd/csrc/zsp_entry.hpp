@@ -17,6 +17,10 @@ zsp_status set_hip_error(hipError_t e, const char* what);
 // ZSP_OK if the plan has state bound on the current device, else the error.
 zsp_status check_bound(const zsp_plan* P);
 
+// Locates the no-alloc list gather's static device array on the current
+// device (zsp_noalloc.hip); ZSP_OK once done.
+zsp_status noalloc_setup();
+
 // zsp_gather_range on a HIP stream (argument checks, then one launch).
 zsp_status gather_range(zsp_plan* P, int32_t first_param, int32_t n_params, zsp_source src,
                         void* out, hipStream_t stream);
