@@ -92,15 +92,21 @@ __device__ __forceinline__ uint16_t to_bf16(float a) {
 }
 
 // 4 consecutive elements of a bf16 or fp32 source at base[off], any element
-// offset.
-template <typename GT>
+// offset; non-temporal unless TG (an ordinary, L2-allocating load).
+template <typename GT, bool TG = false>
 __device__ __forceinline__ void load4(const GT* base, uint32_t off, float (&x)[4]) {
     if constexpr (std::is_same<GT, uint16_t>::value) {
-        const u32x2 u = ldnt_x2_a2(reinterpret_cast<const u32x2_a2*>(base + off));
+        const u32x2_a2* p = reinterpret_cast<const u32x2_a2*>(base + off);
+        u32x2 u;
+        if constexpr (TG) u = *p;
+        else u = ldnt_x2_a2(p);
         x[0] = bf_lo(u.x); x[1] = bf_hi(u.x);
         x[2] = bf_lo(u.y); x[3] = bf_hi(u.y);
     } else {
-        const u32x4 u = ldnt_x4_a4(reinterpret_cast<const u32x4_a4*>(base + off));
+        const u32x4_a4* p = reinterpret_cast<const u32x4_a4*>(base + off);
+        u32x4 u;
+        if constexpr (TG) u = *p;
+        else u = ldnt_x4_a4(p);
         x[0] = __uint_as_float(u.x); x[1] = __uint_as_float(u.y);
         x[2] = __uint_as_float(u.z); x[3] = __uint_as_float(u.w);
     }
@@ -183,8 +189,9 @@ constexpr bool is_adam(int op) { return op == OP_FUSED || op == OP_FUSED_ACC || 
 // Sum over the N_d ranks, in rank order, of NQ quads per lane; quad h of
 // rank r starts at element base[h] + off[h] of grads[r]. When base[] is
 // wave-uniform the address is a scalar base plus a 32-bit lane offset. A
-// batch's loads are all issued before its adds.
-template <typename GT, int CAP, int NQ>
+// batch's loads are all issued before its adds. TG: ordinary loads (see
+// shard_kernel).
+template <typename GT, int CAP, int NQ, bool TG>
 __device__ __forceinline__ void reduce_quads(const ShardArgs<CAP>& a, const int64_t (&base)[NQ],
                                              const uint32_t (&off)[NQ],
                                              float (&g)[NQ][kQuad]) {
@@ -200,7 +207,8 @@ __device__ __forceinline__ void reduce_quads(const ShardArgs<CAP>& a, const int6
         for (int q = 0; q < B; ++q)
 #pragma unroll
             for (int h = 0; h < NQ; ++h)
-                load4<GT>(static_cast<const GT*>(grad_ptr<CAP>(r0 + q)) + base[h], off[h], x[q][h]);
+                load4<GT, TG>(static_cast<const GT*>(grad_ptr<CAP>(r0 + q)) + base[h], off[h],
+                              x[q][h]);
 #pragma unroll
         for (int q = 0; q < B; ++q) {
             const bool first = (r0 + q) == 0;
@@ -218,7 +226,7 @@ __device__ __forceinline__ void reduce_quads(const ShardArgs<CAP>& a, const int6
         for (int q = 0; q < B; ++q)
 #pragma unroll
             for (int h = 0; h < NQ; ++h)
-                load4<GT>(static_cast<const GT*>(grad_ptr<CAP>(min(r0 + q, nd - 1))) + base[h],
+                load4<GT, TG>(static_cast<const GT*>(grad_ptr<CAP>(min(r0 + q, nd - 1))) + base[h],
                           off[h], x[q][h]);
 #pragma unroll
         for (int q = 0; q < B; ++q) {
@@ -256,7 +264,7 @@ __device__ __forceinline__ float reduce1(const ShardArgs<CAP>& a, int64_t sidx) 
 // ib[h] + off[h]. Eb[h] + off[h] is a multiple of 4, so every state access is
 // an aligned 16-byte vector. With wave-uniform Eb/gb/ib (a tile inside one
 // piece) every address is a scalar base plus the lane's 32-bit offset.
-template <int OP, typename GT, int CAP, int NQ>
+template <int OP, typename GT, int CAP, int NQ, bool TG>
 __device__ __forceinline__ void quads_fast(const ShardArgs<CAP>& a, const int64_t (&Eb)[NQ],
                                            const int64_t (&gb)[NQ], const int64_t (&ib)[NQ],
                                            const uint32_t (&off)[NQ]) {
@@ -292,7 +300,7 @@ __device__ __forceinline__ void quads_fast(const ShardArgs<CAP>& a, const int64_
             for (int h = 0; h < NQ; ++h) ld_f32x4(a.acc + Eb[h] + off[h], c[h]);
         }
         if constexpr (uses_grads(OP)) {
-            reduce_quads<GT, CAP, NQ>(a, gb, off, g);
+            reduce_quads<GT, CAP, NQ, TG>(a, gb, off, g);
         }
 #pragma unroll
         for (int h = 0; h < NQ; ++h) {
@@ -517,7 +525,7 @@ __device__ __forceinline__ void quad_mixed(const ShardArgs<CAP>& a, int64_t E, i
 }
 
 // One quad of any kind; p is the index of its piece in `info`.
-template <int OP, typename GT, int CAP>
+template <int OP, typename GT, int CAP, bool TG>
 __device__ __forceinline__ void quad_one(const ShardArgs<CAP>& a, int64_t E, int kind, int p,
                                          PieceInfo pi, const PieceInfo* info) {
     if (kind == Q_FAST) {
@@ -525,7 +533,7 @@ __device__ __forceinline__ void quad_one(const ShardArgs<CAP>& a, int64_t E, int
         const int64_t gb[1] = {a.shard_layout ? E : E + pi.gdelta};
         const int64_t ib[1] = {E + pi.idelta};
         const uint32_t off[1] = {0u};
-        quads_fast<OP, GT, CAP, 1>(a, Eb, gb, ib, off);
+        quads_fast<OP, GT, CAP, 1, TG>(a, Eb, gb, ib, off);
     } else if (kind == Q_PAD) {
         quad_pad<OP, CAP>(a, E);
     } else if (kind == Q_MIXED) {
@@ -544,7 +552,11 @@ __device__ __forceinline__ void quad_one(const ShardArgs<CAP>& a, int64_t E, int
 
 // W waves per tile: W = 1, the wave takes both quads of each lane; W = 2,
 // workgroup 2i + h takes quad h (elements 256h .. 256h + 255) of tile i.
-template <int OP, typename GT, int CAP, int W>
+// TG: the gradients are read with ordinary (L2-allocating) loads instead of
+// non-temporal ones. Launches over short pieces use it: there a tile's
+// gradient runs start mid-line, and the line a run shares with the next
+// tile's run can then still be in L2 when that tile reads it.
+template <int OP, typename GT, int CAP, int W, bool TG>
 __global__ __launch_bounds__(kWaveLanes) void shard_kernel(const ShardArgs<CAP> a) {
     static_assert(W == 1 || W == 2, "one or two waves per tile");
     __shared__ int64_t s_e0[kStage];
@@ -569,13 +581,13 @@ __global__ __launch_bounds__(kWaveLanes) void shard_kernel(const ShardArgs<CAP> 
                 const int64_t gb[1] = {gbase};
                 const int64_t ib[1] = {T0 + pi.idelta};
                 const uint32_t off[1] = {uint32_t(lane) * kQuad + uint32_t(hw) * uint32_t(kHalf)};
-                quads_fast<OP, GT, CAP, 1>(a, Eb, gb, ib, off);
+                quads_fast<OP, GT, CAP, 1, TG>(a, Eb, gb, ib, off);
             } else {
                 const int64_t Eb[2] = {T0, T0};
                 const int64_t gb[2] = {gbase, gbase};
                 const int64_t ib[2] = {T0 + pi.idelta, T0 + pi.idelta};
                 const uint32_t off[2] = {uint32_t(lane) * kQuad, uint32_t(lane) * kQuad + kHalf};
-                quads_fast<OP, GT, CAP, 2>(a, Eb, gb, ib, off);
+                quads_fast<OP, GT, CAP, 2, TG>(a, Eb, gb, ib, off);
             }
             return;
         }
@@ -602,7 +614,7 @@ __global__ __launch_bounds__(kWaveLanes) void shard_kernel(const ShardArgs<CAP> 
         const int64_t E = E0 + h * kHalf;
         const int p = n == 1 ? 0 : find_local(e0, n, E);
         const PieceInfo pi = info[p];
-        quad_one<OP, GT, CAP>(a, E, classify(a, E, pi), p, pi, info);
+        quad_one<OP, GT, CAP, TG>(a, E, classify(a, E, pi), p, pi, info);
     }
 }
 
@@ -1089,6 +1101,12 @@ size_t shard_lds_pad(const ShardLaunch& L, int64_t tiles) {
 template <int OP, int CAP>
 constexpr bool kHalfTiles = CAP <= 16 && OP != OP_COPYIN;
 
+// Ordinary gradient loads (TG) for launches over short pieces that read
+// gradients, up to 16 ranks: 5656-5660 against 5494-5500 GB/s on the
+// 10,000-tensor fused step (three alternating runs on one MI355X).
+template <int OP, int CAP>
+constexpr bool kTemporalShort = CAP <= 16 && uses_grads(OP);
+
 // A launch's work-items (workgroups x 64) must fit in 32 bits.
 constexpr int64_t kMaxBlocks = int64_t(UINT32_MAX) / kWaveLanes;
 
@@ -1119,7 +1137,7 @@ hipError_t launch_t(const ShardLaunch& L, hipStream_t stream) {
     if constexpr (kHalfTiles<OP, CAP>) {
         if (!L.short_pieces && 2 * tiles <= kMaxBlocks) {
             const size_t lds_pad = shard_lds_pad<OP, GT, CAP, 2>(L, tiles);
-            hipLaunchKernelGGL((shard_kernel<OP, GT, CAP, 2>),
+            hipLaunchKernelGGL((shard_kernel<OP, GT, CAP, 2, false>),
                                dim3(static_cast<uint32_t>(2 * tiles)), dim3(kWaveLanes), lds_pad,
                                stream, a);
             return hipGetLastError();
@@ -1127,7 +1145,15 @@ hipError_t launch_t(const ShardLaunch& L, hipStream_t stream) {
     }
     if (tiles > kMaxBlocks) return hipErrorInvalidValue;
     const size_t lds_pad = shard_lds_pad<OP, GT, CAP, 1>(L, tiles);
-    hipLaunchKernelGGL((shard_kernel<OP, GT, CAP, 1>), dim3(static_cast<uint32_t>(tiles)),
+    if constexpr (kTemporalShort<OP, CAP>) {
+        if (L.short_pieces) {
+            hipLaunchKernelGGL((shard_kernel<OP, GT, CAP, 1, true>),
+                               dim3(static_cast<uint32_t>(tiles)), dim3(kWaveLanes), lds_pad,
+                               stream, a);
+            return hipGetLastError();
+        }
+    }
+    hipLaunchKernelGGL((shard_kernel<OP, GT, CAP, 1, false>), dim3(static_cast<uint32_t>(tiles)),
                        dim3(kWaveLanes), lds_pad, stream, a);
     return hipGetLastError();
 }
