@@ -54,9 +54,9 @@ static float load_as_f32(const void* base, int64_t idx, int32_t dtype) {
 /* Layout ([ZD] section 2; [ZST] "What stage 1 partitions")            */
 /* ------------------------------------------------------------------ */
 
-/* [ZD] section 2: the flattened parameter is padded when its element count
- * does not divide evenly across the data-parallel group. The pad is the
- * smallest count that makes it divide: zero when it already does. */
+/* [ZD] section 2: padding makes a flattened parameter's length a multiple of
+ * the rank count; the pad is the smallest number of elements that does so,
+ * zero when the length already is a multiple. */
 int64_t orc_pad(int64_t numel, int32_t nd) {
     int64_t rem = numel % nd;
     return rem == 0 ? 0 : (int64_t)nd - rem;
@@ -242,8 +242,8 @@ void orc_reduce_values(int64_t n, int32_t nd, const void* vals, int32_t dtype,
     free(row);
 }
 
-/* [ZST] "Stage 2 also partitions gradients": reduce per micro-batch and
- * accumulate the reduced slices. */
+/* [ZST] "Stage 2 also partitions gradients": with several micro-batches,
+ * each one's reduced shard is added into a running shard-sized sum. */
 void orc_accumulate(int64_t n, float* acc, const float* g) {
     for (int64_t i = 0; i < n; ++i) acc[i] = acc[i] + g[i];
 }

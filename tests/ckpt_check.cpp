@@ -1,8 +1,9 @@
 // Host driver for the checkpoint file module (zsp_ckpt.cpp), built with g++
 // and AddressSanitizer / UBSan by tests/test_ckpt_sanitized.py. It writes rank
-// files, checks and maps them, then feeds the reader truncated, bit-flipped
+// files, maps and checks them, then feeds the reader truncated, bit-flipped
 // and hostile files: every one must be refused with an error status, and
-// nothing may read or allocate out of bounds. Prints "ok" at the end.
+// nothing may read or allocate out of bounds. A file replaced by rename after
+// its check must not change what the mapping reads. Prints "ok" at the end.
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
@@ -39,10 +40,9 @@ static void spill(const std::string& p, const char* data, size_t n) {
 
 static CkptStatus verify(const std::string& dir, int nd, int r, std::vector<int64_t>* numel,
                          int64_t* S, int64_t* step) {
-    std::vector<char> scratch(1000);  // small, so the payload loop runs many times
+    MappedRank m;
     std::string err;
-    return ckpt_verify_rank(dir.c_str(), nd, r, numel, S, step, scratch.data(), scratch.size(),
-                            &err);
+    return m.open(dir.c_str(), nd, r, numel, S, step, &err);
 }
 
 int main(int argc, char** argv) {
@@ -74,18 +74,14 @@ int main(int argc, char** argv) {
     for (int r = 0; r < nd; ++r) {
         std::vector<int64_t> got;
         int64_t s = -1, step = -1;
-        EXPECT(verify(dir, nd, r, &got, &s, &step) == CkptStatus::Ok);
-        EXPECT(got == numel && s == S && step == 42);
         MappedRank m;
         std::string err;
-        EXPECT(m.map(dir.c_str(), nd, r, int64_t(numel.size()), S, &err) == CkptStatus::Ok);
+        EXPECT(m.open(dir.c_str(), nd, r, &got, &s, &step, &err) == CkptStatus::Ok);
+        EXPECT(got == numel && s == S && step == 42);
         EXPECT(std::memcmp(m.master(), ma[r].data(), size_t(S) * 4) == 0);
         EXPECT(std::memcmp(m.m(), mm[r].data(), size_t(S) * 4) == 0);
         EXPECT(std::memcmp(m.v(), mv[r].data(), size_t(S) * 4) == 0);
         EXPECT(std::memcmp(m.work(), mw[r].data(), size_t(S) * 2) == 0);
-        MappedRank wrong;  // a layout the file does not have
-        EXPECT(wrong.map(dir.c_str(), nd, r, int64_t(numel.size()), S + 1, &err) ==
-               CkptStatus::Corrupt);
     }
 
     // damaged copies of rank 1
@@ -125,6 +121,20 @@ int main(int argc, char** argv) {
     std::remove(p1.c_str());
     EXPECT(verify(dir, nd, 1, &got, &s, &step) == CkptStatus::Missing);
     spill(p1, good.data(), len);
+
+    // a file renamed over the mapped one after its check leaves the mapping,
+    // and the payload read from it, as checked
+    {
+        std::vector<int64_t> g2;
+        int64_t s2 = 0, st2 = 0;
+        MappedRank m;
+        std::string err;
+        EXPECT(m.open(dir.c_str(), nd, 2, &g2, &s2, &st2, &err) == CkptStatus::Ok);
+        HostPayload src(ma[3].data(), mm[3].data(), mv[3].data(), mw[3].data(), S);
+        EXPECT(ckpt_write_rank(dir.c_str(), nd, 2, numel, S, 43, src, &err) == CkptStatus::Ok);
+        EXPECT(std::memcmp(m.master(), ma[2].data(), size_t(S) * 4) == 0);
+        EXPECT(std::memcmp(m.work(), mw[2].data(), size_t(S) * 2) == 0);
+    }
 
     // directory scans: junk names are ignored, two rank counts are refused
     spill(dir + "/rank-x-of-4.zsp", "", 0);

@@ -138,76 +138,6 @@ struct Writer {
     }
 };
 
-struct Reader {
-    FILE* f = nullptr;
-    Xxh64 hash;
-    bool ok = true;
-    void get(void* p, size_t n) {
-        if (!ok || n == 0) return;
-        ok = std::fread(p, 1, n, f) == n;
-        if (ok) hash.add(p, n);
-    }
-};
-
-// Open rank `rank`'s file and read its header and numel list.
-CkptStatus open_and_read_header(const char* dir, int32_t nd, int32_t rank, Reader* r,
-                                std::vector<int64_t>* numel, int64_t* S, int64_t* step,
-                                std::string* path, std::string* err) {
-    *path = rank_path(dir, rank, nd);
-    r->f = std::fopen(path->c_str(), "rb");
-    if (!r->f) {
-        *err = "cannot open " + *path + ": " + std::strerror(errno);
-        return CkptStatus::Missing;
-    }
-    struct stat sb;
-    const bool sized = fstat(fileno(r->f), &sb) == 0;
-    char magic[8];
-    int64_t hdr[5];
-    r->get(magic, sizeof(magic));
-    r->get(hdr, sizeof(hdr));
-    if (!sized || !r->ok || std::memcmp(magic, kMagic, 8) != 0 || hdr[0] != nd ||
-        hdr[1] != rank || hdr[2] < 1 || hdr[2] > (int64_t(1) << 31) || hdr[3] < 0 ||
-        hdr[3] > (int64_t(1) << 40)) {
-        std::fclose(r->f);
-        r->f = nullptr;
-        *err = *path + ": not a shard file of rank " + std::to_string(rank) + " of " +
-               std::to_string(nd);
-        return CkptStatus::Corrupt;
-    }
-    // The header fixes the file's length; check it before sizing anything
-    // from the header (the bounds above keep this sum far from overflow).
-    const int64_t want = int64_t(sizeof(kMagic)) + int64_t(sizeof(hdr)) + 8 * hdr[2] +
-                         ckpt_payload_bytes(hdr[3]) + int64_t(sizeof(uint64_t));
-    if (int64_t(sb.st_size) != want) {
-        std::fclose(r->f);
-        r->f = nullptr;
-        *err = *path + ": truncated or corrupt (" + std::to_string(sb.st_size) +
-               " bytes, its header needs " + std::to_string(want) + ")";
-        return CkptStatus::Corrupt;
-    }
-    numel->resize(size_t(hdr[2]));
-    r->get(numel->data(), numel->size() * sizeof(int64_t));
-    *S = hdr[3];
-    *step = hdr[4];
-    return CkptStatus::Ok;
-}
-
-// After the payload: the stored checksum must match and end the file.
-CkptStatus finish_read(Reader* r, const std::string& path, std::string* err) {
-    const uint64_t want = r->hash.digest();
-    uint64_t got = 0;
-    const bool tail_ok = r->ok && std::fread(&got, 1, sizeof(got), r->f) == sizeof(got);
-    char extra;
-    const bool at_end = std::fread(&extra, 1, 1, r->f) == 0;
-    std::fclose(r->f);
-    r->f = nullptr;
-    if (!tail_ok || got != want || !at_end) {
-        *err = path + ": truncated or corrupt (hash mismatch)";
-        return CkptStatus::Corrupt;
-    }
-    return CkptStatus::Ok;
-}
-
 }  // namespace
 
 HostPayload::HostPayload(const float* master, const float* m, const float* v,
@@ -276,52 +206,72 @@ CkptStatus ckpt_write_rank(const char* dir, int32_t nd, int32_t rank,
     return CkptStatus::Ok;
 }
 
-CkptStatus ckpt_verify_rank(const char* dir, int32_t nd, int32_t rank,
-                            std::vector<int64_t>* numel, int64_t* S, int64_t* step,
-                            void* scratch, size_t scratch_bytes, std::string* err) {
-    Reader r;
-    std::string path;
-    CkptStatus st = open_and_read_header(dir, nd, rank, &r, numel, S, step, &path, err);
-    if (st != CkptStatus::Ok) return st;
-    int64_t left = ckpt_payload_bytes(*S);
-    while (left > 0 && r.ok) {
-        const size_t n = size_t(std::min<int64_t>(left, int64_t(scratch_bytes)));
-        r.get(scratch, n);
-        left -= int64_t(n);
-    }
-    return finish_read(&r, path, err);
-}
-
 MappedRank::~MappedRank() {
     if (base_) munmap(base_, len_);
 }
 
-CkptStatus MappedRank::map(const char* dir, int32_t nd, int32_t rank, int64_t T, int64_t S,
-                           std::string* err) {
+CkptStatus MappedRank::open(const char* dir, int32_t nd, int32_t rank,
+                            std::vector<int64_t>* numel, int64_t* S, int64_t* step,
+                            std::string* err) {
     const std::string path = rank_path(dir, rank, nd);
-    const size_t head = sizeof(kMagic) + 5 * sizeof(int64_t) + size_t(T) * sizeof(int64_t);
-    const size_t want = head + size_t(ckpt_payload_bytes(S)) + sizeof(uint64_t);
-    const int fd = open(path.c_str(), O_RDONLY);
+    const int fd = ::open(path.c_str(), O_RDONLY);
     if (fd < 0) {
         *err = "cannot open " + path + ": " + std::strerror(errno);
         return CkptStatus::Missing;
     }
     struct stat sb;
-    if (fstat(fd, &sb) != 0 || size_t(sb.st_size) != want) {
+    if (fstat(fd, &sb) != 0) {
+        *err = "cannot stat " + path + ": " + std::strerror(errno);
         close(fd);
-        *err = path + ": changed since it was checked";
+        return CkptStatus::Io;
+    }
+    int64_t hdr[5];
+    const size_t head0 = sizeof(kMagic) + sizeof(hdr);
+    if (sb.st_size < int64_t(head0 + sizeof(uint64_t))) {
+        close(fd);
+        *err = path + ": truncated (" + std::to_string(sb.st_size) + " bytes)";
         return CkptStatus::Corrupt;
     }
-    void* p = mmap(nullptr, want, PROT_READ, MAP_PRIVATE, fd, 0);
+    const size_t size = size_t(sb.st_size);
+    void* p = mmap(nullptr, size, PROT_READ, MAP_PRIVATE, fd, 0);
     close(fd);
     if (p == MAP_FAILED) {
         *err = "cannot map " + path + ": " + std::strerror(errno);
         return CkptStatus::Io;
     }
-    base_ = p;
-    len_ = want;
-    payload_ = static_cast<const char*>(p) + head;
-    S_ = S;
+    base_ = p;  // unmapped by the destructor, also after a failed check below
+    len_ = size;
+    const char* b = static_cast<const char*>(p);
+    std::memcpy(hdr, b + sizeof(kMagic), sizeof(hdr));
+    if (std::memcmp(b, kMagic, sizeof(kMagic)) != 0 || hdr[0] != nd || hdr[1] != rank ||
+        hdr[2] < 1 || hdr[2] > (int64_t(1) << 31) || hdr[3] < 0 || hdr[3] > (int64_t(1) << 40)) {
+        *err = path + ": not a shard file of rank " + std::to_string(rank) + " of " +
+               std::to_string(nd);
+        return CkptStatus::Corrupt;
+    }
+    // The header fixes the file's length (the bounds above keep this sum far
+    // from overflow); only then is anything sized from it.
+    const int64_t want = int64_t(head0) + 8 * hdr[2] + ckpt_payload_bytes(hdr[3]) +
+                         int64_t(sizeof(uint64_t));
+    if (int64_t(size) != want) {
+        *err = path + ": truncated or corrupt (" + std::to_string(size) +
+               " bytes, its header needs " + std::to_string(want) + ")";
+        return CkptStatus::Corrupt;
+    }
+    Xxh64 hash;
+    hash.add(b, size - sizeof(uint64_t));
+    uint64_t stored = 0;
+    std::memcpy(&stored, b + size - sizeof(uint64_t), sizeof(stored));
+    if (hash.digest() != stored) {
+        *err = path + ": corrupt (hash mismatch)";
+        return CkptStatus::Corrupt;
+    }
+    numel->resize(size_t(hdr[2]));
+    std::memcpy(numel->data(), b + head0, numel->size() * sizeof(int64_t));
+    *S = hdr[3];
+    *step = hdr[4];
+    payload_ = b + head0 + numel->size() * sizeof(int64_t);
+    S_ = hdr[3];
     return CkptStatus::Ok;
 }
 

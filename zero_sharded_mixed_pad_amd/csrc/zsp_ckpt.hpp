@@ -1,8 +1,8 @@
 // zsp_ckpt.hpp -- per-rank shard files of a sharded checkpoint (format in
 // zsp_ckpt.cpp): writing one rank's file from a payload passed chunk by
-// chunk (so callers can stage it while the file side runs), checking a file
-// whole, and mapping a checked file to read its payload in place. Host
-// only; no HIP here.
+// chunk (so callers can stage it while the file side runs), and mapping a
+// file, checking it whole on the mapping and reading its payload in place.
+// Host only; no HIP here.
 #pragma once
 
 #include <cstddef>
@@ -45,24 +45,19 @@ CkptStatus ckpt_write_rank(const char* dir, int32_t nd, int32_t rank,
                            const std::vector<int64_t>& numel, int64_t S, int64_t step,
                            PayloadSource& src, std::string* err);
 
-// Read rank `rank`'s file whole through `scratch`, checking magic, header,
-// length, checksum and that nothing follows it; returns the header's numel
-// list, S and step.
-CkptStatus ckpt_verify_rank(const char* dir, int32_t nd, int32_t rank,
-                            std::vector<int64_t>* numel, int64_t* S, int64_t* step,
-                            void* scratch, size_t scratch_bytes, std::string* err);
-
-// Rank `rank`'s file mapped read-only, for reading its payload in place
-// after ckpt_verify_rank has checked it: map() checks only that the file has
-// the length a T-parameter, S-element file has.
+// Rank `rank`'s file mapped read-only and checked whole on that one mapping:
+// magic, header, length and the checksum over the mapped bytes. The payload
+// read afterwards is the one the checksum covered (a file renamed into
+// place meanwhile, e.g. by another save, does not replace the mapped one).
+// open() returns the header's numel list, S and step.
 class MappedRank {
   public:
     MappedRank() = default;
     MappedRank(const MappedRank&) = delete;
     MappedRank& operator=(const MappedRank&) = delete;
     ~MappedRank();
-    CkptStatus map(const char* dir, int32_t nd, int32_t rank, int64_t T, int64_t S,
-                   std::string* err);
+    CkptStatus open(const char* dir, int32_t nd, int32_t rank, std::vector<int64_t>* numel,
+                    int64_t* S, int64_t* step, std::string* err);
     // master, m, v (fp32) and work (bf16 bits) of the payload
     const float* master() const { return reinterpret_cast<const float*>(payload_); }
     const float* m() const { return master() + S_; }

@@ -302,7 +302,6 @@ class DevSink {
 
 // ---- rank layouts and resharding -------------------------------------------
 
-constexpr size_t kVerifyChunk = size_t(8) << 20;  // read buffer of a verify pass
 
 struct RankLayout {
     std::vector<int64_t> shard_len, shard_off;
@@ -327,9 +326,10 @@ bool same_model(const zsp_plan* P, const std::vector<int64_t>& numel, int64_t S,
     return numel == P->numel && S == S_want;
 }
 
-// The files of a checkpoint that a load needs: checked whole (one lane per
-// file), then mapped read-only, so that the plan's shards are cut from the
-// page cache without another copy. Under the plan's own rank count a shard
+// The files of a checkpoint that a load needs: each mapped read-only once and
+// checked whole on that mapping (one lane per file), so that the plan's
+// shards are cut from the page cache, from exactly the bytes the checksum
+// covered, without another copy. Under the plan's own rank count a shard
 // is one old file's payload; under another, it takes runs of every file.
 struct OldCheckpoint {
     int32_t nd = 0;
@@ -354,17 +354,19 @@ zsp_status open_old(const zsp_plan* P, const char* dir, int32_t nd_old,
     }
     const int n = int(need.size());
     std::vector<int64_t> steps(size_t(n), 0);
+    std::vector<std::unique_ptr<MappedRank>> opened(static_cast<size_t>(n));
     zsp_status st = run_lanes(n, kLanes, -1, [&](int i, int, std::string* m) {
-        std::unique_ptr<char[]> scratch(new char[kVerifyChunk]);
+        std::unique_ptr<MappedRank> f(new MappedRank);
         std::vector<int64_t> numel;
         int64_t S = 0;
-        if (ckpt_verify_rank(dir, nd_old, need[size_t(i)], &numel, &S, &steps[size_t(i)],
-                             scratch.get(), kVerifyChunk, m) != CkptStatus::Ok)
+        if (f->open(dir, nd_old, need[size_t(i)], &numel, &S, &steps[size_t(i)], m) !=
+            CkptStatus::Ok)
             return ZSP_EIO;
         if (!same_model(P, numel, S, old->L.S)) {
             *m = std::string("checkpoint in ") + dir + " holds another parameter list";
             return ZSP_EIO;
         }
+        opened[size_t(i)] = std::move(f);
         return ZSP_OK;
     });
     if (st != ZSP_OK) return st;
@@ -378,16 +380,14 @@ zsp_status open_old(const zsp_plan* P, const char* dir, int32_t nd_old,
     old->m.assign(size_t(nd_old), nullptr);
     old->v.assign(size_t(nd_old), nullptr);
     old->work.assign(size_t(nd_old), nullptr);
-    for (int32_t r : need) {
-        std::unique_ptr<MappedRank> f(new MappedRank);
-        std::string err;
-        if (f->map(dir, nd_old, r, P->T, old->L.S, &err) != CkptStatus::Ok)
-            return set_error(ZSP_EIO, "%s", err.c_str());
-        old->master[size_t(r)] = f->master();
-        old->m[size_t(r)] = f->m();
-        old->v[size_t(r)] = f->v();
-        old->work[size_t(r)] = f->work();
-        old->files[size_t(r)] = std::move(f);
+    for (int i = 0; i < n; ++i) {
+        const size_t r = size_t(need[size_t(i)]);
+        MappedRank* f = opened[size_t(i)].get();
+        old->master[r] = f->master();
+        old->m[r] = f->m();
+        old->v[r] = f->v();
+        old->work[r] = f->work();
+        old->files[r] = std::move(opened[size_t(i)]);
     }
     return ZSP_OK;
 }
