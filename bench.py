@@ -128,8 +128,8 @@ class Runner:
       1: the gradients all-reduced -- reduce-scatter into the accumulator,
          then its all-gather into a full fp32 gradient replica -- Adam from
          each rank's received slice, then the parameter all-gather.
-    With micro-batches, stages 2 and 3 reduce per micro-batch and accumulate
-    the reduced slices; stage 1 all-reduces once per step."""
+    With micro-batches, stages 2 and 3 add each micro-batch's reduced shard
+    into a shard-sized running sum; stage 1 all-reduces once per step."""
 
     def __init__(self, w, device, stage=3, split=False):
         import torch
@@ -439,6 +439,7 @@ def prefetch_bench(args, device):
       gathers  = passes of gathers alone (depth 0, no compute)
       depth D  = gathers through the schedule with compute
       hidden(D) = (compute + gathers - depth D) / gathers
+    each for the gather kernel and for the copy engines (copy_*).
     """
     import statistics
     import torch
@@ -468,16 +469,19 @@ def prefetch_bench(args, device):
         fixed_views.append(fixed[k:k + w.numel[t]])
         k += w.numel[t]
     scheds = {}
-    for D in [0] + list(args.depths):
-        s = zsp.Schedule(plan, groups, order, D)
-        arena = torch.empty(s.arena_bytes, dtype=torch.uint8, device=device)
-        s.bind(arena, gs if D > 0 else None)
-        scheds[D] = (s, arena)
+    for engine in ("kernel", "copy"):
+        for D in [0] + list(args.depths):
+            s = zsp.Schedule(plan, groups, order, D)
+            s.set_engine(engine)
+            arena = torch.empty(s.arena_bytes, dtype=torch.uint8, device=device)
+            s.bind(arena, gs if D > 0 else None)
+            scheds[(engine, D)] = (s, arena)
     torch.cuda.synchronize()
 
     results = {"layers": L, "n_d": w.n_d, "positions": len(order),
                "gather_bytes_per_layer": 4 * layer_elems,
-               "arena_bytes": {str(D): s.arena_bytes for D, (s, _a) in scheds.items()},
+               "arena_bytes": {str(D): s.arena_bytes for (e, D), (s, _a) in scheds.items()
+                               if e == "kernel"},
                "runs": []}
     for T in args.tokens:
         x = {d: torch.randn(T, d, device=device, dtype=torch.bfloat16) * 0.1
@@ -509,8 +513,11 @@ def prefetch_bench(args, device):
                 b.record(cs)
             return a, b
 
-        modes = [("compute", None, True), ("gathers", scheds[0][0], False)]
-        modes += [(f"depth{D}", scheds[D][0], True) for D in [0] + list(args.depths)]
+        modes = [("compute", None, True), ("gathers", scheds[("kernel", 0)][0], False),
+                 ("gathers_copy", scheds[("copy", 0)][0], False)]
+        modes += [(f"depth{D}", scheds[("kernel", D)][0], True) for D in [0] + list(args.depths)]
+        modes += [(f"copy_depth{D}", scheds[("copy", D)][0], True)
+                  for D in [0] + list(args.depths)]
         for _ in range(max(1, args.warmup)):
             for _name, sch, wc in modes:
                 one_pass(sch, wc)
@@ -521,13 +528,19 @@ def prefetch_bench(args, device):
                 evs[name].append(one_pass(sch, wc))
         torch.cuda.synchronize()
         ms = {name: statistics.median(a.elapsed_time(b) for a, b in e) for name, e in evs.items()}
-        c, g = ms["compute"], ms["gathers"]
+        c, g, gc = ms["compute"], ms["gathers"], ms["gathers_copy"]
         row = {"tokens": T, "compute_ms": round(c, 3), "gathers_ms": round(g, 3),
-               "gather_GBps": round(4 * layer_elems * len(order) / g / 1e6, 1), "depth": {}}
+               "gather_GBps": round(4 * layer_elems * len(order) / g / 1e6, 1),
+               "copy_gathers_ms": round(gc, 3),
+               "copy_gather_GBps": round(4 * layer_elems * len(order) / gc / 1e6, 1),
+               "depth": {}, "copy_depth": {}}
         for D in [0] + list(args.depths):
             t = ms[f"depth{D}"]
             row["depth"][str(D)] = {"ms": round(t, 3), "exposed_gather_ms": round(t - c, 3),
                                     "hidden": round((c + g - t) / g, 3)}
+            t = ms[f"copy_depth{D}"]
+            row["copy_depth"][str(D)] = {"ms": round(t, 3), "exposed_gather_ms": round(t - c, 3),
+                                         "hidden": round((c + gc - t) / gc, 3)}
         results["runs"].append(row)
         print(json.dumps(row), file=sys.stderr, flush=True)
         del x, dw

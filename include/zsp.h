@@ -14,7 +14,8 @@
  *   [ZST] "ZeRO Stages: Sharding Optimizer State, Gradients, and Parameters"
  *         ("What stage 1 partitions": rank i owns [i*N/P, (i+1)*N/P);
  *          "Stage 2 also partitions gradients": reduce-scatter, shard-sized
- *          gradient buffer, reduce per micro-batch and accumulate)
+ *          gradient buffer, each micro-batch's reduced shard summed into a
+ *          running one)
  * The Adam update is the textbook one (Kingma & Ba, Algorithm 1), which the
  * pages name without printing.
  *
@@ -341,6 +342,21 @@ zsp_status zsp_sched_acquire(zsp_sched* sched, int32_t position, void* compute_s
 /* Release the held position: every use of its slot must already be enqueued
  * on `compute_stream`; the slot may be overwritten once that work is done. */
 zsp_status zsp_sched_release(zsp_sched* sched, int32_t position, void* compute_stream);
+
+typedef enum {
+    ZSP_ENGINE_KERNEL = 0, /* the gather kernel (zsp_gather_range's), on the CUs */
+    ZSP_ENGINE_COPY = 1    /* the DMA copy engines: no compute units */
+} zsp_gather_engine;
+
+/* What runs the schedule's gathers ([ZS3] prefetch paragraph: the next
+ * layer's gather should overlap the current layer's computation; a gather
+ * kernel competes with that computation for the CUs, the copy engines do
+ * not). ZSP_ENGINE_COPY issues one device-to-device copy per rank's slice
+ * of each parameter (n_d per parameter) on the stream the kernel would run
+ * on, ordered by the same events. Takes effect at the next zsp_sched_bind:
+ * a bound schedule is unbound (ZSP_ESTATE until bound again); ZSP_ESTATE
+ * while a position is held. */
+zsp_status zsp_sched_set_engine(zsp_sched* sched, zsp_gather_engine engine);
 
 /* Abandon the current pass; the next acquire is position 0. Gathers already
  * issued still complete in stream order before any later one. */

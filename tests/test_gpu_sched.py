@@ -186,3 +186,63 @@ def test_order_rules_and_bind_errors():
     assert st(s2.bind, torch.empty(s2.arena_bytes, dtype=torch.uint8, device=dev()),
               gs) == binding.ESTATE
     s2.destroy()
+
+
+@pytest.mark.parametrize("depth", [0, 1, 2])
+@pytest.mark.parametrize("slow", [True, False])
+@pytest.mark.parametrize("src", ["work", "master"])
+def test_copy_engine_every_position(depth, slow, src):
+    """The schedule with its gathers on the DMA copy engines (one copy per
+    rank's slice of each parameter on the gather stream): each position sees
+    its layer bit for bit, over two passes, then after an Adam step."""
+    numels, groups = model()
+    nd = 8
+    M = Mirror(numels, nd, with_acc=False)
+    order = fwd_bwd(len(groups))
+    s = zsp.Schedule(M.plan, groups, order, depth, source=src)
+    s.set_engine("copy")
+    arena = torch.empty(s.arena_bytes, dtype=torch.uint8, device=dev())
+    cs, gs = torch.cuda.Stream(), torch.cuda.Stream()
+    s.bind(arena, gs if depth > 0 else None)
+    delay = torch.randn(2048, 2048, device=dev(), dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    want = expected(M, groups, order, src)
+    for rep in range(2):
+        caps = run_pass(s, cs, slow, delay)
+        check(caps, want, f"copy engine depth {depth} slow {slow} {src} pass {rep}")
+    grads = M.grads(torch.bfloat16, ("sched-copy", depth))
+    gdev = [g.to(dev()) for g in grads]
+    torch.cuda.synchronize()
+    with torch.cuda.stream(cs):
+        M.plan.reduce_adam_step(zsp.ALL_RANKS, gdev, step=1, stream=cs, **HP)
+    for j in M.ranks:
+        M.o_adam(j, M.o_reduce(j, grads), 1)
+    caps = run_pass(s, cs, slow, delay)
+    check(caps, expected(M, groups, order, src), f"copy engine depth {depth} after update")
+    s.destroy()
+
+
+def test_copy_engine_switch_needs_bind():
+    numels, groups = model()
+    M = Mirror(numels, 4, with_acc=False)
+    s = zsp.Schedule(M.plan, groups, fwd_bwd(len(groups)), 1)
+    arena = torch.empty(s.arena_bytes, dtype=torch.uint8, device=dev())
+    gs = torch.cuda.Stream()
+    s.bind(arena, gs)
+    s.acquire(0)
+    with pytest.raises(zsp.ZspError) as e:
+        s.set_engine("copy")            # a position is held
+    assert e.value.status == binding.ESTATE
+    s.release(0)
+    s.set_engine("copy")
+    with pytest.raises(zsp.ZspError) as e:
+        s.acquire(0)                    # unbound by the switch
+    assert e.value.status == binding.ESTATE
+    s.bind(arena, gs)
+    views = s.acquire(0)
+    s.release(0)
+    torch.cuda.synchronize()
+    f, c = groups[0]
+    for i, t in enumerate(range(f, f + c)):
+        assert_bits(np_of(views[i]), oracle.gather(M.numels, M.nd, t, M.o_work), f"param {t}")
+    s.destroy()

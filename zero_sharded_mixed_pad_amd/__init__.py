@@ -16,5 +16,5 @@ from .binding import (  # noqa: F401
     zsp_gather_many, zsp_gather_many_noalloc, zsp_gather_range, zsp_load_params, zsp_partition, zsp_plan_info, zsp_plan_tensor,
     zsp_reduce_adam_step, zsp_reduce_adam_step_params, zsp_reduce_shard,
     zsp_reduce_shard_params, zsp_adam_step_params, zsp_sched_acquire, zsp_sched_bind, zsp_sched_create,
-    zsp_sched_destroy, zsp_sched_info, zsp_sched_release, zsp_sched_reset,
+    zsp_sched_destroy, zsp_sched_info, zsp_sched_release, zsp_sched_reset, zsp_sched_set_engine,
 )

@@ -69,6 +69,7 @@ def _load():
         "zsp_sched_acquire": (i32, [vp, i32, vp, ctypes.POINTER(vp)]),
         "zsp_sched_release": (i32, [vp, i32, vp]),
         "zsp_sched_reset": (i32, [vp]),
+        "zsp_sched_set_engine": (i32, [vp, i32]),
         "zsp_sched_info": (i32, [vp, i32p, i32p, i64p]),
         "zsp_sched_destroy": (None, [vp]),
         "zsp_last_error": (ctypes.c_char_p, []),
@@ -363,6 +364,15 @@ def zsp_sched_reset(s):
     _check(lib.zsp_sched_reset(s))
 
 
+ENGINE_KERNEL, ENGINE_COPY = 0, 1
+_ENGINES = {"kernel": ENGINE_KERNEL, "copy": ENGINE_COPY, ENGINE_KERNEL: ENGINE_KERNEL,
+            ENGINE_COPY: ENGINE_COPY}
+
+
+def zsp_sched_set_engine(s, engine):
+    _check(lib.zsp_sched_set_engine(s, _ENGINES[engine]))
+
+
 def zsp_sched_info(s):
     d, n, b = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int64()
     _check(lib.zsp_sched_info(s, ctypes.byref(d), ctypes.byref(n), ctypes.byref(b)))
@@ -395,6 +405,11 @@ class Schedule:
         if self._h is None:
             raise ZspError(ESTATE, "the schedule is destroyed (or its plan is)")
         return self._h
+
+    def set_engine(self, engine):
+        """'kernel' or 'copy' (the DMA copy engines); bind again after."""
+        zsp_sched_set_engine(self._live(), engine)
+        self.arena = None
 
     def bind(self, arena, gather_stream):
         zsp_sched_bind(self._live(), arena, gather_stream)

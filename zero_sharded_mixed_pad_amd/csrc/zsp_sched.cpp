@@ -22,6 +22,11 @@
 //     work on position p.
 // Depth 0 gathers on the compute stream itself, in line: the gather-then-
 // compute baseline with nothing hidden.
+//
+// Gathers run either as the gather kernel (the default) or on the DMA copy
+// engines (ZSP_ENGINE_COPY): one device-to-device copy that uses no compute
+// units per rank's slice of each parameter, in order on the same stream the
+// kernel would run on, so the same events order them.
 #include <algorithm>
 #include <new>
 #include <vector>
@@ -46,6 +51,7 @@ struct zsp_sched {
     int32_t slots = 1;
     zsp_source src = ZSP_SRC_WORK;
     int64_t slot_bytes = 0;
+    zsp_gather_engine engine = ZSP_ENGINE_KERNEL;
 
     bool bound = false;
     int device = -1;
@@ -73,7 +79,36 @@ void* slot_ptr(const zsp_sched* s, int32_t pos) {
     return s->arena + int64_t(pos % s->slots) * s->slot_bytes;
 }
 
+// Copy-engine gather of position pos's group, in order on `stream`.
+zsp_status copy_gather(zsp_sched* s, int32_t pos, hipStream_t stream) {
+    const zsp_plan* P = s->plan;
+    zsp_status st = zsp::check_bound(P);
+    if (st != ZSP_OK) return st;
+    if (P->bind_rank != ZSP_ALL_RANKS)
+        return zsp::set_error(ZSP_ESTATE, "gather needs every rank's shard");
+    const int32_t g = s->order[size_t(pos)];
+    const int32_t f = s->first[size_t(g)], c = s->count[size_t(g)];
+    const int64_t esz = s->src == ZSP_SRC_WORK ? 2 : 4;
+    const char* src = s->src == ZSP_SRC_WORK ? reinterpret_cast<const char*>(P->work)
+                                             : reinterpret_cast<const char*>(P->master);
+    char* out = static_cast<char*>(slot_ptr(s, pos));
+    for (int32_t t = f; t < f + c; ++t) {
+        const int64_t sl = P->shard_len[size_t(t)], n = P->numel[size_t(t)];
+        const int64_t o = P->flat_off[size_t(t)] - P->flat_off[size_t(f)];
+        for (int32_t r = 0; r < P->nd && int64_t(r) * sl < n; ++r) {
+            const int64_t cnt = std::min(sl, n - int64_t(r) * sl);
+            const hipError_t e =
+                hipMemcpyAsync(out + (o + int64_t(r) * sl) * esz,
+                               src + (int64_t(r) * P->S + P->shard_off[size_t(t)]) * esz,
+                               size_t(cnt * esz), hipMemcpyDeviceToDeviceNoCU, stream);
+            if (e != hipSuccess) return zsp::set_hip_error(e, "copy-engine gather");
+        }
+    }
+    return ZSP_OK;
+}
+
 zsp_status issue_gather(zsp_sched* s, int32_t pos, hipStream_t stream) {
+    if (s->engine == ZSP_ENGINE_COPY) return copy_gather(s, pos, stream);
     const int32_t g = s->order[size_t(pos)];
     return zsp::gather_range(s->plan, s->first[size_t(g)], s->count[size_t(g)], s->src,
                              slot_ptr(s, pos), stream);
@@ -166,6 +201,7 @@ zsp_status zsp_sched_bind(zsp_sched* s, void* arena, int64_t arena_bytes, void* 
             return zsp::set_hip_error(e, "hipEventCreateWithFlags");
         }
     }
+
     s->arena = static_cast<char*>(arena);
     s->gstream = static_cast<hipStream_t>(gather_stream);
     s->device = dev;
@@ -227,6 +263,20 @@ zsp_status zsp_sched_release(zsp_sched* s, int32_t position, void* compute_strea
         s->next = 0;
         s->issued = -1;
     }
+    return ZSP_OK;
+}
+
+zsp_status zsp_sched_set_engine(zsp_sched* s, zsp_gather_engine engine) {
+    if (!s) return zsp::set_error(ZSP_EINVAL, "schedule is NULL");
+    if (engine != ZSP_ENGINE_KERNEL && engine != ZSP_ENGINE_COPY)
+        return zsp::set_error(ZSP_EINVAL, "bad gather engine %d", engine);
+    if (s->held >= 0)
+        return zsp::set_error(ZSP_ESTATE, "position %d is held", s->held);
+    if (s->bound) {
+        drop_events(s);
+        s->bound = false;
+    }
+    s->engine = engine;
     return ZSP_OK;
 }
 
