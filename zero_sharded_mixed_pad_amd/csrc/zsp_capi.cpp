@@ -91,6 +91,12 @@ zsp_status check_grads(const zsp_plan* P, const void* const* grads, zsp_dtype dt
     return ZSP_OK;
 }
 
+// Elements of each gradient buffer the layout names.
+int64_t grad_len(const zsp_plan* P, zsp_grad_layout layout) {
+    if (layout == ZSP_GRADS_FULL) return P->total_padded;
+    return P->bind_rank == ZSP_ALL_RANKS ? int64_t(P->nd) * P->S : P->S;
+}
+
 zsp_status adam_scalars(float lr, float b1, float b2, float eps, int64_t step,
                         zsp::AdamScalars* hp) {
     if (step < 1) return fail(ZSP_EINVAL, "step must be >= 1 (got %lld)", (long long)step);
@@ -430,6 +436,7 @@ zsp_status reduce_params(zsp_plan* P, int32_t rank_or_all, int32_t first, int32_
     zsp::ShardLaunch L = base_launch(P);
     L.grads = grads;
     L.shard_layout = layout == ZSP_GRADS_SHARD;
+    L.grad_len = grad_len(P, layout);
     L.short_pieces = short_pieces(P, first, n);
     return launch_spans(L, spans, accumulate ? zsp::OP_REDUCE_ACC : zsp::OP_REDUCE_SET, dtype,
                         stream, "reduce launch");
@@ -462,6 +469,7 @@ zsp_status reduce_adam_params(zsp_plan* P, int32_t rank_or_all, int32_t first, i
     if ((st = adam_scalars(lr, beta1, beta2, eps, step, &L.hp)) != ZSP_OK) return st;
     L.grads = grads;
     L.shard_layout = layout == ZSP_GRADS_SHARD;
+    L.grad_len = grad_len(P, layout);
     L.short_pieces = short_pieces(P, first, n);
     return launch_spans(L, spans, use_acc ? zsp::OP_FUSED_ACC : zsp::OP_FUSED, dtype, stream,
                         "fused reduce+adam launch");

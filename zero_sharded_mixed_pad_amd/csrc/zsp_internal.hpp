@@ -113,6 +113,7 @@ struct ShardLaunch {
     int32_t nd = 0;
     int32_t shard_layout = 0;  // 1: grads indexed like E-space
     const void* const* grads = nullptr;  // host array of nd device pointers
+    int64_t grad_len = 0;  // elements of each gradient buffer
     bool short_pieces = false;  // pieces in range average under kShortPiece elements
 };
 

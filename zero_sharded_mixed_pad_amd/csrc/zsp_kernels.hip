@@ -154,6 +154,7 @@ struct ShardArgs {
     const PieceInfo* info;
     const int32_t* tile;
     int64_t tile_first, e_begin, e_end;
+    int64_t glen;  // elements of each gradient buffer
     float* master;
     float* m;
     float* v;
@@ -529,6 +530,161 @@ __device__ __forceinline__ void quad_mixed(const ShardArgs<CAP>& a, int64_t E, i
     }
 }
 
+// A quad of a multi-piece tile lying wholly inside the call's range. Its
+// elements before the end of the first element's piece read their gradient
+// from gA on, the rest (the next piece) from gB on; valid has bit k set when
+// element k is a real (non-pad) element. slow: the quad meets three pieces,
+// or a read at gA or gB would leave the gradient buffers (possible only at
+// their ends); quad_mixed then takes it.
+struct QuadPlan {
+    int64_t gA, gB;
+    uint32_t valid, selB;
+    bool slow;
+};
+
+// Bits of the elements k < x of a quad.
+__device__ __forceinline__ uint32_t quad_below(int64_t x) {
+    return x <= 0 ? 0u : x >= kQuad ? 0xfu : (1u << uint32_t(x)) - 1u;
+}
+
+template <int OP, int CAP>
+__device__ __forceinline__ QuadPlan plan_quad(const ShardArgs<CAP>& a, int64_t E, int p,
+                                              const PieceInfo& pi, const PieceInfo* info) {
+    QuadPlan q{0, 0, 0u, 0u, false};
+    const int64_t ga = a.shard_layout ? E : E + pi.gdelta;
+    if (E + kQuad <= pi.end) {
+        // One piece (its pad slots, if the quad has any, are in the buffers).
+        q.gA = ga;
+        q.gB = ga;
+        q.valid = quad_below(pi.vend - E);
+        return q;
+    }
+    const PieceInfo pn = info[p + 1];  // the tile holds E + 3, so it holds this piece
+    const int64_t gb = a.shard_layout ? E : E + pn.gdelta;
+    if (E + kQuad > pn.end || (uses_grads(OP) && (ga + kQuad > a.glen || gb < 0))) {
+        q.slow = true;
+        return q;
+    }
+    q.gA = ga;
+    q.gB = gb;
+    q.selB = 0xfu & ~quad_below(pi.end - E);
+    q.valid = quad_below(pi.vend - E) | (q.selB & quad_below(pn.vend - E));
+    return q;
+}
+
+// The rank-order sum for two planned quads whose elements may come from
+// two pieces each: both reads go out for every rank of a batch of 4 before
+// the adds, and each element takes the one its piece names.
+template <typename GT, int CAP, bool TG>
+__device__ __forceinline__ void reduce_two(const ShardArgs<CAP>& a, const QuadPlan (&q)[2],
+                                           float (&g)[2][kQuad]) {
+    constexpr int B = 4;
+    const int nd = a.nd;
+    for (int r0 = 0; r0 < nd; r0 += B) {
+        float xa[B][2][kQuad], xb[B][2][kQuad];
+#pragma unroll
+        for (int i = 0; i < B; ++i) {
+            const GT* gp = static_cast<const GT*>(grad_ptr<CAP>(min(r0 + i, nd - 1)));
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                load4<GT, TG>(gp + q[h].gA, 0u, xa[i][h]);
+                load4<GT, TG>(gp + q[h].gB, 0u, xb[i][h]);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < B; ++i) {
+            if (r0 + i < nd) {
+                const bool first = (r0 + i) == 0;
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int k = 0; k < kQuad; ++k) {
+                        const float x = (q[h].selB >> k) & 1u ? xb[i][h][k] : xa[i][h][k];
+                        g[h][k] = first ? x : g[h][k] + x;
+                    }
+            }
+        }
+    }
+}
+
+// Both quads of a lane of a multi-piece tile inside the call's range, as
+// planned: one batch of state and gradient loads, then the stores of every
+// real element (reduce ops also write 0 to pad slots of the accumulator).
+// Pad elements of master, m and v are stored back unchanged; the bf16 copy is
+// written element by element where a quad has pad elements. Slow quads are
+// loaded with the rest and left alone.
+template <int OP, typename GT, int CAP, bool TG>
+__device__ __forceinline__ void quads_planned(const ShardArgs<CAP>& a, const int64_t (&E)[2],
+                                              const QuadPlan (&q)[2]) {
+    float p[2][kQuad], m[2][kQuad], v[2][kQuad], c[2][kQuad], g[2][kQuad];
+    if constexpr (is_adam(OP)) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            ld_f32x4(a.master + E[h], p[h]);
+            ld_f32x4(a.m + E[h], m[h]);
+            ld_f32x4(a.v + E[h], v[h]);
+        }
+    }
+    if constexpr (reads_acc(OP)) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) ld_f32x4(a.acc + E[h], c[h]);
+    }
+    if constexpr (uses_grads(OP)) {
+        const bool two = (q[0].selB != 0u && q[0].gB != q[0].gA) ||
+                         (q[1].selB != 0u && q[1].gB != q[1].gA);
+        if (__any(two)) {
+            reduce_two<GT, CAP, TG>(a, q, g);
+        } else {
+            const int64_t gb[2] = {q[0].gA, q[1].gA};
+            const uint32_t off[2] = {0u, 0u};
+            reduce_quads<GT, CAP, 2, TG>(a, gb, off, g);
+        }
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int k = 0; k < kQuad; ++k) {
+            if constexpr (OP == OP_ADAM) g[h][k] = c[h][k];
+            else if constexpr (reads_acc(OP)) g[h][k] = c[h][k] + g[h][k];
+        }
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        if (q[h].slow) continue;
+        const uint32_t val = q[h].valid;
+        if constexpr (is_reduce(OP)) {
+            float r[kQuad];
+#pragma unroll
+            for (int k = 0; k < kQuad; ++k) r[k] = (val >> k) & 1u ? g[h][k] : 0.0f;
+            st_f32x4(a.acc + E[h], r);
+        } else {
+            if (val == 0u) continue;
+            float pn[kQuad], mn[kQuad], vn[kQuad];
+#pragma unroll
+            for (int k = 0; k < kQuad; ++k) {
+                pn[k] = p[h][k];
+                mn[k] = m[h][k];
+                vn[k] = v[h][k];
+                adam1(pn[k], mn[k], vn[k], g[h][k], a.hp);
+                const bool ok = (val >> k) & 1u;
+                pn[k] = ok ? pn[k] : p[h][k];
+                mn[k] = ok ? mn[k] : m[h][k];
+                vn[k] = ok ? vn[k] : v[h][k];
+            }
+            st_f32x4(a.master + E[h], pn);
+            st_f32x4(a.m + E[h], mn);
+            st_f32x4(a.v + E[h], vn);
+            if (val == 0xfu) {
+                st_bf16x4(a.work + E[h], pn);
+            } else {
+#pragma unroll
+                for (int k = 0; k < kQuad; ++k)
+                    if ((val >> k) & 1u) a.work[E[h] + k] = to_bf16(pn[k]);
+            }
+        }
+    }
+}
+
 // One quad of any kind; p is the index of its piece in `info`.
 template <int OP, typename GT, int CAP, bool TG>
 __device__ __forceinline__ void quad_one(const ShardArgs<CAP>& a, int64_t E, int kind, int p,
@@ -617,36 +773,26 @@ __global__ __launch_bounds__(kWaveLanes) void shard_kernel(const ShardArgs<CAP> 
         e0 = s_e0;
         info = s_info;
     }
-    if constexpr (W == 1 && OP != OP_COPYIN) {
-        // Whole tile inside the call's range: the fast quads of both halves
-        // go out as one batch of loads, as in a single-piece tile (each lane
-        // with its own addresses; a quad that is not fast reads gradient
-        // element 0 and stores nothing). Quads at a piece or pad boundary
-        // follow on their own. Measured 1.5% faster on the 10,000-tensor
-        // fused step than taking the halves one after the other.
+    if constexpr (W == 1 && OP != OP_COPYIN && CAP <= 16) {
+        // Whole tile inside the call's range: both quads of a lane go out as
+        // one batch of loads (each lane with its own addresses), a quad that
+        // crosses into the next piece reading both pieces' gradients; only
+        // quads meeting three pieces, or at the ends of the gradient
+        // buffers, follow on their own. (Not for more than 16 ranks: the
+        // registers it takes there would lower the waves per CU.)
         const int64_t T0 = tile * kTile;
         if (T0 >= a.e_begin && T0 + kTile <= a.e_end) {
-            const int64_t Ea = E0, Ez = E0 + kHalf;
-            const int pa = n == 1 ? 0 : find_local(e0, n, Ea);
-            const int pz = n == 1 ? 0 : find_local(e0, n, Ez);
+            const int64_t E[2] = {E0, E0 + kHalf};
+            const int pa = n == 1 ? 0 : find_local(e0, n, E[0]);
+            const int pz = n == 1 ? 0 : find_local(e0, n, E[1]);
             const PieceInfo ia = info[pa], iz = info[pz];
-            const int ka = classify(a, Ea, ia), kz = classify(a, Ez, iz);
-            const bool ok[2] = {ka == Q_FAST, kz == Q_FAST};
-            const int64_t Eb[2] = {Ea, Ez};
-            const int64_t gb[2] = {ok[0] ? (a.shard_layout ? Ea : Ea + ia.gdelta) : 0,
-                                   ok[1] ? (a.shard_layout ? Ez : Ez + iz.gdelta) : 0};
-            const int64_t ib[2] = {0, 0};
-            const uint32_t off[2] = {0u, 0u};
-            quads_fast<OP, GT, CAP, 2, TG>(a, Eb, gb, ib, off, ok);
+            const QuadPlan q[2] = {plan_quad<OP>(a, E[0], pa, ia, info),
+                                   plan_quad<OP>(a, E[1], pz, iz, info)};
+            quads_planned<OP, GT, CAP, TG>(a, E, q);
 #pragma unroll 1
             for (int h = 0; h < 2; ++h) {
-                const int kh = h ? kz : ka;
-                const int64_t E = h ? Ez : Ea;
-                if (kh == Q_MIXED) {
-                    quad_mixed<OP, GT, CAP>(a, E, h ? pz : pa, h ? iz : ia, info);
-                } else if (kh == Q_PAD) {
-                    quad_pad<OP, CAP>(a, E);
-                }
+                if (h ? q[1].slow : q[0].slow)
+                    quad_mixed<OP, GT, CAP>(a, E[h], h ? pz : pa, h ? iz : ia, info);
             }
             return;
         }
@@ -1171,6 +1317,7 @@ hipError_t launch_t(const ShardLaunch& L, hipStream_t stream) {
     a.hp = L.hp;
     a.nd = L.nd;
     a.shard_layout = L.shard_layout;
+    a.glen = L.grad_len;
     if constexpr (uses_grads(OP)) {
         for (int r = 0; r < L.nd; ++r) a.grads[r] = L.grads[r];
     }
