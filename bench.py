@@ -191,7 +191,7 @@ class Runner:
                 self.gather_groups.append((first, n, out, cnt * 4))
         self.step_no = 0
         self.ev = {k: [] for k in STEP_KINDS + ("gather_cold", "gather_list",
-                                                 "gather_list_cold")}
+                                                 "gather_list_cold", "gather_many_cold")}
 
     def _event(self):
         return self.torch.cuda.Event(enable_timing=True)
@@ -252,21 +252,35 @@ class Runner:
                             self.plan.gather_range(first, n, out, "work"), True)
 
     def list_gathers(self, flush, reps):
-        """Every parameter at once through the list form (zsp_gather_many),
-        each into its own output, `reps` times; after `flush` when it is
-        given (then recorded as gather_list_cold, beside the range form's
-        gather_cold), else back to back (gather_list)."""
+        """Every parameter at once, each into its own output, `reps` times:
+        as a prepared list (zsp_gather_list_run: one launch over records
+        built once) and, when `flush` is given, also as the one-shot call
+        (zsp_gather_many: checks, staging and the record kernel each call).
+        After `flush` they are recorded as gather_list_cold and
+        gather_many_cold, beside the range form's gather_cold; without one,
+        prepared runs back to back (gather_list)."""
         torch = self.torch
+        from zero_sharded_mixed_pad_amd import binding
         if not hasattr(self, "glist"):
+            ids = list(range(len(self.w.numel)))
             outs = [torch.empty(max(n, 1), dtype=torch.bfloat16, device=self.dev)
                     for n in self.w.numel]
+            self.glist = self.plan.gather_list(ids, outs, "work")
             # marshalled once: the timed calls are the library's alone
-            self.glist = self.plan.gather_list(list(range(len(self.w.numel))), outs, "work")
+            self.gmany = binding._list_arrays(ids, outs, torch.bfloat16)
         kind = "gather_list_cold" if flush else "gather_list"
         for _ in range(reps):
             if flush:
                 flush()
             self._timed(kind, lambda: self.plan.gather_prepared(self.glist), True)
+        if flush:
+            ids_c, outs_c, n = self.gmany
+            h, st = self.plan.handle, binding._stream(None)
+            call = lambda: binding._check(binding.lib.zsp_gather_many(  # noqa: E731
+                h, ids_c, n, binding.SRC_WORK, outs_c, st))
+            for _ in range(reps):
+                flush()
+                self._timed("gather_many_cold", call, True)
 
     def step_bytes(self):
         w = self.w
@@ -295,7 +309,7 @@ class Runner:
             return self.bytes_adam
         if kind == "gather_acc":
             return self.bytes_gather_acc
-        if kind.startswith("gather_list"):
+        if kind.startswith("gather_list") or kind == "gather_many_cold":
             return sum(g[3] for g in self.gather_groups)
         return sum(g[3] for g in self.gather_groups) / len(self.gather_groups)
 
@@ -311,7 +325,7 @@ class Runner:
             return "adam_from_acc[f32]"
         if kind == "gather_acc":
             return "gather[f32]"
-        if kind.startswith("gather_list"):
+        if kind.startswith("gather_list") or kind == "gather_many_cold":
             staged = sum(1 for n in self.w.numel if n > 0) > 64
             return f"gather_list_{'recs' if staged else 'args'}[bf16]"
         return "gather[bf16]"

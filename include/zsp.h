@@ -36,13 +36,15 @@
  *   optimizer state, accumulator, gather outputs, schedule arenas). A plan
  *   owns its host tables, the device copies of its offset tables (allocated
  *   in zsp_bind_state), the staging slots of long zsp_gather_many lists
- *   (allocated when such a list first needs them) and, from its first
+ *   (allocated when such a list first needs them; a prepared list,
+ *   zsp_gather_list_create, owns memory of its own) and, from its first
  *   checkpoint save or load, the checkpoint staging (pinned host chunks,
  *   streams, events); zsp_destroy frees them. The other hot-path calls
  *   (reduce, Adam, the range and single gathers, schedule acquire and
  *   release) allocate nothing; checkpoint calls also use host memory for
  *   their own duration. The reduce, Adam, range and single gather calls,
- *   and zsp_gather_many on lists of at most 64 parameters, only check
+ *   zsp_gather_list_run, and zsp_gather_many on lists of at most 64
+ *   parameters, only check
  *   arguments and launch kernels (no host wait, no copy, no memset), so they
  *   can be captured into a HIP graph; Adam's scalars (lr, betas, eps and the
  *   step's bias corrections) are kernel arguments, so a replay repeats the
@@ -87,6 +89,7 @@ extern "C" {
 
 typedef struct zsp_plan zsp_plan;
 typedef struct zsp_sched zsp_sched;
+typedef struct zsp_gather_list zsp_gather_list;
 
 typedef enum {
     ZSP_OK = 0,
@@ -292,6 +295,33 @@ zsp_status zsp_gather_many(zsp_plan* plan, const int32_t* ids, int32_t n, zsp_so
  * at all, as in zsp_gather_many. */
 zsp_status zsp_gather_many_noalloc(zsp_plan* plan, const int32_t* ids, int32_t n,
                                    zsp_source src, void* const* outs, void* stream);
+
+/* A list gather prepared once and run many times: the same bucket into the
+ * same outputs every step ([ZD] section 3: a module's parameters are
+ * gathered before its forward and again before its backward, every step;
+ * section 8: gathers go out in buckets). zsp_gather_list_create takes the
+ * arguments of zsp_gather_many, with the same checks and errors, and keeps
+ * what a run needs: for a list of more than 64 non-empty parameters, its
+ * per-tile records (32 bytes per 512 output elements, plus 16 bytes per
+ * parameter), built on the device once -- create allocates that memory,
+ * enqueues the build on `stream` and waits for it before returning
+ * (ZSP_ENOMEM if the allocation fails). Lists of at most 64 keep their
+ * entries on the host and run as zsp_gather_many's one launch.
+ *   zsp_gather_list_run enqueues the gather on `stream`: one launch, no
+ * copy, no allocation, no host wait (capturable into a HIP graph). It reads
+ * the source named at create from the plan's current binding, so the list
+ * stays valid when state is bound again on the same device; the outputs
+ * named at create must stay allocated while runs may be in flight.
+ * ZSP_ESTATE if the plan has no all-rank binding now, is bound on another
+ * device than at create, or the source is the accumulator and none is
+ * bound; ZSP_EINVAL for a NULL list.
+ *   zsp_gather_list_destroy frees the list (NULL is a no-op); runs must have
+ * finished. A list refers to its plan, which must outlive it. */
+zsp_status zsp_gather_list_create(zsp_plan* plan, const int32_t* ids, int32_t n,
+                                  zsp_source src, void* const* outs, void* stream,
+                                  zsp_gather_list** list);
+zsp_status zsp_gather_list_run(zsp_gather_list* list, void* stream);
+void zsp_gather_list_destroy(zsp_gather_list* list);
 
 /* ---- Per-layer gather schedule with prefetch ------------------------------
  * [ZS3] on-demand fetch list (gather layer l before its computation, discard

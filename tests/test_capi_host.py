@@ -125,6 +125,14 @@ def test_unbound_calls_fail_before_touching_a_device():
     outs = (ctypes.c_void_p * 2)(256, 512)
     assert lib.zsp_gather_many(h, ids, 2, binding.SRC_WORK, outs, null) == binding.ESTATE
     assert "bind" in zsp.last_error()
+    gl = ctypes.c_void_p(1234)
+    assert lib.zsp_gather_list_create(h, ids, 2, binding.SRC_WORK, outs, null,
+                                      ctypes.byref(gl)) == binding.ESTATE
+    assert gl.value is None                       # *list cleared on failure
+    assert lib.zsp_gather_list_create(h, ids, 2, binding.SRC_WORK, outs, null,
+                                      None) == binding.EINVAL
+    assert lib.zsp_gather_list_run(None, null) == binding.EINVAL
+    lib.zsp_gather_list_destroy(None)             # ignored
     assert lib.zsp_reduce_shard(None, -1, grads, 1, 0, 0, null) == binding.EINVAL
     plan.destroy()
 

@@ -212,3 +212,135 @@ def test_prepared_list_after_each_step():
         for ids, outs, gl in lists:
             M.plan.gather_prepared(gl)
             check(M, ids, outs, "work", f"prepared list of {len(ids)}, step {step}")
+
+
+@pytest.mark.parametrize("which", list(LAYOUTS))
+@pytest.mark.parametrize("source", ["work", "master", "acc"])
+def test_prepared_lists_match_oracle(which, source):
+    """zsp_gather_list_create / _run: each id list of test_lists_match_oracle,
+    prepared once and run twice (the second run into outputs refilled with
+    NaN), equals the oracle's gather; the accumulator source against the
+    range form."""
+    numels, nd = LAYOUTS[which]
+    print(f"\n[prepared list] layout {which}, source {source}", flush=True)
+    M = Mirror(numels, nd)
+    d = dev()
+    if source == "acc":
+        grads = M.grads(torch.bfloat16, ("prepared-acc", which))
+        M.plan.reduce_shard(zsp.ALL_RANKS, [g.to(d) for g in grads])
+        whole = torch.empty(max(M.L.total_numel, 1), dtype=torch.float32, device=d)
+        M.plan.gather_range(0, M.L.T, whole, "acc")
+    rng = np.random.default_rng(synth.derive_seed("prepared-list", which))
+    dt = torch.bfloat16 if source == "work" else torch.float32
+    for name, ids in id_lists(M.L.T, rng).items():
+        outs = outputs(M, ids, dt)
+        gl = M.plan.gather_list(ids, outs, source)
+        for run in (0, 1):
+            if run:
+                for o in outs:
+                    o.fill_(float("nan"))
+            M.plan.gather_prepared(gl)
+            if source == "acc":
+                torch.cuda.synchronize()
+                for i, (t, o) in enumerate(zip(ids, outs)):
+                    a, b = int(M.L.flat_off[t]), int(M.L.flat_off[t + 1])
+                    assert torch.equal(o[:b - a].view(torch.int32), whole[a:b].view(torch.int32)), \
+                        f"{which}/{name} run {run}: entry {i} (id {t})"
+                    assert torch.isnan(o[b - a:]).all(), f"{which}/{name}: entry {i} overran"
+            else:
+                check(M, ids, outs, source, f"{which}/{name} run {run}")
+        gl.close()
+        gl.close()   # a second close is a no-op
+
+
+def test_prepared_list_streams_and_rebinding():
+    """A prepared staged list runs on two other streams, and after the state
+    is bound again to new tensors (same layout) it reads the new binding."""
+    numels, nd = synth.small_tensor_sizes(count=150, lo=5, hi=6000, seed=12), 8
+    M = Mirror(numels, nd)
+    d = dev()
+    ids = [int(x) for x in np.random.default_rng(8).permutation(M.L.T)]
+    outs = outputs(M, ids, torch.bfloat16)
+    gl = M.plan.gather_list(ids, outs, "work")
+    for s in (torch.cuda.Stream(), torch.cuda.Stream()):
+        for o in outs:
+            o.fill_(float("nan"))
+        torch.cuda.synchronize()
+        M.plan.gather_prepared(gl, stream=s)
+        check(M, ids, outs, "work", "prepared list on a side stream")
+    # bind fresh state tensors, load other parameters, run the same list
+    n = nd * M.plan.S
+    st = [torch.empty(n, dtype=torch.float32, device=d) for _ in range(3)]
+    work = torch.empty(n, dtype=torch.bfloat16, device=d)
+    M.plan.bind_state(zsp.ALL_RANKS, st[0], st[1], st[2], work)
+    flat = synth.normal(M.plan.total_numel, 0.02, torch.bfloat16, synth.derive_seed("rebind", 0), d)
+    M.plan.load_params(flat)
+    M.plan.gather_prepared(gl)
+    torch.cuda.synchronize()
+    for i, (t, o) in enumerate(zip(ids, outs)):
+        a, b = int(M.L.flat_off[t]), int(M.L.flat_off[t + 1])
+        assert torch.equal(o[:b - a].view(torch.int16), flat[a:b].view(torch.int16)), \
+            f"after rebinding: entry {i} (id {t})"
+    # bound for one rank only: the list cannot run
+    local = torch.empty(M.plan.S, dtype=torch.float32, device=d)
+    M.plan.bind_state(0, local, torch.empty_like(local), torch.empty_like(local),
+                      torch.empty(M.plan.S, dtype=torch.bfloat16, device=d))
+    with pytest.raises(zsp.ZspError) as e:
+        M.plan.gather_prepared(gl)
+    assert e.value.status == zsp.binding.ESTATE
+    gl.close()
+    with pytest.raises(ValueError):
+        gl.run()
+
+
+def test_prepared_list_errors():
+    """Create takes zsp_gather_many's checks; run needs a list."""
+    numels, nd = [1003, 64, 0], 4
+    M = Mirror(numels, nd)
+    d = dev()
+    ok = torch.empty(2048, dtype=torch.bfloat16, device=d)
+    for ids, outs, status in (([0, 3], [ok, ok], zsp.binding.ERANGE),
+                              ([1], [ok[1:]], zsp.binding.EINVAL),
+                              ([1, 0], [ok, None], zsp.binding.EINVAL)):
+        with pytest.raises(zsp.ZspError) as e:
+            M.plan.gather_list(ids, outs, "work")
+        assert e.value.status == status
+    no_acc = Mirror(numels, nd, with_acc=False)
+    with pytest.raises(zsp.ZspError) as e:
+        no_acc.plan.gather_list([0], [torch.empty(2048, dtype=torch.float32, device=d)], "acc")
+    assert e.value.status == zsp.binding.ESTATE
+    assert zsp.binding.lib.zsp_gather_list_run(None, None) == zsp.binding.EINVAL
+    zsp.binding.lib.zsp_gather_list_destroy(None)
+    empty = M.plan.gather_list([2], [None], "work")   # nothing to gather
+    M.plan.gather_prepared(empty)
+    empty.close()
+    M.check_state("after rejected prepared lists", exact=True)
+
+
+def test_prepared_list_beyond_one_slot():
+    """A prepared list of more tiles than one staging slot's record area
+    (2^19 tiles) keeps the records of all of them; gather(partition(x)) == x
+    for every output."""
+    numels = [300_000_000] + [4096 + 3 * i for i in range(70)]
+    nd = 8
+    plan = zsp.partition(numels, nd)
+    d = dev()
+    n = nd * plan.S
+    master = torch.empty(n, dtype=torch.float32, device=d)
+    m = torch.empty_like(master)
+    v = torch.empty_like(master)
+    work = torch.empty(n, dtype=torch.bfloat16, device=d)
+    plan.bind_state(zsp.ALL_RANKS, master, m, v, work)
+    flat = synth.normal(plan.total_numel, 0.02, torch.bfloat16, synth.derive_seed("chunks", 1), d)
+    plan.load_params(flat)
+    ids = list(range(len(numels) - 1, -1, -1))
+    outs = [torch.empty(numels[t], dtype=torch.bfloat16, device=d) for t in ids]
+    gl = plan.gather_list(ids, outs, "work")
+    plan.gather_prepared(gl)
+    torch.cuda.synchronize()
+    offs = np.concatenate([[0], np.cumsum(numels)])
+    for t, o in zip(ids, outs):
+        want = flat[int(offs[t]):int(offs[t + 1])]
+        assert torch.equal(o.view(torch.int16), want.view(torch.int16)), f"parameter {t}"
+    gl.close()
+    plan.destroy()

@@ -59,6 +59,9 @@ def _load():
         "zsp_gather_range": (i32, [vp, i32, i32, i32, vp, vp]),
         "zsp_gather_many": (i32, [vp, i32p, i32, i32, vpp, vp]),
         "zsp_gather_many_noalloc": (i32, [vp, i32p, i32, i32, vpp, vp]),
+        "zsp_gather_list_create": (i32, [vp, i32p, i32, i32, vpp, vp, ctypes.POINTER(vp)]),
+        "zsp_gather_list_run": (i32, [vp, vp]),
+        "zsp_gather_list_destroy": (None, [vp]),
         "zsp_checkpoint_write_host": (i32, [vp, i32, ctypes.c_char_p, i64, vp, vp, vp, vp]),
         "zsp_checkpoint_read_host": (i32, [vp, i32, ctypes.c_char_p, i64p, vp, vp, vp, vp]),
         "zsp_checkpoint_save": (i32, [vp, i32, ctypes.c_char_p, i64, vp]),
@@ -262,21 +265,50 @@ def zsp_gather_many_noalloc(h, ids, outs, source="work", stream=None):
     _check(lib.zsp_gather_many_noalloc(h, ids_c, n, src, outs_c, _stream(stream)))
 
 
+def zsp_gather_list_create(h, ids, outs, source="work", stream=None):
+    """A prepared list gather (zsp_gather_list_create); returns its handle."""
+    src = _SOURCES[source]
+    dt = torch.bfloat16 if src == SRC_WORK else torch.float32
+    ids_c, outs_c, n = _list_arrays(ids, outs, dt)
+    out = ctypes.c_void_p()
+    _check(lib.zsp_gather_list_create(h, ids_c, n, src, outs_c, _stream(stream),
+                                      ctypes.byref(out)))
+    return out
+
+
+def zsp_gather_list_run(gl, stream=None):
+    _check(lib.zsp_gather_list_run(gl, _stream(stream)))
+
+
+def zsp_gather_list_destroy(gl):
+    lib.zsp_gather_list_destroy(gl)
+
+
 class GatherList:
-    """The C arrays of one zsp_gather_many call, marshalled once: a caller
-    that gathers the same bucket into the same outputs again and again (a
-    module's parameters each step) pays the per-tensor conversion once.
-    The outputs are kept alive with the object."""
+    """A list gather prepared once (zsp_gather_list_create) for a caller that
+    gathers the same bucket into the same outputs again and again (a
+    module's parameters each step): each run is one launch. Keeps the plan
+    and the outputs alive; frees the native list when collected or closed."""
 
-    def __init__(self, ids, outs, source="work"):
-        self.src = _SOURCES[source]
-        dt = torch.bfloat16 if self.src == SRC_WORK else torch.float32
-        self.ids_c, self.outs_c, self.n = _list_arrays(ids, outs, dt)
+    def __init__(self, plan, ids, outs, source="work", stream=None):
+        self.plan = plan
         self.ids, self.outs = list(ids), list(outs)
+        self._gl = zsp_gather_list_create(plan._h, self.ids, self.outs, source, stream)
+        plan._lists.add(self)
 
-    def run(self, h, stream=None):
-        _check(lib.zsp_gather_many(h, self.ids_c, self.n, self.src, self.outs_c,
-                                   _stream(stream)))
+    def run(self, stream=None):
+        if self._gl is None:
+            raise ValueError("gather list is closed")
+        zsp_gather_list_run(self._gl, stream)
+
+    def close(self):
+        """Frees the native list; runs already enqueued must have finished."""
+        if getattr(self, "_gl", None) is not None:
+            zsp_gather_list_destroy(self._gl)
+            self._gl = None
+
+    def __del__(self):
+        self.close()
 
 
 def _host_arrays(S, master, m, v, work, writable):
@@ -463,6 +495,7 @@ class Plan:
         self._bound = None
         self._bound_rank = None
         self._schedules = weakref.WeakSet()   # destroyed before the plan
+        self._lists = weakref.WeakSet()       # prepared gather lists, likewise
 
     @property
     def handle(self):
@@ -471,6 +504,8 @@ class Plan:
     def destroy(self):
         for sched in list(self._schedules):
             sched.destroy()
+        for gl in list(self._lists):
+            gl.close()
         if self._h is not None and self._h.value:
             zsp_destroy(self._h)
         self._h = None
@@ -564,15 +599,15 @@ class Plan:
         zsp_gather_many_noalloc(self._h, ids, outs, source, stream)
 
     def gather_list(self, ids, outs, source="work"):
-        """A GatherList for this plan's parameters (sizes checked once);
-        run it with gather_prepared."""
+        """A prepared GatherList for this plan's parameters (sizes checked
+        and records built once); run it with gather_prepared."""
         for i, (t, o) in enumerate(zip(ids, outs)):
             if 0 <= t < len(self.numel):
                 _need(o, self.numel[t], f"outs[{i}]")
-        return GatherList(ids, outs, source)
+        return GatherList(self, ids, outs, source)
 
     def gather_prepared(self, glist, stream=None):
-        glist.run(self._h, stream)
+        glist.run(stream)
 
     def checkpoint_save(self, rank, directory, step, stream=None):
         zsp_checkpoint_save(self._h, rank, directory, step, stream)

@@ -16,10 +16,16 @@
 // gathers still in flight), so calls on any streams and threads stay
 // apart. A slot grows, and is then reallocated, when a list needs more
 // room than it has.
+//
+// A prepared list (zsp_gather_list_create) does the staged form's first
+// kernel once: it keeps the records of every tile in device memory of its
+// own, so each run is the copy kernel alone (a bucket gathered every step
+// into the same outputs pays the staging once).
 #include <algorithm>
 #include <cstring>
 #include <mutex>
 #include <new>
+#include <vector>
 
 #include "zsp_entry.hpp"
 #include "zsp_internal.hpp"
@@ -132,9 +138,8 @@ zsp_status launch_list(const ListLaunch& L, zsp_source src, hipStream_t stream) 
     return ZSP_OK;
 }
 
-zsp_status gather_list_args(const zsp_plan* P, const int32_t* ids, int32_t n,
-                            void* const* outs, zsp_source src, const ListTotals& lt,
-                            hipStream_t stream) {
+ListLaunch list_args(const zsp_plan* P, const int32_t* ids, int32_t n, void* const* outs,
+                     zsp_source src, const ListTotals& lt) {
     ListLaunch L = list_base(P, src, lt);
     L.n_args = static_cast<int32_t>(lt.count);
     for_each_entry(P, ids, n, outs,
@@ -144,7 +149,13 @@ zsp_status gather_list_args(const zsp_plan* P, const int32_t* ids, int32_t n,
                        L.arg_tile0[e] = static_cast<int32_t>(tile0);
                    });
     L.arg_tile0[L.n_args] = static_cast<int32_t>(lt.tiles);
-    return launch_list(L, src, stream);
+    return L;
+}
+
+zsp_status gather_list_args(const zsp_plan* P, const int32_t* ids, int32_t n,
+                            void* const* outs, zsp_source src, const ListTotals& lt,
+                            hipStream_t stream) {
+    return launch_list(list_args(P, ids, n, outs, src, lt), src, stream);
 }
 
 namespace {
@@ -227,4 +238,111 @@ extern "C" zsp_status zsp_gather_many(zsp_plan* P, const int32_t* ids, int32_t n
     }
     s.pending = true;
     return st;
+}
+
+// ---- Prepared lists ---------------------------------------------------------
+
+struct zsp_gather_list {
+    zsp_plan* plan = nullptr;
+    zsp_source src = ZSP_SRC_WORK;
+    int device = -1;
+    zsp::ListLaunch L;    // argument form (n_args > 0) or records (mode 2)
+    void* dev = nullptr;  // records form: entries, coarse index, records
+};
+
+extern "C" zsp_status zsp_gather_list_create(zsp_plan* P, const int32_t* ids, int32_t n,
+                                             zsp_source src, void* const* outs, void* stream,
+                                             zsp_gather_list** out) {
+    using namespace zsp;
+    if (!out) return set_error(ZSP_EINVAL, "out is NULL");
+    *out = nullptr;
+    ListTotals lt;
+    zsp_status st = check_list(P, ids, n, src, outs, &lt);
+    if (st != ZSP_OK) return st;
+    const hipStream_t hs = static_cast<hipStream_t>(stream);
+    zsp_gather_list* G = new (std::nothrow) zsp_gather_list();
+    if (!G) return set_error(ZSP_ENOMEM, "out of host memory");
+    G->plan = P;
+    G->src = src;
+    G->device = P->device;
+    if (lt.tiles == 0) {
+        G->L = list_base(P, src, lt);  // nothing to gather
+    } else if (lt.count <= kListArgMax) {
+        G->L = list_args(P, ids, n, outs, src, lt);
+    } else {
+        // Entries and coarse index made on the host, copied once; the
+        // records of every tile are built on the device and kept.
+        const StagedSizes z = staged_sizes(lt, INT64_MAX);
+        const size_t up = z.ents + z.coarse;
+        std::vector<char> host;
+        try {
+            host.assign(up, 0);
+        } catch (const std::bad_alloc&) {
+            delete G;
+            return set_error(ZSP_ENOMEM, "out of host memory (%zu bytes)", up);
+        }
+        EntSink es{reinterpret_cast<ListEntry*>(host.data())};
+        CoarseSink cs{reinterpret_cast<int32_t*>(host.data() + z.ents)};
+        emit_staged(P, ids, n, outs, es, cs);
+        hipError_t e = hipMalloc(&G->dev, up + z.recs);
+        if (e != hipSuccess) {
+            G->dev = nullptr;
+            delete G;
+            return set_error(ZSP_ENOMEM, "device list of %zu bytes: %s", up + z.recs,
+                             hipGetErrorString(e));
+        }
+        ListLaunch L = list_base(P, src, lt);
+        char* d = static_cast<char*>(G->dev);
+        L.ents = reinterpret_cast<const ListEntry*>(d);
+        L.n_ents = static_cast<int32_t>(lt.count);
+        L.coarse = reinterpret_cast<const int32_t*>(d + z.ents);
+        L.recs = reinterpret_cast<TileRec*>(d + up);
+        L.rec_cap = z.rec_tiles;
+        L.mode = 1;
+        if ((e = hipMemcpyAsync(G->dev, host.data(), up, hipMemcpyHostToDevice, hs)) != hipSuccess)
+            st = set_hip_error(e, "list copy");
+        else
+            st = launch_list(L, src, hs);
+        // the host buffer, and the runs on any stream, wait for this work
+        if ((e = hipStreamSynchronize(hs)) != hipSuccess && st == ZSP_OK)
+            st = set_hip_error(e, "waiting for the list's records");
+        if (st != ZSP_OK) {
+            (void)hipFree(G->dev);
+            delete G;
+            return st;
+        }
+        L.mode = 2;
+        G->L = L;
+    }
+    *out = G;
+    return ZSP_OK;
+}
+
+extern "C" zsp_status zsp_gather_list_run(zsp_gather_list* G, void* stream) {
+    using namespace zsp;
+    if (!G) return set_error(ZSP_EINVAL, "list is NULL");
+    const zsp_plan* P = G->plan;
+    zsp_status st = check_bound(P);
+    if (st != ZSP_OK) return st;
+    if (P->bind_rank != ZSP_ALL_RANKS)
+        return set_error(ZSP_ESTATE,
+                         "gather needs every rank's shard (state bound for rank %d only)",
+                         P->bind_rank);
+    if (P->device != G->device)
+        return set_error(ZSP_ESTATE, "list made on device %d, plan now bound on device %d",
+                         G->device, P->device);
+    if (G->src == ZSP_SRC_ACC && !P->acc)
+        return set_error(ZSP_ESTATE, "gather of the accumulator, but none is bound");
+    if (G->L.tiles == 0) return ZSP_OK;
+    ListLaunch L = G->L;
+    L.src = G->src == ZSP_SRC_WORK     ? static_cast<const void*>(P->work)
+            : G->src == ZSP_SRC_MASTER ? static_cast<const void*>(P->master)
+                                       : static_cast<const void*>(P->acc);
+    return launch_list(L, G->src, static_cast<hipStream_t>(stream));
+}
+
+extern "C" void zsp_gather_list_destroy(zsp_gather_list* G) {
+    if (!G) return;
+    if (G->dev) (void)hipFree(G->dev);
+    delete G;
 }

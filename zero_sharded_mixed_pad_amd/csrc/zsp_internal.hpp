@@ -200,6 +200,10 @@ struct ListLaunch {
     const int32_t* coarse = nullptr;
     TileRec* recs = nullptr;
     int64_t rec_cap = 0;
+    // Staged form only: 0, expand then gather, chunk by chunk; 1, expand
+    // only (records of every tile, rec_cap >= tiles); 2, gather only, from
+    // records built before (rec_cap >= tiles).
+    int32_t mode = 0;
 };
 
 // Launch a list gather (argument form if n_args > 0, else staged); esz is

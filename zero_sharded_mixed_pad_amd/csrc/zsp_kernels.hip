@@ -1443,6 +1443,22 @@ hipError_t launch_list_t(const ListLaunch& L, int esz, hipStream_t stream) {
         return hipGetLastError();
     }
     if (L.rec_cap <= 0 || L.rec_cap % 64 != 0) return hipErrorInvalidValue;
+    if (L.mode != 0 && L.rec_cap < L.tiles) return hipErrorInvalidValue;
+    if (L.mode == 2) {
+        ListRecArgs g{};
+        g.recs = L.recs;
+        g.src = L.src;
+        g.tiles = L.tiles;
+        const int64_t blocks = list_blocks(L.tiles, L.short_pieces);
+        if (blocks > kMaxBlocks) return hipErrorInvalidValue;
+        if (L.short_pieces)
+            hipLaunchKernelGGL((gather_list_recs<T, true>), dim3(uint32_t(blocks)), block, 0,
+                               stream, g);
+        else
+            hipLaunchKernelGGL((gather_list_recs<T, false>), dim3(uint32_t(blocks)), block, 0,
+                               stream, g);
+        return hipGetLastError();
+    }
     for (int64_t t = 0; t < L.tiles; t += L.rec_cap) {
         const int64_t t_end = min(L.tiles, t + L.rec_cap);
         ListExpandArgs e{};
@@ -1459,6 +1475,7 @@ hipError_t launch_list_t(const ListLaunch& L, int esz, hipStream_t stream) {
         hipLaunchKernelGGL(list_expand_kernel, dim3(uint32_t(waves)), block, 0, stream, e);
         hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
+        if (L.mode == 1) continue;
         ListRecArgs g{};
         g.recs = L.recs;
         g.src = L.src;

@@ -40,7 +40,10 @@ ListLaunch list_base(const zsp_plan* P, zsp_source src, const ListTotals& lt);
 StagedSizes staged_sizes(const ListTotals& lt, int64_t rec_chunk);
 // Launch, turning a HIP failure into ZSP_EHIP with a message.
 zsp_status launch_list(const ListLaunch& L, zsp_source src, hipStream_t stream);
-// The kernel-argument form (lists of at most kListArgMax entries with elements).
+// The kernel-argument form (lists of at most kListArgMax entries with
+// elements): its launch description, and that launch.
+ListLaunch list_args(const zsp_plan* P, const int32_t* ids, int32_t n, void* const* outs,
+                     zsp_source src, const ListTotals& lt);
 zsp_status gather_list_args(const zsp_plan* P, const int32_t* ids, int32_t n,
                             void* const* outs, zsp_source src, const ListTotals& lt,
                             hipStream_t stream);
