@@ -847,19 +847,13 @@ __device__ __forceinline__ u32x4 ld_src(const u32x4_a2* p) {
     else return ldnt_x4_a2(p);
 }
 
-// out[k] = src[K + delta(piece of K)], K = k_first + k, k < count.
+// One tile of the gather: out[k] = src[K + delta(piece of K)], K = k_first
+// + k, for the tile's k < count. s_k0 and s_delta: the wave's LDS for
+// staging the pieces of a tile of many.
 template <typename T, bool SHORT>
-__global__ __launch_bounds__(kWaveLanes) void gather_kernel(const GatherArgs a) {
+__device__ __forceinline__ void gather_tile(const GatherArgs& a, int64_t tile, int lane,
+                                            int64_t* s_k0, int64_t* s_delta) {
     using S = GatherShape<T>;
-    __shared__ int64_t s_k0[kStage + 1];
-    __shared__ int64_t s_delta[kStage];
-    const int lane = threadIdx.x;
-    int64_t tile = blockIdx.x;
-    if constexpr (SHORT) {
-        const int64_t x = tile % 8, i = tile / 8;
-        tile = ((i / kXcdRun) * 8 + x) * kXcdRun + (i % kXcdRun);
-        if (tile * kTile >= a.count) return;  // the grid is rounded up to 8 runs
-    }
     const int64_t kw = tile * kTile;  // local start of the wave's tile
     const T* src = static_cast<const T*>(a.src);
     T* out = static_cast<T*>(a.out);
@@ -1025,6 +1019,20 @@ __global__ __launch_bounds__(kWaveLanes) void gather_kernel(const GatherArgs a) 
             }
         }
     }
+}
+
+// One wave per tile (short-piece launches: XCD runs of kXcdRun tiles).
+template <typename T, bool SHORT>
+__global__ __launch_bounds__(kWaveLanes) void gather_kernel(const GatherArgs a) {
+    __shared__ int64_t s_k0[kStage + 1];
+    __shared__ int64_t s_delta[kStage];
+    int64_t tile = blockIdx.x;
+    if constexpr (SHORT) {
+        const int64_t x = tile % 8, i = tile / 8;
+        tile = ((i / kXcdRun) * 8 + x) * kXcdRun + (i % kXcdRun);
+        if (tile * kTile >= a.count) return;  // the grid is rounded up to 8 runs
+    }
+    gather_tile<T, SHORT>(a, tile, threadIdx.x, s_k0, s_delta);
 }
 
 // ---- Gather of a list of parameters into separate outputs ------------------
