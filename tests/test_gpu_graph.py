@@ -5,7 +5,8 @@ one step and replay it. Captured once, replayed three times with eager work
 and host synchronisations between the replays; after every replay the state
 and the gathered parameters equal those of the same calls made eagerly on a
 twin plan. The Adam step's scalars are kernel arguments, so a replay repeats
-the step number it was captured with (the eager twin does the same)."""
+the step number it was captured with (the eager twin does the same). A
+prepared list's run (zsp_gather_list_run) is captured the same way."""
 import pytest
 import torch
 
@@ -55,3 +56,39 @@ def test_capture_and_replay_matches_eager(numels, nd):
         assert_bits(np_of(out_a[:A.L.total_numel]), np_of(out_b[:B.L.total_numel]),
                     f"replay {rep}: gathered parameters")
     del g
+
+
+@pytest.mark.parametrize("n_ids", [9, 150])
+def test_prepared_list_run_under_capture(n_ids):
+    """zsp_gather_list_run captured into a graph (argument form for 9 ids,
+    records for 150): each of three replays, after an eager fused step
+    between them, gathers the current working copy, bit for bit as an eager
+    zsp_gather_many of the same list."""
+    from test_gpu_gather_list import outputs
+    from zero_sharded_mixed_pad_amd import synth
+    numels, nd = synth.small_tensor_sizes(count=160, lo=5, hi=7000, seed=21), 8
+    M = Mirror(numels, nd)
+    ids = [(7 * i) % M.L.T for i in range(n_ids)]
+    got = outputs(M, ids, torch.bfloat16)
+    want = outputs(M, ids, torch.bfloat16)
+    gl = M.plan.gather_list(ids, got, "work")
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            M.plan.gather_prepared(gl, stream=s)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        grads = [x.to(dev()) for x in M.grads(torch.bfloat16, ("graph-list", rep), poison=False)]
+        M.plan.reduce_adam_step(zsp.ALL_RANKS, grads, step=rep + 1, **HP)
+        torch.cuda.synchronize()
+        g.replay()
+        M.plan.gather_many(ids, want, "work")
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(zip(got, want)):
+            n = int(M.L.numel[ids[i]])
+            assert_bits(np_of(a[:n]), np_of(b[:n]), f"replay {rep}: entry {i}")
+    del g
+    gl.close()
