@@ -28,6 +28,7 @@
  *   full_off[t]   sum_{u<t} (numel[u] + pad[u])   (full padded layout)
  *   shard_off[t]  sum_{u<t} shard_len[u]          (a rank's shard layout)
  *   flat_off[t]   sum_{u<t} numel[u]              (unpadded concatenation)
+ *   total_numel   sum of numel over all parameters
  *   Rank r owns elements [r*s_t, (r+1)*s_t) of padded parameter t and stores
  *   them at shard_off[t] of its shard; positions >= numel[t] are pad.
  *
@@ -132,16 +133,17 @@ void zsp_destroy(zsp_plan* plan);
 /* Sizes of the plan. Any output pointer may be NULL.
  *   shard_elems  S
  *   total_padded sum of numel+pad (elements of one full-layout gradient)
- *   total_numel  sum of numel
  *   model_state_bytes_per_rank  16*S: 16-bit param + 16-bit grad + fp32
- *     master + fp32 m + fp32 v per owned element ([ZS3] equation M_Stage3). */
+ *     master + fp32 m + fp32 v per owned element ([ZS3] equation M_Stage3).
+ * total_numel and flat_off[t] (see Terms) follow from the numel list. */
 zsp_status zsp_plan_info(const zsp_plan* plan, int64_t* shard_elems, int64_t* total_padded,
-                         int64_t* total_numel, int64_t* model_state_bytes_per_rank);
+                         int64_t* model_state_bytes_per_rank);
 
-/* Layout of parameter t (0 <= t < n_params). Any output pointer may be NULL. */
+/* Layout of parameter t (0 <= t < n_params). Any output pointer may be NULL.
+ * full_off: its offset in a full-layout gradient; shard_off: its slot's
+ * offset in each rank's shard. */
 zsp_status zsp_plan_tensor(const zsp_plan* plan, int32_t t, int64_t* numel, int64_t* pad,
-                           int64_t* shard_len, int64_t* full_off, int64_t* shard_off,
-                           int64_t* flat_off);
+                           int64_t* shard_len, int64_t* full_off, int64_t* shard_off);
 
 /* Bind the caller-owned optimizer state and build the device tables.
  *   rank_or_all = ZSP_ALL_RANKS: every array holds n_d*S elements (all ranks

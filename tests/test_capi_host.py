@@ -52,7 +52,7 @@ def test_layout_tables_match_oracle(numels, nd):
     info = plan.info()
     assert info["shard_elems"] == L.S
     assert info["total_padded"] == L.total_padded
-    assert info["total_numel"] == L.total_numel
+    assert plan.total_numel == L.total_numel
     assert info["model_state_bytes_per_rank"] == oracle.model_state_bytes(L.S)
     for t in range(len(numels)):
         d = plan.tensor(t)
@@ -100,8 +100,8 @@ def test_query_errors():
     plan = zsp.partition([5, 6], 3)
     assert _status(zsp.zsp_plan_tensor, plan.handle, 2) == binding.ERANGE
     assert _status(zsp.zsp_plan_tensor, plan.handle, -1) == binding.ERANGE
-    assert lib.zsp_plan_info(None, None, None, None, None) == binding.EINVAL
-    assert lib.zsp_plan_info(plan.handle, None, None, None, None) == binding.OK
+    assert lib.zsp_plan_info(None, None, None, None) == binding.EINVAL
+    assert lib.zsp_plan_info(plan.handle, None, None, None) == binding.OK
     lib.zsp_destroy(None)  # ignored
     plan.destroy()
 
@@ -175,7 +175,7 @@ if given is not None:
         plan = zsp.partition(numels, nd)
         L = oracle.Layout(numels, nd)
         info = plan.info()
-        assert (info["shard_elems"], info["total_padded"], info["total_numel"]) == (
+        assert (info["shard_elems"], info["total_padded"], plan.total_numel) == (
             L.S, L.total_padded, L.total_numel)
         for t in range(len(numels)):
             d = plan.tensor(t)

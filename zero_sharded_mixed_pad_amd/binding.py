@@ -43,8 +43,8 @@ def _load():
     sigs = {
         "zsp_partition": (i32, [i64p, i32, i32, ctypes.POINTER(vp)]),
         "zsp_destroy": (None, [vp]),
-        "zsp_plan_info": (i32, [vp, i64p, i64p, i64p, i64p]),
-        "zsp_plan_tensor": (i32, [vp, i32, i64p, i64p, i64p, i64p, i64p, i64p]),
+        "zsp_plan_info": (i32, [vp, i64p, i64p, i64p]),
+        "zsp_plan_tensor": (i32, [vp, i32, i64p, i64p, i64p, i64p, i64p]),
         "zsp_bind_state": (i32, [vp, i32, vp, vp, vp, vp, vp]),
         "zsp_load_params": (i32, [vp, vp, i32, vp]),
         "zsp_reduce_shard": (i32, [vp, i32, vpp, i32, i32, i32, vp]),
@@ -163,16 +163,16 @@ def zsp_destroy(h):
 
 
 def zsp_plan_info(h):
-    out = [ctypes.c_int64() for _ in range(4)]
+    out = [ctypes.c_int64() for _ in range(3)]
     _check(lib.zsp_plan_info(h, *[ctypes.byref(o) for o in out]))
-    return dict(zip(("shard_elems", "total_padded", "total_numel",
-                     "model_state_bytes_per_rank"), (o.value for o in out)))
+    return dict(zip(("shard_elems", "total_padded", "model_state_bytes_per_rank"),
+                    (o.value for o in out)))
 
 
 def zsp_plan_tensor(h, t):
-    out = [ctypes.c_int64() for _ in range(6)]
+    out = [ctypes.c_int64() for _ in range(5)]
     _check(lib.zsp_plan_tensor(h, int(t), *[ctypes.byref(o) for o in out]))
-    return dict(zip(("numel", "pad", "shard_len", "full_off", "shard_off", "flat_off"),
+    return dict(zip(("numel", "pad", "shard_len", "full_off", "shard_off"),
                     (o.value for o in out)))
 
 
@@ -490,7 +490,10 @@ class Plan:
         info = zsp_plan_info(self._h)
         self.S = info["shard_elems"]
         self.total_padded = info["total_padded"]
-        self.total_numel = info["total_numel"]
+        self.total_numel = sum(self.numel)
+        self.flat_off = [0]
+        for n in self.numel:
+            self.flat_off.append(self.flat_off[-1] + n)
         self.model_state_bytes_per_rank = info["model_state_bytes_per_rank"]
         self._bound = None
         self._bound_rank = None
@@ -520,7 +523,11 @@ class Plan:
         return zsp_plan_info(self._h)
 
     def tensor(self, t):
-        return zsp_plan_tensor(self._h, t)
+        """Parameter t's layout (zsp_plan_tensor), with flat_off: its offset
+        in the unpadded concatenation."""
+        d = zsp_plan_tensor(self._h, t)
+        d["flat_off"] = self.flat_off[t]
+        return d
 
     # The C calls take raw pointers and cannot see buffer sizes; these methods
     # check every tensor against the plan before anything is launched.

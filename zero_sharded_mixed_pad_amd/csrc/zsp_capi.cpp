@@ -229,19 +229,17 @@ void zsp_destroy(zsp_plan* plan) {
 }
 
 zsp_status zsp_plan_info(const zsp_plan* P, int64_t* shard_elems, int64_t* total_padded,
-                         int64_t* total_numel, int64_t* model_state_bytes_per_rank) {
+                         int64_t* model_state_bytes_per_rank) {
     if (!P) return fail(ZSP_EINVAL, "plan is NULL");
     if (shard_elems) *shard_elems = P->S;
     if (total_padded) *total_padded = P->total_padded;
-    if (total_numel) *total_numel = P->total_numel;
     // 2 (16-bit param) + 2 (16-bit grad) + 4 (fp32 master) + 4 (m) + 4 (v)
     if (model_state_bytes_per_rank) *model_state_bytes_per_rank = 16 * P->S;
     return ZSP_OK;
 }
 
 zsp_status zsp_plan_tensor(const zsp_plan* P, int32_t t, int64_t* numel, int64_t* pad,
-                           int64_t* shard_len, int64_t* full_off, int64_t* shard_off,
-                           int64_t* flat_off) {
+                           int64_t* shard_len, int64_t* full_off, int64_t* shard_off) {
     if (!P) return fail(ZSP_EINVAL, "plan is NULL");
     if (t < 0 || t >= P->T) return fail(ZSP_ERANGE, "parameter %d outside [0, %d)", t, P->T);
     if (numel) *numel = P->numel[t];
@@ -249,7 +247,6 @@ zsp_status zsp_plan_tensor(const zsp_plan* P, int32_t t, int64_t* numel, int64_t
     if (shard_len) *shard_len = P->shard_len[t];
     if (full_off) *full_off = P->full_off[t];
     if (shard_off) *shard_off = P->shard_off[t];
-    if (flat_off) *flat_off = P->flat_off[t];
     return ZSP_OK;
 }
 
