@@ -153,7 +153,7 @@ struct ShardArgs {
     const int64_t* e0;
     const PieceInfo* info;
     const int32_t* tile;
-    int64_t tile_first, e_begin, e_end;
+    int64_t tile_first, tile_end, e_begin, e_end;
     int64_t glen;  // elements of each gradient buffer
     float* master;
     float* m;
@@ -712,19 +712,39 @@ __device__ __forceinline__ void quad_one(const ShardArgs<CAP>& a, int64_t E, int
     }
 }
 
+// Workgroups go to the 8 XCDs in turn (workgroup b to XCD b % 8), each XCD
+// with an L2 of its own. Launches over short pieces give each XCD runs of
+// kXcdRun consecutive tiles instead: a cache line that two neighbouring
+// tiles share (a piece starts at any element offset) is then fetched once,
+// into the L2 of the XCD that runs both. The grid is rounded up to whole
+// rounds of 8 runs; xcd_run_tile maps workgroup b to its tile.
+constexpr int kXcdRun = 16;
+
+__device__ __forceinline__ int64_t xcd_run_tile(int64_t b) {
+    const int64_t x = b % 8, i = b / 8;
+    return ((i / kXcdRun) * 8 + x) * kXcdRun + (i % kXcdRun);
+}
+
 // W waves per tile: W = 1, the wave takes both quads of each lane; W = 2,
 // workgroup 2i + h takes quad h (elements 256h .. 256h + 255) of tile i.
-// TG: the gradients are read with ordinary (L2-allocating) loads instead of
-// non-temporal ones. Launches over short pieces use it: there a tile's
-// gradient runs start mid-line, and the line a run shares with the next
-// tile's run can then still be in L2 when that tile reads it.
+// TG: launches over short pieces. Their gradients are read with ordinary
+// (L2-allocating) loads instead of non-temporal ones, and their tiles go
+// to the XCDs in runs (xcd_run_tile): a tile's gradient runs start
+// mid-line, and the line a run shares with the next tile's run is then
+// still in that XCD's L2 when the next tile reads it. Runs of 16 tiles cut
+// the 10,000-tensor fused step's read excess from +11.5% to +4.1% (all
+// bytes: +7.7% to +2.7%) for 0.7% of its time.
 template <int OP, typename GT, int CAP, int W, bool TG>
 __global__ __launch_bounds__(kWaveLanes) void shard_kernel(const ShardArgs<CAP> a) {
     static_assert(W == 1 || W == 2, "one or two waves per tile");
     __shared__ int64_t s_e0[kStage];
     __shared__ PieceInfo s_info[kStage];
     const int lane = threadIdx.x;
-    const int64_t tile = a.tile_first + blockIdx.x / W;
+    int64_t tile = a.tile_first + blockIdx.x / W;
+    if constexpr (W == 1 && TG) {
+        tile = a.tile_first + xcd_run_tile(blockIdx.x);
+        if (tile >= a.tile_end) return;  // the grid is rounded up to 8 runs
+    }
     const int hw = W == 2 ? int(blockIdx.x % 2) : 0;
     const int64_t E0 = tile * kTile + int64_t(lane) * kQuad;
     // Wave-uniform bracket of the tile's pieces (scalar loads).
@@ -836,10 +856,9 @@ constexpr int kPick = 8;
 // a piece starts at any element offset, so its first and last cache lines
 // are shared with the neighbouring pieces, which neighbouring tiles read.
 // Such launches load their sources with ordinary (L2-allocating) loads and
-// give each XCD runs of kXcdRun consecutive tiles (workgroup b runs on XCD
-// b % 8), so a shared line is fetched once into that XCD's L2. Long pieces
-// keep non-temporal loads and the plain order: each line is read once.
-constexpr int kXcdRun = 16;
+// give each XCD runs of kXcdRun consecutive tiles (xcd_run_tile), so a shared
+// line is fetched once into that XCD's L2. Long pieces keep non-temporal
+// loads and the plain order: each line is read once.
 
 template <bool SHORT>
 __device__ __forceinline__ u32x4 ld_src(const u32x4_a2* p) {
@@ -1028,8 +1047,7 @@ __global__ __launch_bounds__(kWaveLanes) void gather_kernel(const GatherArgs a) 
     __shared__ int64_t s_delta[kStage];
     int64_t tile = blockIdx.x;
     if constexpr (SHORT) {
-        const int64_t x = tile % 8, i = tile / 8;
-        tile = ((i / kXcdRun) * 8 + x) * kXcdRun + (i % kXcdRun);
+        tile = xcd_run_tile(tile);
         if (tile * kTile >= a.count) return;  // the grid is rounded up to 8 runs
     }
     gather_tile<T, SHORT>(a, tile, threadIdx.x, s_k0, s_delta);
@@ -1118,8 +1136,7 @@ __device__ __forceinline__ void copy_rec_tile(const TileRec& rc, const T* src, i
 template <bool SHORT>
 __device__ __forceinline__ int64_t list_tile(int64_t blk, int64_t tiles) {
     if constexpr (SHORT) {
-        const int64_t x = blk % 8, i = blk / 8;
-        const int64_t t = ((i / kXcdRun) * 8 + x) * kXcdRun + (i % kXcdRun);
+        const int64_t t = xcd_run_tile(blk);
         return t < tiles ? t : -1;
     } else {
         return blk;
@@ -1316,6 +1333,7 @@ hipError_t launch_t(const ShardLaunch& L, hipStream_t stream) {
     a.e_end = L.e_end;
     a.tile_first = L.e_begin / kTile;
     const int64_t tile_end = (L.e_end + kTile - 1) / kTile;
+    a.tile_end = tile_end;
     a.master = L.master;
     a.m = L.m;
     a.v = L.v;
@@ -1344,8 +1362,10 @@ hipError_t launch_t(const ShardLaunch& L, hipStream_t stream) {
     const size_t lds_pad = shard_lds_pad<OP, GT, CAP, 1>(L, tiles);
     if constexpr (kTemporalShort<OP, CAP>) {
         if (L.short_pieces) {
+            const int64_t grid = (tiles + 8 * kXcdRun - 1) / (8 * kXcdRun) * (8 * kXcdRun);
+            if (grid > kMaxBlocks) return hipErrorInvalidValue;
             hipLaunchKernelGGL((shard_kernel<OP, GT, CAP, 1, true>),
-                               dim3(static_cast<uint32_t>(tiles)), dim3(kWaveLanes), lds_pad,
+                               dim3(static_cast<uint32_t>(grid)), dim3(kWaveLanes), lds_pad,
                                stream, a);
             return hipGetLastError();
         }
