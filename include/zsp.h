@@ -68,13 +68,14 @@
  *   recent failure. Values are not checked: NaN and Inf propagate.
  *
  * Threads
- *   The reduce, Adam and gather calls (whole-model and _params forms) and
- *   zsp_load_params only read the plan (zsp_gather_many takes the plan's
- *   staging slots under a lock of their own): several threads may issue
- *   them on one plan at once, e.g. one thread per rank, each on its own
- *   stream (work that writes the same state at the same time is the
- *   caller's race, as for any two kernels). zsp_bind_state, the checkpoint calls and
- *   zsp_destroy change the plan and must not overlap any other call on it.
+ *   The reduce, Adam and gather calls (whole-model and _params forms, list
+ *   gathers, prepared-list create and run) and zsp_load_params only read
+ *   the plan (zsp_gather_many takes the plan's staging slots under a lock
+ *   of their own): several threads may issue them on one plan at once, e.g.
+ *   one thread per rank, each on its own stream (work that writes the same
+ *   state at the same time is the caller's race, as for any two kernels).
+ *   zsp_bind_state, the checkpoint calls and zsp_destroy change the plan
+ *   and must not overlap any other call on it.
  *   A schedule's calls must not overlap one another; other schedules and
  *   the read-only calls above may run beside them. Different plans are
  *   independent.

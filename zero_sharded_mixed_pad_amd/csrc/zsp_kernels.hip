@@ -18,8 +18,11 @@
 //    elements instead makes each fp32 instruction touch every other 16 bytes
 //    of a 2 KiB run, which measured ~5% slower.
 //  * Every stream is touched once per launch, so global loads and stores
-//    carry the non-temporal hint; that measured a further ~5%. The one
-//    exception is the gather over short pieces (below).
+//    carry the non-temporal hint; that measured a further ~5%. The
+//    exceptions are launches over short pieces (many parameters of a few
+//    thousand elements): their gradient or source loads are ordinary ones,
+//    and their tiles go to the XCDs in runs, so a cache line two
+//    neighbouring tiles share is fetched once (xcd_run_tile).
 //  * The optimizer state of the wave's quads is loaded before the gradients
 //    so the state's latency overlaps the rank loop.
 //  * The tile's parameter comes from a per-tile table: wave-uniform, so the
@@ -32,8 +35,10 @@
 //    the quads (each parameter is padded on its own, so slices do not line
 //    up). gfx9 global memory serves unaligned vector loads, so the fast path
 //    stays one vector load per quad. Quads that cross a parameter or pad
-//    boundary keep vector state access and mask per element; only quads at
-//    the edge of a launch's range go element by element.
+//    boundary keep vector state access and mask per element (reading both
+//    pieces' gradient vectors when they cross into the next piece); only
+//    quads meeting three pieces or the edge of a launch's range go element
+//    by element.
 //  * The reduce over N_d ranks keeps each lane's 4 or 8 sums in registers
 //    and adds rank r's values strictly after rank r-1's (fixed order,
 //    bit-exact); the ranks are loaded 8 at a time (16 at a time for more
