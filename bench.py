@@ -55,14 +55,25 @@ KERNEL_SOURCES = ["zero_sharded_mixed_pad_amd/csrc/zsp_kernels.hip",
                   "zero_sharded_mixed_pad_amd/csrc/zsp_internal.hpp"]
 
 
+def _code_only(text):
+    """C++ source without its comments and with runs of white space folded,
+    so that editing a comment leaves the hash alone (string literals in the
+    kernel sources hold no comment markers)."""
+    import re
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_hash():
-    """Hash of what determines the kernels' code: their source, its header and
-    the device compile flags (other library sources do not enter it)."""
+    """Hash of what determines the kernels' code: their source and header
+    (comments aside) and the device compile flags (other library sources do
+    not enter it)."""
     import importlib.util
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, p), encoding="utf-8") as f:
+            h.update(_code_only(f.read()).encode())
     spec = importlib.util.spec_from_file_location(
         "_zsp_build_flags", os.path.join(ROOT, "zero_sharded_mixed_pad_amd", "_build.py"))
     mod = importlib.util.module_from_spec(spec)
