@@ -490,3 +490,60 @@ def test_all_empty_plan(tmp_path):
     assert torch.all(out.float() == 3.0)
     plan.destroy()
     other.destroy()
+
+
+# Layouts for the batched multi-piece path of short-piece launches (up to 16
+# ranks, whole tiles): quads crossing into the next piece (two gradient
+# vectors), quads crossing a pad boundary, quads meeting three pieces
+# (slices under 4 elements), a crossing at the start of a rank's region whose
+# next piece's gradient starts within 3 elements of the buffer's start, and
+# one near the buffer's end; every piece boundary offset mod 4 occurs.
+MULTI_PIECE = {
+    "tiny_first": ([1, 1, 2, 3] + [37 + 11 * i for i in range(60)] + [5], 8),
+    # s_0 = 2 and S = 3 mod 4: the quad that starts 3 elements before rank
+    # 1's region crosses into that rank's slice of parameter 0, whose
+    # gradient starts at element 2 of the buffer
+    "region_start": ([16] + [37 + 11 * i for i in range(60)] + [25], 8),
+    "tiny_last": ([700 + 13 * i for i in range(50)] + [3, 13], 8),
+    "boundaries_mod4": ([4 * k + r for k in range(30, 70) for r in range(4)], 5),
+    "sixteen": (synth.small_tensor_sizes(count=250, lo=2, hi=4000, seed=31), 16),
+    "eight_small": (synth.small_tensor_sizes(count=400, lo=1, hi=900, seed=32), 8),
+}
+
+
+@pytest.mark.parametrize("which", list(MULTI_PIECE))
+@pytest.mark.parametrize("layout", ["full", "shard"])
+def test_multi_piece_quads_every_op(which, layout):
+    numels, nd = MULTI_PIECE[which]
+    print(f"\n[multi-piece quads] {which}, {layout} layout", flush=True)
+    M = Mirror(numels, nd)
+    d = dev()
+    g0 = M.grads(torch.bfloat16, ("mp0", which), layout=layout)
+    M.plan.reduce_shard(zsp.ALL_RANKS, [g.to(d) for g in g0], layout=layout)
+    for j in M.ranks:
+        M.o_acc[M.o_slice(j)] = M.o_reduce(j, g0, layout)
+    M.check_acc("reduce set")
+    g1 = M.grads(torch.bfloat16, ("mp1", which), layout=layout)
+    M.plan.reduce_shard(zsp.ALL_RANKS, [g.to(d) for g in g1], layout=layout, accumulate=True)
+    for j in M.ranks:
+        oracle.accumulate(M.o_acc[M.o_slice(j)], M.o_reduce(j, g1, layout))
+    M.check_acc("reduce accumulate")
+    g2 = M.grads(torch.bfloat16, ("mp2", which), layout=layout)
+    M.plan.reduce_adam_step(zsp.ALL_RANKS, [g.to(d) for g in g2], step=1, layout=layout,
+                            use_acc=True, **HP)
+    for j in M.ranks:
+        acc = M.o_acc[M.o_slice(j)].copy()
+        oracle.accumulate(acc, M.o_reduce(j, g2, layout))
+        M.o_adam(j, acc, 1)
+    assert M.check_state("fused with the accumulator") == 0
+    for step in (2, 3):
+        gs = M.grads(torch.float32, ("mp", which, step), layout=layout)
+        M.plan.reduce_adam_step(zsp.ALL_RANKS, [g.to(d) for g in gs], step=step, layout=layout,
+                                **HP)
+        for j in M.ranks:
+            M.o_adam(j, M.o_reduce(j, gs, layout), step)
+        assert M.check_state(f"fused step {step} (fp32 gradients)") == 0
+    M.plan.adam_step(zsp.ALL_RANKS, step=4, **HP)
+    for j in M.ranks:
+        M.o_adam(j, M.o_acc[M.o_slice(j)].copy(), 4)
+    assert M.check_state("adam from the accumulator") == 0
