@@ -23,6 +23,7 @@ LAYOUT = "tests/test_oracle_layout.py"
 REDUCE = "tests/test_oracle_reduce.py"
 ADAM = "tests/test_oracle_adam.py"
 STAGES = "tests/test_oracle_stages.py"
+BRUTE = "tests/test_oracle_brute.py"
 
 MUTANTS = [
     ("stage 1 shards the gradients too", "const int64_t grads_n = stage >= 2 ? shard_elems : psi;",
@@ -82,6 +83,15 @@ MUTANTS = [
     ("adam updates pad slots",
      "if (k >= numel[t]) continue;\n            int64_t e = L.shard_off[t] + i;\n            adam_one",
      "int64_t e = L.shard_off[t] + i;\n            adam_one", ADAM),
+    # differences of one rounding, inside every bound above: the second
+    # implementation (bit for bit) is what catches them
+    ("update divides before scaling by lr", "float update = (lr * mhat) / denom;",
+     "float update = lr * (mhat / denom);", BRUTE),
+    ("g squared after scaling", "omb2 * (g * g)", "(omb2 * g) * g", BRUTE),
+    ("bias correction through a reciprocal", "float mhat = m_new / bc1;",
+     "float mhat = m_new * (1.0f / bc1);", BRUTE),
+    ("bias corrections in fp32", "out4[2] = (float)(1.0 - pow((double)b1, (double)step));",
+     "out4[2] = 1.0f - powf(b1, (float)step);", BRUTE),
 ]
 
 
