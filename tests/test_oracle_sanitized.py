@@ -12,7 +12,8 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 sys.path.insert(0, ROOT)
 PINS = ["tests/test_oracle_layout.py", "tests/test_oracle_reduce.py",
-        "tests/test_oracle_adam.py", "tests/test_oracle_stages.py"]
+        "tests/test_oracle_adam.py", "tests/test_oracle_stages.py",
+        "tests/test_oracle_brute.py"]
 
 
 def asan_runtime():
