@@ -122,3 +122,30 @@ def test_steps_agree_bit_for_bit(numel, nd, special, with_acc):
                 nan_b = np.isnan(oracle.bf16_to_f32(wb))
                 assert np.array_equal(nan_o, nan_b) and np.array_equal(wo[~nan_o], wb[~nan_b]), \
                     f"work, {what}"
+
+
+try:
+    from hypothesis import given, settings, strategies as st
+except ImportError:  # the property test below needs hypothesis
+    given = None
+
+if given is not None:
+    @settings(max_examples=300, deadline=None)
+    @given(numel=st.lists(st.integers(0, 300), min_size=1, max_size=12),
+           nd=st.integers(1, 17))
+    def test_layout_tables_agree_on_random_lists(numel, nd):
+        """Random parameter lists: the oracle's tables equal those read off the
+        padded, sliced index lists, and every owner position maps to the
+        element the slices give it."""
+        L = oracle.Layout(numel, nd)
+        B = brute.layout(numel, nd)
+        assert (list(L.pad), list(L.shard_len), list(L.full_off), list(L.shard_off),
+                list(L.flat_off), L.S) == (B["pad"], B["shard_len"], B["full_off"],
+                                           B["shard_off"], B["flat_off"], B["S"])
+        own = brute.owners(numel, nd)
+        for j in range(nd):
+            assert len(own[j]) == L.S
+            for k, o in enumerate(own[j]):
+                t, i = L.locate(k)
+                elem = int(j * L.shard_len[t] + i)     # element of parameter t held there
+                assert o == (None if elem >= numel[t] else (int(t), elem))
