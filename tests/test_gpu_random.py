@@ -130,3 +130,48 @@ def test_random_groups_update_and_schedule(seed):
             assert_bits(np_of(caps[p][i]), oracle.gather(numels, nd, t, M.o_work),
                         f"{what}: schedule depth {depth}, position {p}, parameter {t}")
     s.destroy()
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_list_gathers(seed):
+    """Random layouts, rank counts and id lists (repeats, empty parameters,
+    any order, 1 to 150 entries) gathered one-shot (zsp_gather_many), without
+    allocation (zsp_gather_many_noalloc) and prepared (zsp_gather_list_*), from
+    the work copy or the master, after a fused step: each output equals the
+    oracle's gather of its parameter, bit for bit."""
+    rng = np.random.default_rng(20261203 + seed)
+    numels = random_numels(rng) + random_numels(rng)
+    nd = int(rng.choice([n for n in ND_CHOICES if n <= 40]))
+    source = "master" if rng.integers(0, 3) == 0 else "work"
+    n_ids = int(rng.choice([1, 5, 64, 65, 150]))
+    ids = [int(x) for x in rng.integers(0, len(numels), size=n_ids)]
+    print(f"\n[random list] seed {seed}: {len(numels)} parameters, N_d {nd}, {source}, "
+          f"{n_ids} ids", flush=True)
+    M = Mirror(numels, nd, seed=seed)
+    d = dev()
+    grads = M.grads(torch.bfloat16, ("rand-list", seed))
+    M.plan.reduce_adam_step(zsp.ALL_RANKS, [g.to(d) for g in grads], step=1, **HP)
+    for j in M.ranks:
+        M.o_adam(j, M.o_reduce(j, grads), 1)
+    dt = torch.bfloat16 if source == "work" else torch.float32
+    src = M.o_work if source == "work" else M.o_master
+    gl_outs = [torch.full((max(int(M.L.numel[t]), 1),), float("nan"), dtype=dt, device=d)
+               for t in ids]
+    gl = M.plan.gather_list(ids, gl_outs, source)
+    for form in ("many", "noalloc", "prepared"):
+        outs = gl_outs if form == "prepared" else [
+            torch.full((max(int(M.L.numel[t]), 1),), float("nan"), dtype=dt, device=d)
+            for t in ids]
+        if form == "many":
+            M.plan.gather_many(ids, outs, source)
+        elif form == "noalloc":
+            M.plan.gather_many_noalloc(ids, outs, source)
+        else:
+            M.plan.gather_prepared(gl)
+        torch.cuda.synchronize()
+        for i, (t, o) in enumerate(zip(ids, outs)):
+            n = int(M.L.numel[t])
+            if n:
+                assert_bits(np_of(o[:n]), oracle.gather(M.numels, M.nd, t, src),
+                            f"seed {seed}, {form}: entry {i} (id {t})")
+    gl.close()
