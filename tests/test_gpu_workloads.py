@@ -33,13 +33,13 @@ pytestmark = pytest.mark.gpu
 N_SAMPLES = 20000
 
 
-def sample_positions(L, w, rng):
-    """Sample positions in the bound arrays' index space and their layout
-    facts, all from the oracle's tables."""
+def sample_positions(L, w, rng, extra=()):
+    """Sample positions in the bound arrays' index space (plus the `extra`
+    ones) and their layout facts, all from the oracle's tables."""
     nd, S = w.n_d, L.S
     local = w.rank_local >= 0
     total = S if local else nd * S
-    pos = [rng.integers(0, total, size=N_SAMPLES)]
+    pos = [rng.integers(0, total, size=N_SAMPLES), np.asarray(extra, np.int64)]
     # first and last slot of up to 2000 pieces (rank j's slice of tensor t)
     T = L.T
     ts = rng.integers(0, T, size=min(2000, T * (1 if local else nd)))
@@ -182,6 +182,74 @@ def test_workload_full_size(name):
                 got = take(out, sp["flat"][sel] - lo)
                 assert_bits(got, after[3][sel], "gather after step vs work")
     assert worst == 0, f"{name}: not bit-exact, max ulp {worst}"
+
+
+def test_steps_beyond_32bit_indices():
+    """32 Llama-7B layers plus one odd-sized tensor (one pad slot) at N_d = 2,
+    every rank resident: each rank's slice holds 3.24e9 elements (past 2^31)
+    and the state and gradient indices pass 2^32. A fused reduce+Adam+cast
+    step, then a reduce into the accumulator and a fused step from it (two
+    micro-batches), over all ranks; sampled master, m, v and work (random
+    positions, the first and last slot of pieces, and the slots around 2^31,
+    2^32 and the rank boundary) equal the oracle's bit for bit, and the pad
+    slot stays +0."""
+    import zero_sharded_mixed_pad_amd as zsp
+    from types import SimpleNamespace
+    torch.cuda.empty_cache()
+    stack = synth.llama_stack(32, 2)
+    w = synth.Workload("llama7b_32layers_odd_nd2", stack.numel + [4096 * 3 + 1], 2,
+                       torch.bfloat16, torch.bfloat16, 0.02, 1e-3, ones=stack.ones)
+    dev = torch.device("cuda")
+    L = oracle.Layout(w.numel, w.n_d)
+    plan = zsp.partition(w.numel, w.n_d)
+    S = plan.S
+    n = w.n_d * S
+    assert S > 2 ** 31 and n > 2 ** 32 and L.total_padded > 2 ** 32 and L.pad[-1] == 1
+    print(f"\n[beyond 2^32] S = {S}, state {n} elements", flush=True)
+    r = SimpleNamespace(w=w)
+    r.master = torch.empty(n, dtype=torch.float32, device=dev)
+    r.m = torch.empty(n, dtype=torch.float32, device=dev)
+    r.v = torch.empty(n, dtype=torch.float32, device=dev)
+    r.work = torch.empty(n, dtype=torch.bfloat16, device=dev)
+    acc = torch.empty(n, dtype=torch.float32, device=dev)
+    plan.bind_state(zsp.ALL_RANKS, r.master, r.m, r.v, r.work, acc)
+    flat = synth.flat_params(w, device=dev)
+    plan.load_params(flat)
+    del flat
+    extra = [2 ** 31 - 1, 2 ** 31, 2 ** 32 - 1, 2 ** 32, 2 ** 32 + 1, S - 1, S, S + 1,
+             S + 2 ** 31, n - 1, n - 2]
+    sp = sample_positions(L, w, np.random.default_rng(7), extra)
+    assert (sp["E"] >= 2 ** 32).sum() > 1000 and not sp["valid"][-1]
+    r.grads = [torch.empty(L.total_padded, dtype=torch.bfloat16, device=dev)
+               for _ in range(w.n_d)]
+
+    def fill(step, mb):
+        for q, g in enumerate(r.grads):
+            g.copy_(synth.grad_buffer(w, g.numel(), q, step=step, micro_batch=mb, device=dev))
+        return oracle.reduce_values(grad_values(r, sp, "full"))
+
+    hp = dict(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps)
+    before = snapshot(r, sp["E"])
+    g = fill(1, 0)
+    plan.reduce_adam_step(zsp.ALL_RANKS, r.grads, step=1, **hp)
+    torch.cuda.synchronize()
+    u1, before = compare(r, sp, before, g, 1, "fused step")
+    print(f"[beyond 2^32] fused step: max ulp {u1}", flush=True)
+    red0 = fill(2, 0)
+    plan.reduce_shard(zsp.ALL_RANKS, r.grads)
+    torch.cuda.synchronize()
+    got = take(acc, sp["E"])
+    assert_bits(got[sp["valid"]], red0, "reduce into the accumulator")
+    assert not got[~sp["valid"]].view(np.uint8).any(), "accumulator pad slot not +0"
+    red1 = fill(2, 1)
+    plan.reduce_adam_step(zsp.ALL_RANKS, r.grads, step=2, use_acc=True, **hp)
+    torch.cuda.synchronize()
+    u2, _ = compare(r, sp, before, oracle.accumulate(red0, red1), 2, "fused step from acc")
+    print(f"[beyond 2^32] fused step from the accumulator: max ulp {u2}", flush=True)
+    assert u1 == 0 and u2 == 0
+    plan.destroy()
+    del r, acc
+    torch.cuda.empty_cache()
 
 
 def test_small_workload_every_element():
