@@ -134,8 +134,8 @@ class Runner:
     stage ("ZeRO Stages: ...", stage sections):
       3: fused reduce-scatter + Adam, then each layer gathered before forward
          and again before backward (two gathers per step);
-      2: the same reduction and update, then one all-gather of the updated
-         parameters (the replica forward and backward use);
+      2: the same reduction and update, then every rank's new slice is
+         gathered back into the full copy that forward and backward read;
       1: the gradients all-reduced -- reduce-scatter into the accumulator,
          then its all-gather into a full fp32 gradient replica -- Adam from
          each rank's received slice, then the parameter all-gather.

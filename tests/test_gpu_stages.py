@@ -3,7 +3,7 @@ Sharding Optimizer State, Gradients, and Parameters", stage 1 and stage 2
 sections), against the oracle and against the stage-3 path:
   stage 1: reduce-scatter into the accumulator, all-gather of it (the
            all-reduced gradient every rank holds), Adam from each rank's
-           slice, all-gather of the updated parameters;
+           slice, then each rank's new slice gathered into the full copy;
   stage 2: fused reduce-scatter + Adam, one all-gather of the parameters;
   stage 3: fused reduce-scatter + Adam (per-layer gathers happen around
            compute, not here).
