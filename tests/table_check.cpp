@@ -2,7 +2,9 @@
 // tables with the library's own host code (zsp_layout.cpp) and verifies
 // every property the kernels' indexing relies on, so that no kernel can
 // address memory outside its buffers. Input on stdin: nd rank T numel...
-// (rank -1 = all ranks). Prints "ok" or the first violated property.
+// [force] (rank -1 = all ranks; force = 1 builds span tables for any
+// layout). Prints "ok <pieces> pieces <spans> spans" or the first violated
+// property.
 #include <algorithm>
 #include <cstdio>
 #include <vector>
@@ -28,6 +30,124 @@ static int check_tiles(const std::vector<int64_t>& starts, const std::vector<int
         if (p < 0 || p >= n) return bad("tile entry out of range", g, p);
         if (!(starts[p] <= x && x < starts[p + 1])) return bad("tile entry misses", g, p);
     }
+    return 0;
+}
+
+// Span tables: spans cover every tile in order within the limits, each
+// rank run stays inside the source array, and the span gather's addressing
+// -- run chunks into LDS, then per element its piece's offset, found as the
+// kernel finds it -- reads, for every flat index K, source element
+// K + delta(piece of K).
+static int check_spans(const HostGatherTable& g, int64_t S, int64_t nd) {
+    if (g.spans.empty()) {
+        if (!g.span_runs.empty() || !g.span_segs.empty() || !g.tile_segs.empty())
+            return bad("span parts without spans", 0, 0);
+        return 0;
+    }
+    const int64_t total = g.total, ntile = (total + kTile - 1) / kTile;
+    const int64_t C = kSpanChunkElems, src_elems = nd * S;
+    const int64_t src_chunks = (src_elems + C - 1) / C;
+    if (int64_t(g.tile_segs.size()) != ntile) return bad("tile_segs size", g.tile_segs.size(), ntile);
+    int64_t next_tile = 0, runs = 0, segs = 0;
+    std::vector<int64_t> lds_src;  // source element of each LDS element
+    for (size_t i = 0; i < g.spans.size(); ++i) {
+        const SpanRec& R = g.spans[i];
+        if (R.k_a != next_tile * kTile) return bad("span start", int64_t(i), R.k_a);
+        if (R.tiles < 1 || R.tiles > kSpanTiles) return bad("span tiles", int64_t(i), R.tiles);
+        if (R.chunks < 1 || R.chunks > kSpanChunks) return bad("span chunks", int64_t(i), R.chunks);
+        if (R.nseg < 1 || R.nseg > kSpanSegs) return bad("span pieces", int64_t(i), R.nseg);
+        if (R.nrun < 1 || R.nrun > kSpanRuns) return bad("span runs", int64_t(i), R.nrun);
+        if (R.run_first != runs || R.seg_first != segs) return bad("span table order", int64_t(i), R.run_first);
+        runs += R.nrun;
+        segs += R.nseg;
+        if (runs > int64_t(g.span_runs.size()) || segs > int64_t(g.span_segs.size()))
+            return bad("span tables short", runs, segs);
+        next_tile += R.tiles;
+        if (next_tile > ntile) return bad("spans past the last tile", int64_t(i), next_tile);
+        // every span of a small table; of a large one the first and last
+        // 512 and every seventh
+        const size_t ns = g.spans.size();
+        const bool full_check = ns <= 4096 || i < 512 || i + 512 >= ns || i % 7 == 0;
+        lds_src.assign(size_t(R.chunks * C), -1);
+        int32_t at = 0;
+        for (int32_t q = 0; q < R.nrun; ++q) {
+            const SpanRun& U = g.span_runs[size_t(R.run_first + q)];
+            if (U.lds0 != at || U.nchunk < 1) return bad("run placement", q, U.lds0);
+            if (U.chunk0 < 0 || U.chunk0 + U.nchunk > src_chunks) return bad("run outside source", q, U.chunk0);
+            for (int64_t c = 0; c < U.nchunk; ++c)
+                for (int64_t e = 0; e < C; ++e)
+                    lds_src[size_t((at + c) * C + e)] = (U.chunk0 + c) * C + e;
+            at += U.nchunk;
+        }
+        if (at != R.chunks) return bad("run chunks", int64_t(i), at);
+        const SpanSeg* sg = &g.span_segs[size_t(R.seg_first)];
+        for (int32_t j = 0; j < R.nseg; ++j) {
+            if (sg[j].k < 0 || sg[j].k >= R.tiles * kTile) return bad("piece start", j, sg[j].k);
+            if (j > 0 && sg[j].k <= sg[j - 1].k) return bad("pieces unordered", j, sg[j].k);
+        }
+        if (sg[0].k != 0) return bad("first piece of span", int64_t(i), sg[0].k);
+        for (int32_t tau = 0; tau < R.tiles && full_check; ++tau) {
+            const int64_t gt = R.k_a / kTile + tau;
+            const int lo = int(g.tile_segs[size_t(gt)] & 0xffffu), hi = int(g.tile_segs[size_t(gt)] >> 16);
+            if (lo > hi || hi >= R.nseg) return bad("tile pieces", gt, lo);
+            const int64_t kl_last = std::min<int64_t>(total - R.k_a, R.tiles * kTile) - 1;
+            for (int lane = 0; lane < kWaveLanes; ++lane) {
+                const int64_t kl = int64_t(tau) * kTile + lane * C;
+                // the kernel's search: binary over [lo, hi], then forward
+                // (lanes past the end search from the last element)
+                const int64_t kls = std::min(kl, kl_last);
+                int s = lo;
+                for (int h = hi; s < h;) {
+                    const int mid = (s + h + 1) >> 1;
+                    if (sg[mid].k <= kls) s = mid;
+                    else h = mid - 1;
+                }
+                for (int64_t e = 0; e < C; ++e) {
+                    const int64_t K = std::min(kl + e, kl_last);
+                    while (s < hi && sg[s + 1].k <= K) ++s;
+                    const int64_t pos = K + sg[s].off;
+                    if (pos < 0 || pos >= int64_t(lds_src.size())) return bad("LDS index", R.k_a + K, pos);
+                    const int64_t Kg = R.k_a + K;
+                    const int64_t p = int64_t(std::upper_bound(g.k0.begin(), g.k0.end() - 1, Kg) -
+                                              g.k0.begin()) - 1;
+                    if (lds_src[size_t(pos)] != Kg + g.delta[size_t(p)])
+                        return bad("span element source", Kg, lds_src[size_t(pos)]);
+                }
+            }
+        }
+    }
+    if (next_tile != ntile) return bad("spans cover the tiles", next_tile, ntile);
+    // device records: the same spans, packed as the kernel reads them; its
+    // chunk-to-run choice (last run whose LDS start is at or below the chunk)
+    // names the run holding every chunk
+    if (g.wspans.size() != g.spans.size()) return bad("span records", g.wspans.size(), g.spans.size());
+    for (size_t i = 0; i < g.spans.size(); ++i) {
+        const SpanRec& R = g.spans[i];
+        const WaveSpan& w = g.wspans[i];
+        if (w.k_a != R.k_a || w.seg_first != R.seg_first || w.chunks != R.chunks ||
+            w.nrun != R.nrun || w.nseg != R.nseg || w.ntile != R.tiles)
+            return bad("span record header", int64_t(i), w.k_a);
+        for (int32_t t = 0; t < R.tiles; ++t) {
+            const uint32_t ts = g.tile_segs[size_t(R.k_a / kTile + t)];
+            const uint64_t pair = (w.tseg[t / 4] >> (16 * (t % 4))) & 0xffffu;
+            if ((pair & 0xff) != (ts & 0xffffu) || (pair >> 8) != (ts >> 16))
+                return bad("span record pieces", int64_t(i), t);
+        }
+        for (int32_t c = 0; c < R.chunks; ++c) {
+            int64_t gd = w.chunk0[0] - w.lds0[0];
+            for (int q = 1; q < kSpanRuns && q < w.nrun; ++q)
+                if (c >= w.lds0[q]) gd = w.chunk0[q] - w.lds0[q];
+            // the generic run holding chunk c
+            int64_t want = -1;
+            for (int32_t q = 0; q < R.nrun; ++q) {
+                const SpanRun& U = g.span_runs[size_t(R.run_first + q)];
+                if (c >= U.lds0 && c < U.lds0 + U.nchunk) want = U.chunk0 + (c - U.lds0);
+            }
+            if (c + gd != want) return bad("span record chunk", int64_t(i), c);
+        }
+    }
+    if (runs != int64_t(g.span_runs.size()) || segs != int64_t(g.span_segs.size()))
+        return bad("span tables long", runs, segs);
     return 0;
 }
 
@@ -106,6 +226,18 @@ int main() {
             }
         }
     }
-    std::printf("ok %lld pieces\n", (long long)np);
+    long long nspan = 0;
+    if (rank < 0) {
+        HostGatherTable hg;
+        build_gather_table(numel, sl, so, flo, S, int32_t(nd), hg);
+        // span tables where the library builds them (short-piece layouts),
+        // or of any layout when a nonzero value follows the sizes
+        long long force = 0;
+        if (std::scanf("%lld", &force) != 1) force = 0;
+        if (force || wants_span_table(hg)) build_span_table(S, int32_t(nd), hg);
+        if (check_spans(hg, S, nd)) return 1;
+        nspan = (long long)hg.spans.size();
+    }
+    std::printf("ok %lld pieces %lld spans\n", (long long)np, nspan);
     return 0;
 }

@@ -1,10 +1,13 @@
 """The library's offset tables satisfy every property its kernels index by
 (CPU only): pieces ordered and non-empty, every gradient / parameter /
 gather source range inside its buffer, each tile-table entry naming the
-piece that holds the tile's first element, and the gather's per-tile deltas
-and two-piece records matching a search of the piece starts. Built from the
-library's own host code with g++ (AddressSanitizer and UBSan on) and driven
-over small edge cases, seeded random layouts and the full workloads."""
+piece that holds the tile's first element, the gather's per-tile deltas
+and two-piece records matching a search of the piece starts, and the span
+gather's records, whose addressing (runs into LDS, then each element's
+piece offset, found as the kernel finds it) is emulated for every element.
+Built from the library's own host code with g++ (AddressSanitizer and UBSan
+on) and driven over small edge cases, seeded random layouts and the full
+workloads."""
 import os
 import subprocess
 
@@ -28,13 +31,17 @@ def checker(tmp_path_factory):
     return exe
 
 
-def run(exe, numels, nd, rank):
+def run(exe, numels, nd, rank, force_spans=False):
+    """Check the tables of one layout; returns the number of spans."""
     inp = f"{nd} {rank} {len(numels)} " + " ".join(str(n) for n in numels)
+    if force_spans:
+        inp += " 1"
     env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:verify_asan_link_order=0")
     res = subprocess.run([exe], input=inp.encode(), stdout=subprocess.PIPE,
                          stderr=subprocess.STDOUT, timeout=600, env=env)
     out = res.stdout.decode()
     assert res.returncode == 0 and out.startswith("ok"), out
+    return int(out.split()[3])
 
 
 SMALL = [
@@ -47,7 +54,20 @@ SMALL = [
 @pytest.mark.parametrize("numels,nd", SMALL)
 def test_small_tables(checker, numels, nd):
     for rank in [-1, 0, nd - 1, nd // 2]:
-        run(checker, numels, nd, rank)
+        run(checker, numels, nd, rank, force_spans=True)
+
+
+def test_span_tables_where_the_span_gather_runs(checker):
+    """The 10,000-tensor workload and the layouts of the GPU span-gather tests
+    get span tables (the gather's span form runs on them), every span
+    emulated as the kernel addresses it; layouts where one tile meets more
+    ranks than a span record holds get none and gather by tiles."""
+    w = synth.workloads()["small_tensors_10k_nd8"]
+    assert run(checker, w.numel, w.n_d, -1) > 0
+    import test_gpu_span_gather as sg
+    for name, (numels, nd) in sg.LAYOUTS.items():
+        spans = run(checker, numels, nd, -1)
+        assert (spans > 0) == (name not in sg.TILE_FORM), name
 
 
 @pytest.mark.parametrize("name", list(synth.workloads()))
@@ -78,4 +98,4 @@ def test_random_layout_tables(checker, seed):
         numels = [int(x) for x in np.floor(np.exp(rng.uniform(0, np.log(2e5), count)))]
         numels = [0 if rng.random() < 0.05 else n for n in numels]
         for rank in (-1, int(rng.integers(0, nd))):
-            run(checker, numels, nd, rank)
+            run(checker, numels, nd, rank, force_spans=True)

@@ -128,6 +128,7 @@ void free_tables(zsp_plan* P) {
     P->dev_blob = nullptr;
     P->shard = zsp::ShardTable{};
     P->gather = zsp::GatherTable{};
+    P->span_k.clear();
     P->params = nullptr;
 }
 
@@ -274,6 +275,7 @@ zsp_status zsp_bind_state(zsp_plan* P, int32_t rank_or_all, float* master, float
         if (rank_or_all == ZSP_ALL_RANKS) {
             zsp::build_gather_table(P->numel, P->shard_len, P->shard_off, P->flat_off, P->S,
                                     P->nd, hg);
+            if (zsp::wants_span_table(hg)) zsp::build_span_table(P->S, P->nd, hg);
             hp.resize(size_t(P->T));
             for (int32_t t = 0; t < P->T; ++t)
                 hp[size_t(t)] = zsp::ParamInfo{P->shard_off[size_t(t)], P->shard_len[size_t(t)],
@@ -290,14 +292,17 @@ zsp_status zsp_bind_state(zsp_plan* P, int32_t rank_or_all, float* master, float
     if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
 
     // One allocation: [e0 | info | tile | k0 | delta | gtile | gtile_delta |
-    // gtile_pair | params], 256-byte aligned parts.
-    constexpr int kParts = 9;
+    // gtile_pair | params | span records | span pieces], 256-byte aligned
+    // parts.
+    constexpr int kParts = 11;
     const size_t sz[kParts] = {bytes_of(hs.e0), bytes_of(hs.info),  bytes_of(hs.tile),
                                bytes_of(hg.k0), bytes_of(hg.delta), bytes_of(hg.tile),
-                               bytes_of(hg.tile_delta), bytes_of(hg.tile_pair), bytes_of(hp)};
+                               bytes_of(hg.tile_delta), bytes_of(hg.tile_pair), bytes_of(hp),
+                               bytes_of(hg.wspans), bytes_of(hg.span_segs)};
     const void* src[kParts] = {hs.e0.data(), hs.info.data(),  hs.tile.data(),
                                hg.k0.data(), hg.delta.data(), hg.tile.data(),
-                               hg.tile_delta.data(), hg.tile_pair.data(), hp.data()};
+                               hg.tile_delta.data(), hg.tile_pair.data(), hp.data(),
+                               hg.wspans.data(), hg.span_segs.data()};
     size_t off[kParts], total = 0;
     for (int i = 0; i < kParts; ++i) {
         off[i] = total;
@@ -357,6 +362,13 @@ zsp_status zsp_bind_state(zsp_plan* P, int32_t rank_or_all, float* master, float
         P->gather.ntile = hg.tile.empty() ? 0 : int64_t(hg.tile.size()) - 1;
         P->gather.total = hg.total;
         P->params = reinterpret_cast<const zsp::ParamInfo*>(b + off[8]);
+        if (!hg.wspans.empty()) {
+            P->gather.spans = reinterpret_cast<const zsp::WaveSpan*>(b + off[9]);
+            P->gather.span_segs = reinterpret_cast<const zsp::SpanSeg*>(b + off[10]);
+            P->gather.nspan = int64_t(hg.wspans.size());
+            P->span_k.resize(hg.spans.size());
+            for (size_t i = 0; i < hg.spans.size(); ++i) P->span_k[i] = hg.spans[i].k_a;
+        }
     }
     P->bind_rank = rank_or_all;
     P->device = dev;
@@ -557,6 +569,16 @@ zsp_status zsp::gather_range(zsp_plan* P, int32_t first_param, int32_t n_params,
     if (k_first % zsp::kTile == 0 && P->gather.tile_delta) {
         L.tile_delta = P->gather.tile_delta + k_first / zsp::kTile;
         L.tile_pair = P->gather.tile_pair + 3 * (k_first / zsp::kTile);
+    }
+    if (src == ZSP_SRC_WORK && L.short_pieces && P->gather.spans && k_first % zsp::kTile == 0 &&
+        count >= zsp::kSpanMinElems) {
+        // spans holding the launch's first and last tiles
+        const auto first = std::upper_bound(P->span_k.begin(), P->span_k.end(), k_first) - 1;
+        const auto last =
+            std::upper_bound(P->span_k.begin(), P->span_k.end(), k_first + count - 1) - 1;
+        L.span_first = first - P->span_k.begin();
+        L.nspan = last - first + 1;
+        L.src_elems = int64_t(P->nd) * P->S;
     }
     hipError_t e = zsp::launch_gather(L, src == ZSP_SRC_WORK ? ZSP_BF16 : ZSP_F32, stream);
     if (e != hipSuccess) return fail_hip(e, "gather launch");

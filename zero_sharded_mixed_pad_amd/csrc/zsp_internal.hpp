@@ -64,8 +64,86 @@ struct GatherTable {
     int64_t nq = 0;
     int64_t ntile = 0;
     int64_t total = 0;
+    // Span tables of the bf16 work copy (NULL when the layout does not fit
+    // them; see WaveSpan).
+    const struct WaveSpan* spans = nullptr;
+    const struct SpanSeg* span_segs = nullptr;
+    int64_t nspan = 0;
 };
 constexpr int64_t kNoTileDelta = INT64_MIN;
+
+// ---- Span gather of the bf16 work copy over short pieces -----------------
+// A span is a run of consecutive whole tiles of K-space. For any run of
+// consecutive flat indices, the elements that one rank holds lie in one
+// contiguous range of its shard (a rank keeps its slices of consecutive
+// parameters one after another), pad slots between them included. So one
+// wave gathers a span: it reads each rank's range -- aligned 16-byte
+// chunks, one run per rank -- into LDS, then writes the span's output with
+// aligned 16-byte stores, taking each element from LDS at its piece's
+// offset. The host cuts spans so that their tiles, runs, pieces and chunks
+// fit the limits below; a layout in which one tile alone does not fit gets
+// no span tables and gathers by tiles.
+#ifndef ZSP_SPAN_TILES
+#define ZSP_SPAN_TILES 2
+#endif
+constexpr int kSpanTiles = ZSP_SPAN_TILES;            // tiles per span at most
+constexpr int kSpanChunkElems = 8;                    // bf16 elements per chunk
+constexpr int kSpanChunks = kSpanTiles * 64 + 32;     // 16-byte LDS chunks per span at most
+constexpr int kSpanSegs = 128;                        // pieces meeting a span at most
+constexpr int kSpanRuns = 8;                          // ranks with elements in a span at most
+
+// Generic span tables (host side; also what the table checks read). One
+// span: tiles [k_a / kTile, k_a / kTile + tiles); runs [run_first, run_first
+// + nrun) and pieces [seg_first, seg_first + nseg); chunks = LDS chunks of
+// all runs.
+struct SpanRec {
+    int64_t k_a;
+    int32_t tiles;
+    int32_t nrun;
+    int32_t run_first;
+    int32_t seg_first;
+    int32_t nseg;
+    int32_t chunks;
+};
+
+// One rank's range: source chunks [chunk0, chunk0 + nchunk) of the n_d*S
+// work array (chunk c = elements 8c .. 8c+7) go to LDS chunks
+// [lds0, lds0 + nchunk).
+struct SpanRun {
+    int64_t chunk0;
+    int32_t lds0;
+    int32_t nchunk;
+};
+
+// One piece meeting a span, in K order: it starts at span-local index k (0
+// for a piece begun in an earlier span), and its element at span-local index
+// x sits at LDS element x + off.
+struct SpanSeg {
+    int32_t k;
+    int32_t off;
+};
+
+// The device record of one span (128 bytes, read with scalar loads): the
+// span's header, its runs inline, and per tile t the first and last piece
+// meeting it (span-local, first | last << 8) in bits 16t .. 16t+15 of tseg
+// (tiles 0-3 in tseg[0], 4-7 in tseg[1]). Pieces live in the SpanSeg table
+// from seg_first on.
+struct WaveSpan {
+    int64_t k_a;
+    int32_t seg_first;
+    uint16_t chunks;
+    uint8_t nrun;
+    uint8_t nseg;
+    uint64_t tseg[2];
+    int64_t chunk0[kSpanRuns];
+    uint16_t lds0[kSpanRuns];
+    uint32_t ntile;  // a whole word: the kernel reads every field with scalar loads
+    uint8_t reserved[12];
+};
+static_assert(kSpanTiles <= 8, "a span record holds the pieces of 8 tiles at most");
+static_assert(sizeof(WaveSpan) == 128, "span record is 128 bytes");
+static_assert(sizeof(WaveSpan) % 16 == 0, "span records are read as 16-byte words");
+static_assert(kSpanSegs <= 255 && kSpanChunks <= 65535, "span record field widths");
 
 // Host-side tables before upload.
 struct HostShardTable {
@@ -82,6 +160,12 @@ struct HostGatherTable {
     std::vector<int64_t> tile_delta;
     std::vector<int64_t> tile_pair;
     int64_t total = 0;
+    // span tables (empty when the layout does not fit them)
+    std::vector<SpanRec> spans;
+    std::vector<SpanRun> span_runs;
+    std::vector<SpanSeg> span_segs;
+    std::vector<uint32_t> tile_segs;  // per tile: first | last piece << 16, span-local
+    std::vector<WaveSpan> wspans;     // device records of the spans
 };
 
 // Kernel operations over E-space.
@@ -129,7 +213,15 @@ struct GatherLaunch {
     // else NULL
     const int64_t* tile_delta = nullptr;
     const int64_t* tile_pair = nullptr;  // tab.tile_pair likewise, or NULL
+    // Span form (bf16, short pieces, tile-aligned k_first): spans
+    // [span_first, span_first + nspan) of tab.spans cover the launch.
+    int64_t span_first = -1;
+    int64_t nspan = 0;
+    int64_t src_elems = 0;  // elements of src (n_d*S)
 };
+// Range gathers of at least this many elements take the span form when
+// they can (fewer leave too few spans to fill the chip).
+constexpr int64_t kSpanMinElems = 64 * kTile;
 
 // Below this average piece length (elements) a gather takes its short-piece
 // form: shared boundary lines make up a few percent of the bytes or more.
@@ -230,5 +322,11 @@ void build_gather_table(const std::vector<int64_t>& numel,
                         HostGatherTable& out);
 void build_tile_index(const std::vector<int64_t>& starts, int64_t total,
                       std::vector<int32_t>& tile);
+// Span tables from a gather table (k0, delta, tile filled) of an n_d*S
+// source. Leaves them empty when some tile alone exceeds the span limits.
+void build_span_table(int64_t S, int32_t nd, HostGatherTable& g);
+// Whether a layout gets span tables: only layouts of short pieces, whose
+// gathers take the span form.
+bool wants_span_table(const HostGatherTable& g);
 
 }  // namespace zsp

@@ -49,7 +49,6 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
-#include <cstddef>
 #include <type_traits>
 
 #include "zsp_internal.hpp"
@@ -1058,6 +1057,168 @@ __global__ __launch_bounds__(kWaveLanes) void gather_kernel(const GatherArgs a) 
     gather_tile<T, SHORT>(a, tile, threadIdx.x, s_k0, s_delta);
 }
 
+// ---- Span gather (bf16 work copy, short pieces) ---------------------------
+// One wave per span (see WaveSpan): it reads the span's record with scalar
+// loads, loads every rank's run of the span as aligned 16-byte chunks and
+// the span's pieces in one batch (ordinary loads: the first and last line
+// of a run are shared with the neighbouring spans, which the same XCD runs),
+// lands them in LDS, then writes the span's tiles with aligned 16-byte
+// stores, each lane taking its 8 elements from LDS at the offset of their
+// piece. Spans of two tiles measured fastest: larger spans leave fewer
+// waves in flight, and waves that loop over spans (prefetching the next
+// record and data) were slower still.
+constexpr int kSpanPer = (kSpanChunks + kWaveLanes - 1) / kWaveLanes;  // chunks per lane
+constexpr int kSegPer = (kSpanSegs + kWaveLanes - 1) / kWaveLanes;     // pieces per lane
+
+struct SpanArgs {
+    const WaveSpan* spans;
+    const SpanSeg* segs;
+    const uint16_t* src;
+    uint16_t* out;
+    int64_t span_first;
+    int64_t nspan;
+    int64_t k_first;
+    int64_t count;
+    int64_t src_elems;
+};
+
+// The record, read whole in one batch of 16-byte loads (scalar loads: the
+// address is wave-uniform and nothing is stored before).
+__device__ __forceinline__ WaveSpan load_span(const WaveSpan* p) {
+    struct Words {
+        u32x4 w[sizeof(WaveSpan) / 16];
+    } words;
+    const u32x4* rp = reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+    for (int i = 0; i < int(sizeof(WaveSpan) / 16); ++i) words.w[i] = rp[i];
+    return __builtin_bit_cast(WaveSpan, words);
+}
+
+// Source chunk of span chunk c: c + (chunk0 - lds0) of its run (the last
+// run whose LDS start is at or below c).
+__device__ __forceinline__ int64_t span_chunk(const WaveSpan& R, int c) {
+    int64_t gd = R.chunk0[0] - R.lds0[0];
+#pragma unroll
+    for (int q = 1; q < kSpanRuns; ++q) {
+        if (q >= R.nrun) break;
+        gd = c >= R.lds0[q] ? R.chunk0[q] - R.lds0[q] : gd;
+    }
+    return c + gd;
+}
+
+__global__ __launch_bounds__(kWaveLanes) void gather_span_kernel(const SpanArgs a) {
+    __shared__ u32x4 s_data[kSpanChunks];
+    __shared__ SpanSeg s_seg[kSpanSegs];
+    const int64_t sp = xcd_run_tile(blockIdx.x);
+    if (sp >= a.nspan) return;  // the grid is rounded up to whole rounds of runs
+    const WaveSpan R = load_span(a.spans + (a.span_first + sp));
+    const int lane = threadIdx.x;
+    const int chunks = R.chunks, nseg = R.nseg;
+
+    // Every chunk of every run, then the pieces: one batch of loads, issued
+    // unconditionally (lanes past the end reload the last chunk or piece).
+    const u32x4* src16 = reinterpret_cast<const u32x4*>(a.src);
+    const int64_t whole = a.src_elems / kSpanChunkElems;  // chunks inside src (>= 1)
+    u32x4 v[kSpanPer];
+    bool tail = false;  // some chunk of this lane holds the end of src
+#pragma unroll
+    for (int j = 0; j < kSpanPer; ++j) {
+        const int64_t gc = span_chunk(R, min(lane + j * kWaveLanes, chunks - 1));
+        tail |= gc >= whole;
+        v[j] = src16[min(gc, whole - 1)];
+    }
+    SpanSeg sg[kSegPer];
+#pragma unroll
+    for (int j = 0; j < kSegPer; ++j)
+        sg[j] = a.segs[R.seg_first + min(lane + j * kWaveLanes, nseg - 1)];
+    if (tail) {
+        // a chunk holding the end of src: only its elements inside src
+#pragma unroll
+        for (int j = 0; j < kSpanPer; ++j) {
+            const int64_t gc = span_chunk(R, min(lane + j * kWaveLanes, chunks - 1));
+            if (gc >= whole) {
+                uint16_t e[kSpanChunkElems];
+#pragma unroll
+                for (int k = 0; k < kSpanChunkElems; ++k) {
+                    const int64_t x = gc * kSpanChunkElems + k;
+                    e[k] = x < a.src_elems ? a.src[x] : uint16_t(0);
+                }
+                v[j] = __builtin_bit_cast(u32x4, e);
+            }
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < kSegPer; ++j)
+        if (lane + j * kWaveLanes < nseg) s_seg[lane + j * kWaveLanes] = sg[j];
+#pragma unroll
+    for (int j = 0; j < kSpanPer; ++j) {
+        const int c = lane + j * kWaveLanes;
+        if (c < chunks) s_data[c] = v[j];
+    }
+    __syncthreads();
+
+    const uint32_t* s32 = reinterpret_cast<const uint32_t*>(s_data);
+    const uint16_t* s16 = reinterpret_cast<const uint16_t*>(s_data);
+    const int64_t k_end = a.k_first + a.count;
+    // span-local index of the launch's last element
+    const int64_t kl_last = k_end - 1 - R.k_a;
+    const int ntile = int(R.ntile);
+    for (int tau = 0; tau < ntile; ++tau) {
+        const int64_t K0 = R.k_a + int64_t(tau) * kTile;
+        if (K0 + kTile <= a.k_first) continue;
+        if (K0 >= k_end) break;
+        // the tile's first and last piece (shifts: no indexing of registers)
+        const uint64_t tw = tau < 4 ? R.tseg[0] : R.tseg[1];
+        const int ts = int((tw >> (16 * (tau & 3))) & 0xffffu);
+        const int lo = ts & 0xff, hi = ts >> 8;
+        const int kl = tau * int(kTile) + lane * kSpanChunkElems;
+        const int64_t jo = R.k_a + kl - a.k_first;  // output index of the lane's first element
+        const bool full = jo >= 0 && jo + kSpanChunkElems <= a.count;
+        if (lo == hi && full) {
+            // One piece: the lane's 8 elements are LDS elements p .. p + 7,
+            // read as the dwords holding them (measured faster than whole
+            // 16-byte chunks and a shift).
+            const int p = kl + s_seg[lo].off;
+            const int dw = p >> 1;
+            u32x4 o;
+            if ((p & 1) == 0) {
+                o = u32x4{s32[dw], s32[dw + 1], s32[dw + 2], s32[dw + 3]};
+            } else {
+                const uint32_t d0 = s32[dw], d1 = s32[dw + 1], d2 = s32[dw + 2],
+                               d3 = s32[dw + 3], d4 = s32[dw + 4];
+                o = u32x4{__builtin_amdgcn_alignbyte(d1, d0, 2), __builtin_amdgcn_alignbyte(d2, d1, 2),
+                          __builtin_amdgcn_alignbyte(d3, d2, 2), __builtin_amdgcn_alignbyte(d4, d3, 2)};
+            }
+            stnt(reinterpret_cast<u32x4*>(a.out + jo), o);
+        } else {
+            // Several pieces, or the launch's end: each element finds its
+            // piece (binary search, then forward); elements past the
+            // launch's end read its last element and are not stored.
+            const int kls = int(min(int64_t(kl), kl_last));
+            int q = lo;
+            for (int h = hi; q < h;) {
+                const int mid = (q + h + 1) >> 1;
+                if (s_seg[mid].k <= kls) q = mid;
+                else h = mid - 1;
+            }
+            uint16_t e[kSpanChunkElems];
+#pragma unroll
+            for (int k = 0; k < kSpanChunkElems; ++k) {
+                const int K = int(min(int64_t(kl + k), kl_last));
+                while (q < hi && s_seg[q + 1].k <= K) ++q;
+                e[k] = s16[K + s_seg[q].off];
+            }
+            if (full) {
+                stnt(reinterpret_cast<u32x4*>(a.out + jo), __builtin_bit_cast(u32x4, e));
+            } else {
+#pragma unroll
+                for (int k = 0; k < kSpanChunkElems; ++k)
+                    if (jo + k >= 0 && jo + k < a.count) a.out[jo + k] = e[k];
+            }
+        }
+    }
+}
+
 // ---- Gather of a list of parameters into separate outputs ------------------
 // Each wave copies one tile of kTile elements of one output. Its record
 // (TileRec) says where the tile's elements come from: a tile of a
@@ -1426,6 +1587,24 @@ hipError_t launch_gather(const GatherLaunch& L, zsp_dtype dtype, hipStream_t str
     a.count = L.count;
     a.src = L.src;
     a.out = L.out;
+    if (L.nspan > 0 && dtype == ZSP_BF16) {
+        SpanArgs sa{};
+        sa.spans = L.tab.spans;
+        sa.segs = L.tab.span_segs;
+        sa.src = static_cast<const uint16_t*>(L.src);
+        sa.out = static_cast<uint16_t*>(L.out);
+        sa.span_first = L.span_first;
+        sa.nspan = L.nspan;
+        sa.k_first = L.k_first;
+        sa.count = L.count;
+        sa.src_elems = L.src_elems;
+        const int64_t round = 8 * kXcdRun;  // one wave per span, XCD runs of spans
+        const int64_t blocks = (L.nspan + round - 1) / round * round;
+        if (blocks > kMaxBlocks) return hipErrorInvalidValue;
+        hipLaunchKernelGGL(gather_span_kernel, dim3(static_cast<uint32_t>(blocks)),
+                           dim3(kWaveLanes), 0, stream, sa);
+        return hipGetLastError();
+    }
     const int64_t tiles = (L.count + kTile - 1) / kTile;  // one wave per 512 outputs
     const int64_t runs = 8 * kXcdRun;
     const int64_t blocks = L.short_pieces ? (tiles + runs - 1) / runs * runs : tiles;

@@ -8,6 +8,7 @@
 // padded to a multiple of N_d on its own, and rank r owns the contiguous
 // slice [r*s, (r+1)*s) of it.
 #include <algorithm>
+#include <utility>
 
 #include "zsp_internal.hpp"
 
@@ -114,6 +115,185 @@ void build_gather_table(const std::vector<int64_t>& numel,
             r[0] = q > p ? out.k0[size_t(q)] : INT64_MAX;
             r[1] = out.delta[size_t(p)];
             r[2] = out.delta[size_t(q)];
+        }
+    }
+}
+
+bool wants_span_table(const HostGatherTable& g) {
+    return int64_t(g.delta.size()) * kShortPiece > g.total;
+}
+
+// Span tables. Tiles are added to the current span in order while the
+// span's runs, pieces and LDS chunks stay within the limits; a tile that
+// does not fit starts the next span. A rank's run is the range of its shard
+// from the first to the last element the span reads from it; its LDS image
+// starts at the 16-byte chunk holding the first element.
+void build_span_table(int64_t S, int32_t nd, HostGatherTable& g) {
+    g.spans.clear();
+    g.span_runs.clear();
+    g.span_segs.clear();
+    g.tile_segs.clear();
+    g.wspans.clear();
+    const int64_t total = g.total;
+    const int64_t nq = static_cast<int64_t>(g.delta.size());
+    if (total <= 0 || S <= 0 || nd < 1 || nq == 0) return;
+    const int64_t ntile = (total + kTile - 1) / kTile;
+    constexpr int64_t C = kSpanChunkElems;
+    auto extent = [](int64_t l, int64_t h) { return (h + C - 1) / C - l / C; };
+    auto rank_of = [&](int64_t q) { return (g.k0[size_t(q)] + g.delta[size_t(q)]) / S; };
+
+    const size_t n_ranks = static_cast<size_t>(nd);
+    std::vector<int64_t> lo(n_ranks), hi(n_ranks), stamp(n_ranks, -1);
+    std::vector<int32_t> lds0(n_ranks), ranks;
+    std::vector<std::pair<int64_t, int64_t>> segs;  // (piece, first global K in span)
+    int64_t sid = 0, k_a = 0, chunks = 0, last_q = -1;
+    int32_t tiles = 0;
+    struct TileRun {
+        int64_t r, lo, hi;
+    };
+    std::vector<TileRun> trun;
+    std::vector<uint32_t> tile_segs(static_cast<size_t>(ntile));
+
+    auto finish = [&]() -> bool {
+        std::sort(ranks.begin(), ranks.end());
+        SpanRec rec{k_a, tiles, int32_t(ranks.size()), int32_t(g.span_runs.size()),
+                    int32_t(g.span_segs.size()), int32_t(segs.size()), int32_t(chunks)};
+        if (g.span_runs.size() + ranks.size() > size_t(INT32_MAX) ||
+            g.span_segs.size() + segs.size() > size_t(INT32_MAX))
+            return false;
+        int32_t at = 0;
+        for (int32_t r : ranks) {
+            const int64_t c0 = lo[size_t(r)] / C;
+            const int32_t n = int32_t(extent(lo[size_t(r)], hi[size_t(r)]));
+            g.span_runs.push_back(SpanRun{c0, at, n});
+            lds0[size_t(r)] = at;
+            at += n;
+        }
+        for (const auto& sq : segs) {
+            const int64_t q = sq.first, K = sq.second;
+            const int64_t r = rank_of(q);
+            const int64_t pos = C * lds0[size_t(r)] + (K + g.delta[size_t(q)] - C * (lo[size_t(r)] / C));
+            const int64_t k = K - k_a;
+            g.span_segs.push_back(SpanSeg{int32_t(k), int32_t(pos - k)});
+        }
+        g.spans.push_back(rec);
+        ranks.clear();
+        segs.clear();
+        chunks = 0;
+        tiles = 0;
+        last_q = -1;
+        ++sid;
+        return true;
+    };
+    auto fail = [&]() {
+        g.spans.clear();
+        g.span_runs.clear();
+        g.span_segs.clear();
+        g.tile_segs.clear();
+        g.wspans.clear();
+    };
+
+    for (int64_t t = 0; t < ntile; ++t) {
+        const int64_t t0 = t * kTile, t1 = std::min(t0 + kTile, total);
+        const int64_t q0 = g.tile[size_t(t)];
+        int64_t q1 = q0;  // last piece meeting the tile
+        while (q1 + 1 < nq && g.k0[size_t(q1) + 1] < t1) ++q1;
+        // the tile's range of each rank (pieces of one rank merged)
+        trun.clear();
+        for (int64_t q = q0; q <= q1; ++q) {
+            const int64_t a = std::max(g.k0[size_t(q)], t0) + g.delta[size_t(q)];
+            const int64_t b = std::min(g.k0[size_t(q) + 1], t1) + g.delta[size_t(q)];
+            const int64_t r = rank_of(q);
+            bool merged = false;
+            for (auto& x : trun) {
+                if (x.r == r) {
+                    x.lo = std::min(x.lo, a);
+                    x.hi = std::max(x.hi, b);
+                    merged = true;
+                    break;
+                }
+            }
+            if (!merged) trun.push_back(TileRun{r, a, b});
+        }
+        for (int pass = 0; pass < 2; ++pass) {
+            int64_t add_chunks = 0, add_runs = 0;
+            for (const auto& x : trun) {
+                if (stamp[size_t(x.r)] == sid) {
+                    const int64_t l = lo[size_t(x.r)], h = hi[size_t(x.r)];
+                    add_chunks += extent(std::min(l, x.lo), std::max(h, x.hi)) - extent(l, h);
+                } else {
+                    add_chunks += extent(x.lo, x.hi);
+                    ++add_runs;
+                }
+            }
+            const int64_t add_segs = (q1 - q0 + 1) - (q0 == last_q ? 1 : 0);
+            const bool fits = tiles + 1 <= kSpanTiles && chunks + add_chunks <= kSpanChunks &&
+                              int64_t(segs.size()) + add_segs <= kSpanSegs &&
+                              int64_t(ranks.size()) + add_runs <= kSpanRuns;
+            if (fits) {
+                for (const auto& x : trun) {
+                    if (stamp[size_t(x.r)] == sid) {
+                        lo[size_t(x.r)] = std::min(lo[size_t(x.r)], x.lo);
+                        hi[size_t(x.r)] = std::max(hi[size_t(x.r)], x.hi);
+                    } else {
+                        stamp[size_t(x.r)] = sid;
+                        lo[size_t(x.r)] = x.lo;
+                        hi[size_t(x.r)] = x.hi;
+                        ranks.push_back(int32_t(x.r));
+                    }
+                }
+                chunks += add_chunks;
+                if (tiles == 0) k_a = t0;
+                const uint32_t first = uint32_t(q0 == last_q ? segs.size() - 1 : segs.size());
+                for (int64_t q = q0; q <= q1; ++q) {
+                    if (q == last_q) continue;
+                    segs.emplace_back(q, std::max(g.k0[size_t(q)], t0));
+                }
+                last_q = q1;
+                tile_segs[size_t(t)] = first | (uint32_t(segs.size() - 1) << 16);
+                ++tiles;
+                break;
+            }
+            if (tiles == 0 || pass == 1) {  // the tile alone does not fit
+                fail();
+                return;
+            }
+            if (!finish()) {
+                fail();
+                return;
+            }
+        }
+    }
+    if (tiles > 0 && !finish()) {
+        fail();
+        return;
+    }
+    g.tile_segs = std::move(tile_segs);
+    // device records: header, runs inline, per-tile pieces
+    g.wspans.assign(g.spans.size(), WaveSpan{});
+    for (size_t i = 0; i < g.spans.size(); ++i) {
+        const SpanRec& R = g.spans[i];
+        WaveSpan& w = g.wspans[i];
+        w.k_a = R.k_a;
+        w.seg_first = R.seg_first;
+        w.chunks = uint16_t(R.chunks);
+        w.nrun = uint8_t(R.nrun);
+        w.nseg = uint8_t(R.nseg);
+        w.ntile = uint32_t(R.tiles);
+        for (int32_t t = 0; t < R.tiles; ++t) {
+            const uint32_t ts = g.tile_segs[size_t(R.k_a / kTile + t)];
+            const uint64_t pair = (ts & 0xffffu) | ((ts >> 16) << 8);
+            w.tseg[t / 4] |= pair << (16 * (t % 4));
+        }
+        for (int32_t q = 0; q < kSpanRuns; ++q) {
+            if (q < R.nrun) {
+                const SpanRun& U = g.span_runs[size_t(R.run_first + q)];
+                w.chunk0[q] = U.chunk0;
+                w.lds0[q] = uint16_t(U.lds0);
+            } else {
+                w.chunk0[q] = 0;
+                w.lds0[q] = 0xffffu;  // never reached by a chunk index
+            }
         }
     }
 }

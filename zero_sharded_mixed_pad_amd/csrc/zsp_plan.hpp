@@ -39,6 +39,7 @@ struct zsp_plan {
     void* dev_blob = nullptr;  // one device allocation holding every table
     zsp::ShardTable shard;
     zsp::GatherTable gather;
+    std::vector<int64_t> span_k;  // first flat index of each span (host copy)
     const zsp::ParamInfo* params = nullptr;  // per parameter (all-rank bindings)
     zsp::ListStaging* lists = nullptr;       // made at an all-rank bind
 
