@@ -741,6 +741,8 @@ def _short(name):
         return f"{_OPS[int(m.group(1))]}[{dt}]"
     if "gather_kernel" in name:
         return "gather[f32]" if ("IfE" in name or "<float>" in name) else "gather[bf16]"
+    if "gather_span_kernel" in name:  # the range gather's form over short pieces (bf16)
+        return "gather[bf16]"
     m = re.search(r"gather_list_(args|recs)", name)
     if m:
         dt = "f32" if ("IfLb" in name or "<float," in name) else "bf16"
