@@ -124,19 +124,20 @@ static int check_spans(const HostGatherTable& g, int64_t S, int64_t nd) {
     for (size_t i = 0; i < g.spans.size(); ++i) {
         const SpanRec& R = g.spans[i];
         const WaveSpan& w = g.wspans[i];
-        if (w.k_a != R.k_a || w.seg_first != R.seg_first || w.chunks != R.chunks ||
-            w.nrun != R.nrun || w.nseg != R.nseg || w.ntile != R.tiles)
-            return bad("span record header", int64_t(i), w.k_a);
+        if (int64_t(w.tile0) * kTile != R.k_a || w.seg_first != R.seg_first ||
+            w.chunks != R.chunks || w.nrun != R.nrun || w.nseg != R.nseg || w.ntile != R.tiles)
+            return bad("span record header", int64_t(i), R.k_a);
         for (int32_t t = 0; t < R.tiles; ++t) {
             const uint32_t ts = g.tile_segs[size_t(R.k_a / kTile + t)];
-            const uint64_t pair = (w.tseg[t / 4] >> (16 * (t % 4))) & 0xffffu;
+            const uint32_t pair = w.tseg[t];
             if ((pair & 0xff) != (ts & 0xffffu) || (pair >> 8) != (ts >> 16))
                 return bad("span record pieces", int64_t(i), t);
         }
+        if (w.lds0[0] != 0) return bad("first run's LDS start", int64_t(i), w.lds0[0]);
         for (int32_t c = 0; c < R.chunks; ++c) {
-            int64_t gd = w.chunk0[0] - w.lds0[0];
+            int64_t gd = w.chunk0;
             for (int q = 1; q < kSpanRuns && q < w.nrun; ++q)
-                if (c >= w.lds0[q]) gd = w.chunk0[q] - w.lds0[q];
+                if (c >= w.lds0[q]) gd = w.chunk0 + w.dchunk[q - 1] - w.lds0[q];
             // the generic run holding chunk c
             int64_t want = -1;
             for (int32_t q = 0; q < R.nrun; ++q) {

@@ -83,14 +83,11 @@ constexpr int64_t kNoTileDelta = INT64_MIN;
 // offset. The host cuts spans so that their tiles, runs, pieces and chunks
 // fit the limits below; a layout in which one tile alone does not fit gets
 // no span tables and gathers by tiles.
-#ifndef ZSP_SPAN_TILES
-#define ZSP_SPAN_TILES 2
-#endif
-constexpr int kSpanTiles = ZSP_SPAN_TILES;            // tiles per span at most
-constexpr int kSpanChunkElems = 8;                    // bf16 elements per chunk
-constexpr int kSpanChunks = kSpanTiles * 64 + 32;     // 16-byte LDS chunks per span at most
-constexpr int kSpanSegs = 128;                        // pieces meeting a span at most
-constexpr int kSpanRuns = 8;                          // ranks with elements in a span at most
+constexpr int kSpanTiles = 2;                        // tiles per span at most
+constexpr int kSpanChunkElems = 8;                   // bf16 elements per chunk
+constexpr int kSpanChunks = kSpanTiles * 64 + 32;    // 16-byte LDS chunks per span at most
+constexpr int kSpanSegs = 128;                       // pieces meeting a span at most
+constexpr int kSpanRuns = 8;                         // ranks with elements in a span at most
 
 // Generic span tables (host side; also what the table checks read). One
 // span: tiles [k_a / kTile, k_a / kTile + tiles); runs [run_first, run_first
@@ -123,27 +120,27 @@ struct SpanSeg {
     int32_t off;
 };
 
-// The device record of one span (128 bytes, read with scalar loads): the
-// span's header, its runs inline, and per tile t the first and last piece
-// meeting it (span-local, first | last << 8) in bits 16t .. 16t+15 of tseg
-// (tiles 0-3 in tseg[0], 4-7 in tseg[1]). Pieces live in the SpanSeg table
-// from seg_first on.
+// The device record of one span (64 bytes, one scalar load): its first
+// tile, its pieces' place in the SpanSeg table, run 0's first source chunk
+// and every other run's as an offset from it, each run's first LDS chunk,
+// per tile the first and last piece meeting it (span-local, first | last
+// << 8), and the span's chunk, run, piece and tile counts.
 struct WaveSpan {
-    int64_t k_a;
+    int64_t chunk0;
+    int32_t tile0;
     int32_t seg_first;
-    uint16_t chunks;
+    int32_t dchunk[kSpanRuns - 1];  // chunk0 of run q + 1 minus chunk0
+    uint8_t lds0[kSpanRuns];        // lds0[0] = 0
+    uint16_t tseg[kSpanTiles];
+    uint8_t chunks;
     uint8_t nrun;
     uint8_t nseg;
-    uint64_t tseg[2];
-    int64_t chunk0[kSpanRuns];
-    uint16_t lds0[kSpanRuns];
-    uint32_t ntile;  // a whole word: the kernel reads every field with scalar loads
-    uint8_t reserved[12];
+    uint8_t ntile;
+    uint32_t reserved;
 };
-static_assert(kSpanTiles <= 8, "a span record holds the pieces of 8 tiles at most");
-static_assert(sizeof(WaveSpan) == 128, "span record is 128 bytes");
-static_assert(sizeof(WaveSpan) % 16 == 0, "span records are read as 16-byte words");
-static_assert(kSpanSegs <= 255 && kSpanChunks <= 65535, "span record field widths");
+static_assert(sizeof(WaveSpan) == 64, "span record is 64 bytes");
+static_assert(kSpanSegs <= 255 && kSpanChunks <= 255, "span record field widths");
+
 
 // Host-side tables before upload.
 struct HostShardTable {

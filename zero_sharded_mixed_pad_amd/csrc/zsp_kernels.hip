@@ -1094,14 +1094,14 @@ __device__ __forceinline__ WaveSpan load_span(const WaveSpan* p) {
     return __builtin_bit_cast(WaveSpan, words);
 }
 
-// Source chunk of span chunk c: c + (chunk0 - lds0) of its run (the last
-// run whose LDS start is at or below c).
+// Source chunk of span chunk c: c + (first source chunk - first LDS chunk)
+// of its run (the last run whose LDS start is at or below c).
 __device__ __forceinline__ int64_t span_chunk(const WaveSpan& R, int c) {
-    int64_t gd = R.chunk0[0] - R.lds0[0];
+    int64_t gd = R.chunk0;  // run 0 starts at LDS chunk 0
 #pragma unroll
     for (int q = 1; q < kSpanRuns; ++q) {
         if (q >= R.nrun) break;
-        gd = c >= R.lds0[q] ? R.chunk0[q] - R.lds0[q] : gd;
+        gd = c >= R.lds0[q] ? R.chunk0 + R.dchunk[q - 1] - R.lds0[q] : gd;
     }
     return c + gd;
 }
@@ -1114,6 +1114,7 @@ __global__ __launch_bounds__(kWaveLanes) void gather_span_kernel(const SpanArgs 
     const WaveSpan R = load_span(a.spans + (a.span_first + sp));
     const int lane = threadIdx.x;
     const int chunks = R.chunks, nseg = R.nseg;
+    const int64_t k_a = int64_t(R.tile0) * kTile;  // the span's first flat index
 
     // Every chunk of every run, then the pieces: one batch of loads, issued
     // unconditionally (lanes past the end reload the last chunk or piece).
@@ -1161,18 +1162,18 @@ __global__ __launch_bounds__(kWaveLanes) void gather_span_kernel(const SpanArgs 
     const uint16_t* s16 = reinterpret_cast<const uint16_t*>(s_data);
     const int64_t k_end = a.k_first + a.count;
     // span-local index of the launch's last element
-    const int64_t kl_last = k_end - 1 - R.k_a;
-    const int ntile = int(R.ntile);
+    const int64_t kl_last = k_end - 1 - k_a;
+    const int ntile = R.ntile;
+    static_assert(kSpanTiles == 2, "the tile loop picks tseg[0] or tseg[1]");
     for (int tau = 0; tau < ntile; ++tau) {
-        const int64_t K0 = R.k_a + int64_t(tau) * kTile;
+        const int64_t K0 = k_a + int64_t(tau) * kTile;
         if (K0 + kTile <= a.k_first) continue;
         if (K0 >= k_end) break;
-        // the tile's first and last piece (shifts: no indexing of registers)
-        const uint64_t tw = tau < 4 ? R.tseg[0] : R.tseg[1];
-        const int ts = int((tw >> (16 * (tau & 3))) & 0xffffu);
+        // the tile's first and last piece (a select: no indexing of registers)
+        const int ts = tau == 0 ? R.tseg[0] : R.tseg[1];
         const int lo = ts & 0xff, hi = ts >> 8;
         const int kl = tau * int(kTile) + lane * kSpanChunkElems;
-        const int64_t jo = R.k_a + kl - a.k_first;  // output index of the lane's first element
+        const int64_t jo = k_a + kl - a.k_first;  // output index of the lane's first element
         const bool full = jo >= 0 && jo + kSpanChunkElems <= a.count;
         if (lo == hi && full) {
             // One piece: the lane's 8 elements are LDS elements p .. p + 7,

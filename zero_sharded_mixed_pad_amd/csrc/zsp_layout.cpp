@@ -269,30 +269,41 @@ void build_span_table(int64_t S, int32_t nd, HostGatherTable& g) {
         return;
     }
     g.tile_segs = std::move(tile_segs);
-    // device records: header, runs inline, per-tile pieces
+    // device records: runs and per-tile pieces inline; a layout whose runs
+    // lie more than 2^31 chunks apart, or with more than 2^31 tiles, gets none
     g.wspans.assign(g.spans.size(), WaveSpan{});
     for (size_t i = 0; i < g.spans.size(); ++i) {
         const SpanRec& R = g.spans[i];
         WaveSpan& w = g.wspans[i];
-        w.k_a = R.k_a;
+        if (R.k_a / kTile > INT32_MAX) {
+            fail();
+            return;
+        }
+        w.tile0 = int32_t(R.k_a / kTile);
         w.seg_first = R.seg_first;
-        w.chunks = uint16_t(R.chunks);
+        w.chunks = uint8_t(R.chunks);
         w.nrun = uint8_t(R.nrun);
         w.nseg = uint8_t(R.nseg);
-        w.ntile = uint32_t(R.tiles);
+        w.ntile = uint8_t(R.tiles);
         for (int32_t t = 0; t < R.tiles; ++t) {
             const uint32_t ts = g.tile_segs[size_t(R.k_a / kTile + t)];
-            const uint64_t pair = (ts & 0xffffu) | ((ts >> 16) << 8);
-            w.tseg[t / 4] |= pair << (16 * (t % 4));
+            w.tseg[t] = uint16_t((ts & 0xffffu) | ((ts >> 16) << 8));
         }
+        const SpanRun* U = &g.span_runs[size_t(R.run_first)];
+        w.chunk0 = U[0].chunk0;
         for (int32_t q = 0; q < kSpanRuns; ++q) {
             if (q < R.nrun) {
-                const SpanRun& U = g.span_runs[size_t(R.run_first + q)];
-                w.chunk0[q] = U.chunk0;
-                w.lds0[q] = uint16_t(U.lds0);
+                w.lds0[q] = uint8_t(U[q].lds0);
+                if (q > 0) {
+                    const int64_t d = U[q].chunk0 - U[0].chunk0;
+                    if (d > INT32_MAX || d < INT32_MIN) {
+                        fail();
+                        return;
+                    }
+                    w.dchunk[q - 1] = int32_t(d);
+                }
             } else {
-                w.chunk0[q] = 0;
-                w.lds0[q] = 0xffffu;  // never reached by a chunk index
+                w.lds0[q] = 0xffu;  // never reached by a chunk index
             }
         }
     }
