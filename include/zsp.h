@@ -281,10 +281,14 @@ zsp_status zsp_gather_range(zsp_plan* plan, int32_t first_param, int32_t n_param
 zsp_status zsp_gather_many(zsp_plan* plan, const int32_t* ids, int32_t n, zsp_source src,
                            void* const* outs, void* stream);
 
-/* zsp_gather_many for callers that cannot allocate (code under HIP graph
- * capture, tight serving loops, harnesses that forbid allocation): the same
- * arguments, checks and results, but nothing is allocated, on the device
- * or the host. A long list (more than 64 non-empty parameters) is staged
+/* zsp_gather_many for callers that cannot allocate (tight serving loops,
+ * harnesses that forbid allocation, and code under HIP graph capture for
+ * lists of at most 64 non-empty parameters, which are one kernel launch):
+ * the same arguments, checks and results, but nothing is allocated, on the
+ * device or the host. A longer list's staging copy reads a host buffer that
+ * the next call refills, so a captured copy would replay stale entries:
+ * capture such lists as a prepared list (zsp_gather_list_run) instead.
+ * A long list (more than 64 non-empty parameters) is staged
  * in a fixed device array the library holds on every GPU it runs on from
  * load to process end (9.25 MiB): its entries and coarse index are copied
  * there from a static host buffer, then the same two kernels run. Limits:

@@ -6,11 +6,14 @@ and host synchronisations between the replays; after every replay the state
 and the gathered parameters equal those of the same calls made eagerly on a
 twin plan. The Adam step's scalars are kernel arguments, so a replay repeats
 the step number it was captured with (the eager twin does the same). A
-prepared list's run (zsp_gather_list_run) is captured the same way."""
+prepared list's run (zsp_gather_list_run) is captured the same way. The
+layouts take the gather's tile form (long pieces, and a small launch) and
+its span form (300 parameters of 64-2000 elements)."""
 import pytest
 import torch
 
 import zero_sharded_mixed_pad_amd as zsp
+from zero_sharded_mixed_pad_amd import synth
 
 from test_gpu_parity import HP, Mirror, assert_bits, dev, np_of
 
@@ -18,7 +21,10 @@ pytestmark = pytest.mark.gpu
 
 
 @pytest.mark.parametrize("numels,nd", [([1003, 64, 5, 0, 3 * 4096 + 1], 4),
-                                       ([4096 * 3, 11008 * 2, 4096, 4096], 8)])
+                                       ([4096 * 3, 11008 * 2, 4096, 4096], 8),
+                                       # short pieces: the range gather's span form
+                                       (synth.small_tensor_sizes(count=300, lo=64, hi=2000,
+                                                                 seed=21), 8)])
 def test_capture_and_replay_matches_eager(numels, nd):
     A, B = Mirror(numels, nd), Mirror(numels, nd)
     grads = [g.to(dev()) for g in A.grads(torch.bfloat16, "graph", poison=False)]

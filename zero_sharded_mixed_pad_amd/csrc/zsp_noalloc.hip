@@ -13,7 +13,9 @@
 // One array per GPU serves every call on it: calls on one stream follow each
 // other in order; calls on one GPU that overlap (other streams, other
 // threads) race on it. Nothing in it needs clearing: a call writes every
-// byte it reads before reading it.
+// byte it reads before reading it. The staging copies read static host
+// buffers that the next call refills, so a long list's call is not for
+// stream capture (a replay would copy whatever those buffers hold then).
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
