@@ -319,8 +319,35 @@ void build_gather_table(const std::vector<int64_t>& numel,
                         HostGatherTable& out);
 void build_tile_index(const std::vector<int64_t>& starts, int64_t total,
                       std::vector<int32_t>& tile);
-// Span tables from a gather table (k0, delta, tile filled) of an n_d*S
-// source. Leaves them empty when some tile alone exceeds the span limits.
+// A tile handed to build_spans: flat indices [K0, K0 + n).
+struct SpanTileIn {
+    int64_t K0;
+    int64_t n;
+};
+// What build_spans makes: spans (k_a = the flat index of their first tile's
+// first element, span-local indices counted from it), their runs and pieces,
+// and per input tile the first and last piece meeting it (span-local, first
+// | last << 16). Span i holds the tiles after those of spans 0 .. i-1.
+struct SpanBuild {
+    std::vector<SpanRec> spans;
+    std::vector<SpanRun> runs;
+    std::vector<SpanSeg> segs;
+    std::vector<uint32_t> tile_segs;
+};
+// Spans over tiles in[0 .. n_in) of an n_d*S source (gather table k0,
+// delta filled), at most max_tiles tiles each; a tile joins the span before
+// it only when it starts where the previous tile ended. False when some tile
+// alone exceeds the span limits (or a tile lies outside the flat indices).
+bool build_spans(const HostGatherTable& g, int64_t S, int32_t nd, const SpanTileIn* in,
+                 int64_t n_in, int32_t max_tiles, SpanBuild& out);
+// Runs of a span in record form: run 0's first source chunk, the others' as
+// offsets from it, and each run's first LDS chunk (0xff for none). False
+// when an offset does not fit 32 bits.
+bool pack_runs(const SpanRun* U, int32_t nrun, int64_t& chunk0,
+               int32_t (&dchunk)[kSpanRuns - 1], uint8_t (&lds0)[kSpanRuns]);
+// Span tables of the range gather from a gather table (k0, delta, tile
+// filled) of an n_d*S source. Leaves them empty when some tile alone
+// exceeds the span limits.
 void build_span_table(int64_t S, int32_t nd, HostGatherTable& g);
 // Whether a layout gets span tables: only layouts of short pieces, whose
 // gathers take the span form.

@@ -1096,7 +1096,8 @@ __device__ __forceinline__ WaveSpan load_span(const WaveSpan* p) {
 
 // Source chunk of span chunk c: c + (first source chunk - first LDS chunk)
 // of its run (the last run whose LDS start is at or below c).
-__device__ __forceinline__ int64_t span_chunk(const WaveSpan& R, int c) {
+template <typename Rec>
+__device__ __forceinline__ int64_t span_chunk(const Rec& R, int c) {
     int64_t gd = R.chunk0;  // run 0 starts at LDS chunk 0
 #pragma unroll
     for (int q = 1; q < kSpanRuns; ++q) {
@@ -1106,20 +1107,16 @@ __device__ __forceinline__ int64_t span_chunk(const WaveSpan& R, int c) {
     return c + gd;
 }
 
-__global__ __launch_bounds__(kWaveLanes) void gather_span_kernel(const SpanArgs a) {
-    __shared__ u32x4 s_data[kSpanChunks];
-    __shared__ SpanSeg s_seg[kSpanSegs];
-    const int64_t sp = xcd_run_tile(blockIdx.x);
-    if (sp >= a.nspan) return;  // the grid is rounded up to whole rounds of runs
-    const WaveSpan R = load_span(a.spans + (a.span_first + sp));
-    const int lane = threadIdx.x;
+// A span's LDS image: every chunk of every run, then the pieces, in one
+// batch of loads issued unconditionally (lanes past the end reload the last
+// chunk or piece), then landed in LDS. src holds src_elems elements.
+template <typename Rec>
+__device__ __forceinline__ void span_land(const Rec& R, int lane, const uint16_t* src,
+                                          int64_t src_elems, const SpanSeg* segs,
+                                          u32x4* s_data, SpanSeg* s_seg) {
     const int chunks = R.chunks, nseg = R.nseg;
-    const int64_t k_a = int64_t(R.tile0) * kTile;  // the span's first flat index
-
-    // Every chunk of every run, then the pieces: one batch of loads, issued
-    // unconditionally (lanes past the end reload the last chunk or piece).
-    const u32x4* src16 = reinterpret_cast<const u32x4*>(a.src);
-    const int64_t whole = a.src_elems / kSpanChunkElems;  // chunks inside src (>= 1)
+    const u32x4* src16 = reinterpret_cast<const u32x4*>(src);
+    const int64_t whole = src_elems / kSpanChunkElems;  // chunks inside src (>= 1)
     u32x4 v[kSpanPer];
     bool tail = false;  // some chunk of this lane holds the end of src
 #pragma unroll
@@ -1131,7 +1128,7 @@ __global__ __launch_bounds__(kWaveLanes) void gather_span_kernel(const SpanArgs 
     SpanSeg sg[kSegPer];
 #pragma unroll
     for (int j = 0; j < kSegPer; ++j)
-        sg[j] = a.segs[R.seg_first + min(lane + j * kWaveLanes, nseg - 1)];
+        sg[j] = segs[R.seg_first + min(lane + j * kWaveLanes, nseg - 1)];
     if (tail) {
         // a chunk holding the end of src: only its elements inside src
 #pragma unroll
@@ -1142,7 +1139,7 @@ __global__ __launch_bounds__(kWaveLanes) void gather_span_kernel(const SpanArgs 
 #pragma unroll
                 for (int k = 0; k < kSpanChunkElems; ++k) {
                     const int64_t x = gc * kSpanChunkElems + k;
-                    e[k] = x < a.src_elems ? a.src[x] : uint16_t(0);
+                    e[k] = x < src_elems ? src[x] : uint16_t(0);
                 }
                 v[j] = __builtin_bit_cast(u32x4, e);
             }
@@ -1157,12 +1154,70 @@ __global__ __launch_bounds__(kWaveLanes) void gather_span_kernel(const SpanArgs 
         if (c < chunks) s_data[c] = v[j];
     }
     __syncthreads();
+}
 
+// One lane's output chunk: the n (1 <= n) elements at span-local flat
+// indices kl .. kl + min(n, 8) - 1, which meet pieces lo .. hi of the span,
+// written to out (16-byte aligned) from the span's LDS image.
+__device__ __forceinline__ void span_write8(const u32x4* s_data, const SpanSeg* s_seg, int kl,
+                                            int lo, int hi, int n, uint16_t* out) {
     const uint32_t* s32 = reinterpret_cast<const uint32_t*>(s_data);
     const uint16_t* s16 = reinterpret_cast<const uint16_t*>(s_data);
+    if (lo == hi && n >= kSpanChunkElems) {
+        // One piece: the 8 elements are LDS elements p .. p + 7, read as the
+        // dwords holding them (measured faster than whole 16-byte chunks and
+        // a shift).
+        const int p = kl + s_seg[lo].off;
+        const int dw = p >> 1;
+        u32x4 o;
+        if ((p & 1) == 0) {
+            o = u32x4{s32[dw], s32[dw + 1], s32[dw + 2], s32[dw + 3]};
+        } else {
+            const uint32_t d0 = s32[dw], d1 = s32[dw + 1], d2 = s32[dw + 2], d3 = s32[dw + 3],
+                           d4 = s32[dw + 4];
+            o = u32x4{__builtin_amdgcn_alignbyte(d1, d0, 2), __builtin_amdgcn_alignbyte(d2, d1, 2),
+                      __builtin_amdgcn_alignbyte(d3, d2, 2), __builtin_amdgcn_alignbyte(d4, d3, 2)};
+        }
+        stnt(reinterpret_cast<u32x4*>(out), o);
+        return;
+    }
+    // Several pieces, or fewer than 8 elements: each element finds its piece
+    // (binary search, then forward); elements past the n-th read the last
+    // one and are not stored.
+    const int kl_last = kl + min(n, kSpanChunkElems) - 1;
+    int q = lo;
+    for (int h = hi; q < h;) {
+        const int mid = (q + h + 1) >> 1;
+        if (s_seg[mid].k <= kl) q = mid;
+        else h = mid - 1;
+    }
+    uint16_t e[kSpanChunkElems];
+#pragma unroll
+    for (int k = 0; k < kSpanChunkElems; ++k) {
+        const int K = min(kl + k, kl_last);
+        while (q < hi && s_seg[q + 1].k <= K) ++q;
+        e[k] = s16[K + s_seg[q].off];
+    }
+    if (n >= kSpanChunkElems) {
+        stnt(reinterpret_cast<u32x4*>(out), __builtin_bit_cast(u32x4, e));
+    } else {
+#pragma unroll
+        for (int k = 0; k < kSpanChunkElems; ++k)
+            if (k < n) out[k] = e[k];
+    }
+}
+
+__global__ __launch_bounds__(kWaveLanes) void gather_span_kernel(const SpanArgs a) {
+    __shared__ u32x4 s_data[kSpanChunks];
+    __shared__ SpanSeg s_seg[kSpanSegs];
+    const int64_t sp = xcd_run_tile(blockIdx.x);
+    if (sp >= a.nspan) return;  // the grid is rounded up to whole rounds of runs
+    const WaveSpan R = load_span(a.spans + (a.span_first + sp));
+    const int lane = threadIdx.x;
+    const int64_t k_a = int64_t(R.tile0) * kTile;  // the span's first flat index
+    span_land(R, lane, a.src, a.src_elems, a.segs, s_data, s_seg);
+
     const int64_t k_end = a.k_first + a.count;
-    // span-local index of the launch's last element
-    const int64_t kl_last = k_end - 1 - k_a;
     const int ntile = R.ntile;
     static_assert(kSpanTiles == 2, "the tile loop picks tseg[0] or tseg[1]");
     for (int tau = 0; tau < ntile; ++tau) {
@@ -1171,52 +1226,11 @@ __global__ __launch_bounds__(kWaveLanes) void gather_span_kernel(const SpanArgs 
         if (K0 >= k_end) break;
         // the tile's first and last piece (a select: no indexing of registers)
         const int ts = tau == 0 ? R.tseg[0] : R.tseg[1];
-        const int lo = ts & 0xff, hi = ts >> 8;
         const int kl = tau * int(kTile) + lane * kSpanChunkElems;
         const int64_t jo = k_a + kl - a.k_first;  // output index of the lane's first element
-        const bool full = jo >= 0 && jo + kSpanChunkElems <= a.count;
-        if (lo == hi && full) {
-            // One piece: the lane's 8 elements are LDS elements p .. p + 7,
-            // read as the dwords holding them (measured faster than whole
-            // 16-byte chunks and a shift).
-            const int p = kl + s_seg[lo].off;
-            const int dw = p >> 1;
-            u32x4 o;
-            if ((p & 1) == 0) {
-                o = u32x4{s32[dw], s32[dw + 1], s32[dw + 2], s32[dw + 3]};
-            } else {
-                const uint32_t d0 = s32[dw], d1 = s32[dw + 1], d2 = s32[dw + 2],
-                               d3 = s32[dw + 3], d4 = s32[dw + 4];
-                o = u32x4{__builtin_amdgcn_alignbyte(d1, d0, 2), __builtin_amdgcn_alignbyte(d2, d1, 2),
-                          __builtin_amdgcn_alignbyte(d3, d2, 2), __builtin_amdgcn_alignbyte(d4, d3, 2)};
-            }
-            stnt(reinterpret_cast<u32x4*>(a.out + jo), o);
-        } else {
-            // Several pieces, or the launch's end: each element finds its
-            // piece (binary search, then forward); elements past the
-            // launch's end read its last element and are not stored.
-            const int kls = int(min(int64_t(kl), kl_last));
-            int q = lo;
-            for (int h = hi; q < h;) {
-                const int mid = (q + h + 1) >> 1;
-                if (s_seg[mid].k <= kls) q = mid;
-                else h = mid - 1;
-            }
-            uint16_t e[kSpanChunkElems];
-#pragma unroll
-            for (int k = 0; k < kSpanChunkElems; ++k) {
-                const int K = int(min(int64_t(kl + k), kl_last));
-                while (q < hi && s_seg[q + 1].k <= K) ++q;
-                e[k] = s16[K + s_seg[q].off];
-            }
-            if (full) {
-                stnt(reinterpret_cast<u32x4*>(a.out + jo), __builtin_bit_cast(u32x4, e));
-            } else {
-#pragma unroll
-                for (int k = 0; k < kSpanChunkElems; ++k)
-                    if (jo + k >= 0 && jo + k < a.count) a.out[jo + k] = e[k];
-            }
-        }
+        if (jo < 0 || jo >= a.count) continue;  // (k_first is a multiple of kTile: jo >= 0)
+        span_write8(s_data, s_seg, kl, ts & 0xff, ts >> 8, int(min(a.count - jo, int64_t(8))),
+                    a.out + jo);
     }
 }
 

@@ -123,49 +123,50 @@ bool wants_span_table(const HostGatherTable& g) {
     return int64_t(g.delta.size()) * kShortPiece > g.total;
 }
 
-// Span tables. Tiles are added to the current span in order while the
-// span's runs, pieces and LDS chunks stay within the limits; a tile that
-// does not fit starts the next span. A rank's run is the range of its shard
-// from the first to the last element the span reads from it; its LDS image
-// starts at the 16-byte chunk holding the first element.
-void build_span_table(int64_t S, int32_t nd, HostGatherTable& g) {
-    g.spans.clear();
-    g.span_runs.clear();
-    g.span_segs.clear();
-    g.tile_segs.clear();
-    g.wspans.clear();
-    const int64_t total = g.total;
+// Span building. Tiles are added to the current span in order while the
+// span's tiles, runs, pieces and LDS chunks stay within the limits, and
+// while each tile starts where the one before it ended; any other tile
+// starts the next span. A rank's run is the range of its shard from the
+// first to the last element the span reads from it; its LDS image starts at
+// the 16-byte chunk holding the first element.
+bool build_spans(const HostGatherTable& g, int64_t S, int32_t nd, const SpanTileIn* in,
+                 int64_t n_in, int32_t max_tiles, SpanBuild& out) {
+    out = SpanBuild{};
     const int64_t nq = static_cast<int64_t>(g.delta.size());
-    if (total <= 0 || S <= 0 || nd < 1 || nq == 0) return;
-    const int64_t ntile = (total + kTile - 1) / kTile;
+    if (n_in == 0) return true;
+    if (S <= 0 || nd < 1 || nq == 0) return false;
     constexpr int64_t C = kSpanChunkElems;
     auto extent = [](int64_t l, int64_t h) { return (h + C - 1) / C - l / C; };
     auto rank_of = [&](int64_t q) { return (g.k0[size_t(q)] + g.delta[size_t(q)]) / S; };
+    // the piece holding flat index K
+    auto piece_of = [&](int64_t K) {
+        return int64_t(std::upper_bound(g.k0.begin(), g.k0.end() - 1, K) - g.k0.begin()) - 1;
+    };
 
     const size_t n_ranks = static_cast<size_t>(nd);
     std::vector<int64_t> lo(n_ranks), hi(n_ranks), stamp(n_ranks, -1);
     std::vector<int32_t> lds0(n_ranks), ranks;
     std::vector<std::pair<int64_t, int64_t>> segs;  // (piece, first global K in span)
-    int64_t sid = 0, k_a = 0, chunks = 0, last_q = -1;
+    int64_t sid = 0, k_a = 0, chunks = 0, last_q = -1, next_K = -1;
     int32_t tiles = 0;
     struct TileRun {
         int64_t r, lo, hi;
     };
     std::vector<TileRun> trun;
-    std::vector<uint32_t> tile_segs(static_cast<size_t>(ntile));
+    out.tile_segs.resize(static_cast<size_t>(n_in));
 
     auto finish = [&]() -> bool {
         std::sort(ranks.begin(), ranks.end());
-        SpanRec rec{k_a, tiles, int32_t(ranks.size()), int32_t(g.span_runs.size()),
-                    int32_t(g.span_segs.size()), int32_t(segs.size()), int32_t(chunks)};
-        if (g.span_runs.size() + ranks.size() > size_t(INT32_MAX) ||
-            g.span_segs.size() + segs.size() > size_t(INT32_MAX))
+        SpanRec rec{k_a, tiles, int32_t(ranks.size()), int32_t(out.runs.size()),
+                    int32_t(out.segs.size()), int32_t(segs.size()), int32_t(chunks)};
+        if (out.runs.size() + ranks.size() > size_t(INT32_MAX) ||
+            out.segs.size() + segs.size() > size_t(INT32_MAX))
             return false;
         int32_t at = 0;
         for (int32_t r : ranks) {
             const int64_t c0 = lo[size_t(r)] / C;
             const int32_t n = int32_t(extent(lo[size_t(r)], hi[size_t(r)]));
-            g.span_runs.push_back(SpanRun{c0, at, n});
+            out.runs.push_back(SpanRun{c0, at, n});
             lds0[size_t(r)] = at;
             at += n;
         }
@@ -174,9 +175,9 @@ void build_span_table(int64_t S, int32_t nd, HostGatherTable& g) {
             const int64_t r = rank_of(q);
             const int64_t pos = C * lds0[size_t(r)] + (K + g.delta[size_t(q)] - C * (lo[size_t(r)] / C));
             const int64_t k = K - k_a;
-            g.span_segs.push_back(SpanSeg{int32_t(k), int32_t(pos - k)});
+            out.segs.push_back(SpanSeg{int32_t(k), int32_t(pos - k)});
         }
-        g.spans.push_back(rec);
+        out.spans.push_back(rec);
         ranks.clear();
         segs.clear();
         chunks = 0;
@@ -185,19 +186,19 @@ void build_span_table(int64_t S, int32_t nd, HostGatherTable& g) {
         ++sid;
         return true;
     };
-    auto fail = [&]() {
-        g.spans.clear();
-        g.span_runs.clear();
-        g.span_segs.clear();
-        g.tile_segs.clear();
-        g.wspans.clear();
-    };
 
-    for (int64_t t = 0; t < ntile; ++t) {
-        const int64_t t0 = t * kTile, t1 = std::min(t0 + kTile, total);
-        const int64_t q0 = g.tile[size_t(t)];
+    int64_t q_prev_last = -1;
+    for (int64_t t = 0; t < n_in; ++t) {
+        const int64_t t0 = in[t].K0, t1 = in[t].K0 + in[t].n;
+        if (in[t].n <= 0 || t0 < 0 || t1 > g.total) return false;
+        const bool joins = t0 == next_K;
+        // first piece meeting the tile: walk on from the previous tile's
+        // last piece when this tile follows it, else search
+        int64_t q0 = joins ? q_prev_last : piece_of(t0);
+        while (q0 + 1 < nq && g.k0[size_t(q0) + 1] <= t0) ++q0;
         int64_t q1 = q0;  // last piece meeting the tile
         while (q1 + 1 < nq && g.k0[size_t(q1) + 1] < t1) ++q1;
+        q_prev_last = q1;
         // the tile's range of each rank (pieces of one rank merged)
         trun.clear();
         for (int64_t q = q0; q <= q1; ++q) {
@@ -226,8 +227,10 @@ void build_span_table(int64_t S, int32_t nd, HostGatherTable& g) {
                     ++add_runs;
                 }
             }
-            const int64_t add_segs = (q1 - q0 + 1) - (q0 == last_q ? 1 : 0);
-            const bool fits = tiles + 1 <= kSpanTiles && chunks + add_chunks <= kSpanChunks &&
+            const bool cont = tiles > 0 && t0 == next_K;
+            const int64_t add_segs = (q1 - q0 + 1) - (cont && q0 == last_q ? 1 : 0);
+            const bool fits = (tiles == 0 || cont) && tiles + 1 <= max_tiles &&
+                              chunks + add_chunks <= kSpanChunks &&
                               int64_t(segs.size()) + add_segs <= kSpanSegs &&
                               int64_t(ranks.size()) + add_runs <= kSpanRuns;
             if (fits) {
@@ -244,31 +247,53 @@ void build_span_table(int64_t S, int32_t nd, HostGatherTable& g) {
                 }
                 chunks += add_chunks;
                 if (tiles == 0) k_a = t0;
-                const uint32_t first = uint32_t(q0 == last_q ? segs.size() - 1 : segs.size());
+                const bool shares = cont && q0 == last_q;
+                const uint32_t first = uint32_t(shares ? segs.size() - 1 : segs.size());
                 for (int64_t q = q0; q <= q1; ++q) {
-                    if (q == last_q) continue;
+                    if (shares && q == q0) continue;
                     segs.emplace_back(q, std::max(g.k0[size_t(q)], t0));
                 }
                 last_q = q1;
-                tile_segs[size_t(t)] = first | (uint32_t(segs.size() - 1) << 16);
+                next_K = t1;
+                out.tile_segs[size_t(t)] = first | (uint32_t(segs.size() - 1) << 16);
                 ++tiles;
                 break;
             }
-            if (tiles == 0 || pass == 1) {  // the tile alone does not fit
-                fail();
-                return;
-            }
-            if (!finish()) {
-                fail();
-                return;
-            }
+            if (tiles == 0 || pass == 1) return false;  // the tile alone does not fit
+            if (!finish()) return false;
         }
     }
-    if (tiles > 0 && !finish()) {
-        fail();
-        return;
-    }
-    g.tile_segs = std::move(tile_segs);
+    if (tiles > 0 && !finish()) return false;
+    return true;
+}
+
+// Span tables of the range gather: spans of up to kSpanTiles tiles of the
+// global 512-element grid, packed into 64-byte records.
+void build_span_table(int64_t S, int32_t nd, HostGatherTable& g) {
+    g.spans.clear();
+    g.span_runs.clear();
+    g.span_segs.clear();
+    g.tile_segs.clear();
+    g.wspans.clear();
+    const int64_t total = g.total;
+    if (total <= 0 || g.delta.empty()) return;
+    const int64_t ntile = (total + kTile - 1) / kTile;
+    std::vector<SpanTileIn> in(static_cast<size_t>(ntile));
+    for (int64_t t = 0; t < ntile; ++t)
+        in[size_t(t)] = SpanTileIn{t * kTile, std::min(kTile, total - t * kTile)};
+    SpanBuild b;
+    if (!build_spans(g, S, nd, in.data(), ntile, kSpanTiles, b)) return;
+    g.spans = std::move(b.spans);
+    g.span_runs = std::move(b.runs);
+    g.span_segs = std::move(b.segs);
+    g.tile_segs = std::move(b.tile_segs);
+    auto fail = [&]() {
+        g.spans.clear();
+        g.span_runs.clear();
+        g.span_segs.clear();
+        g.tile_segs.clear();
+        g.wspans.clear();
+    };
     // device records: runs and per-tile pieces inline; a layout whose runs
     // lie more than 2^31 chunks apart, or with more than 2^31 tiles, gets none
     g.wspans.assign(g.spans.size(), WaveSpan{});
@@ -289,24 +314,30 @@ void build_span_table(int64_t S, int32_t nd, HostGatherTable& g) {
             const uint32_t ts = g.tile_segs[size_t(R.k_a / kTile + t)];
             w.tseg[t] = uint16_t((ts & 0xffffu) | ((ts >> 16) << 8));
         }
-        const SpanRun* U = &g.span_runs[size_t(R.run_first)];
-        w.chunk0 = U[0].chunk0;
-        for (int32_t q = 0; q < kSpanRuns; ++q) {
-            if (q < R.nrun) {
-                w.lds0[q] = uint8_t(U[q].lds0);
-                if (q > 0) {
-                    const int64_t d = U[q].chunk0 - U[0].chunk0;
-                    if (d > INT32_MAX || d < INT32_MIN) {
-                        fail();
-                        return;
-                    }
-                    w.dchunk[q - 1] = int32_t(d);
-                }
-            } else {
-                w.lds0[q] = 0xffu;  // never reached by a chunk index
-            }
+        if (!pack_runs(g.span_runs.data() + R.run_first, R.nrun, w.chunk0, w.dchunk, w.lds0)) {
+            fail();
+            return;
         }
     }
+}
+
+bool pack_runs(const SpanRun* U, int32_t nrun, int64_t& chunk0, int32_t (&dchunk)[kSpanRuns - 1],
+               uint8_t (&lds0)[kSpanRuns]) {
+    chunk0 = U[0].chunk0;
+    for (int32_t q = 0; q < kSpanRuns; ++q) {
+        if (q < nrun) {
+            lds0[q] = uint8_t(U[q].lds0);
+            if (q > 0) {
+                const int64_t d = U[q].chunk0 - U[0].chunk0;
+                if (d > INT32_MAX || d < INT32_MIN) return false;
+                dchunk[q - 1] = int32_t(d);
+            }
+        } else {
+            lds0[q] = 0xffu;  // never reached by a chunk index
+            if (q > 0) dchunk[q - 1] = 0;
+        }
+    }
+    return true;
 }
 
 }  // namespace zsp
