@@ -1,13 +1,16 @@
 // zsp_kernels.hip -- HIP kernels of libzsp for gfx950 (MI355X, CDNA4).
 //
 // Every kernel here is a stream over HBM with a few fp32 operations per
-// byte: no contraction, so no MFMA and no LDS for data. Design points, each
-// chosen by measurement on MI355X:
+// byte: no contraction, so no MFMA. LDS holds data only in the range
+// gather's span form (many short parameters), which realigns each rank's
+// run of a span through it. Design points, each chosen by measurement on
+// MI355X:
 //
 //  * One wavefront per workgroup, owning one 512-element tile of the index
 //    space, or one half of it (shard launches of up to 16 ranks over long
-//    pieces). Small workgroups keep more, shorter-lived waves in flight,
-//    which measured faster than 256-thread groups for these streams.
+//    pieces), or one span of two tiles (span gather). Small workgroups keep
+//    more, shorter-lived waves in flight, which measured faster than
+//    256-thread groups for these streams.
 //  * Large shard launches cap the workgroups resident per CU (7 to 16,
 //    through the LDS each reserves): fewer waves, each with 4-12 KiB of
 //    loads in flight, let HBM serve the mixed read/write streams faster
