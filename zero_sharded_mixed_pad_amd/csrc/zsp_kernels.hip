@@ -854,6 +854,12 @@ struct GatherShape {
     static constexpr int kLaneStep = kGroup;                            // lane offset
 };
 
+// N elements as one value (to bit-cast a 16-byte group into its elements).
+template <typename T, int N>
+struct ElemArray {
+    T v[N];
+};
+
 // Tiles of the gather holding at most this many pieces read the pieces'
 // starts and deltas with wave-uniform scalar loads and pick per lane with
 // register selects: one scalar round trip, like a single-piece tile.
@@ -1238,7 +1244,8 @@ __global__ __launch_bounds__(kWaveLanes) void gather_span_kernel(const SpanArgs 
 }
 
 // ---- Gather of a list of parameters into separate outputs ------------------
-// Each wave copies one tile of kTile elements of one output. Its record
+// A wave copies one tile of kTile elements of one output (two consecutive
+// tiles in the record form of bf16 short-piece lists). A tile's record
 // (TileRec) says where the tile's elements come from: a tile of a
 // parameter whose slices hold kTile elements or more meets at most two
 // ranks' slices, so two bases and a split describe it; a tile of a smaller
@@ -1273,28 +1280,39 @@ __device__ __forceinline__ int64_t rec_delta(const TileRec& rc, int k, int rem, 
     return rc.base + int64_t(uint32_t(rem + k) / s) * rc.step;
 }
 
-// Copy one tile: 16-byte groups (8 bf16, or two quads of fp32 per lane).
+// One lane's share of a tile, loaded and not yet stored: its 16-byte groups
+// (8 bf16, or two quads of fp32) and how many elements of each to store.
+// Loading and storing apart lets a wave have several tiles' loads in
+// flight before it stores any.
+template <typename T>
+struct RecGroups {
+    u32x4 x[GatherShape<T>::kGroups];
+    int n[GatherShape<T>::kGroups];  // elements to store (kGroup: the whole group)
+    T* out;                          // the lane's first group; group h at + h * kStride
+};
+
 template <typename T, bool SHORT>
-__device__ __forceinline__ void copy_rec_tile(const TileRec& rc, const T* src, int lane) {
+__device__ __forceinline__ RecGroups<T> load_rec_tile(const TileRec& rc, const T* src, int lane) {
     using Sh = GatherShape<T>;
-    T* out = static_cast<T*>(rc.out);
+    RecGroups<T> g;
     const bool many = rc.split < 0;
     const int count = many ? (rc.count & 0xffff) : rc.count;
     const int rem = many ? (rc.count >> 16) : 0;
     const uint32_t s = many ? uint32_t(-rc.split) : 1u;
+    g.out = static_cast<T*>(rc.out) + lane * Sh::kLaneStep;
 #pragma unroll
     for (int h = 0; h < Sh::kGroups; ++h) {
         const int o = h * Sh::kStride + lane * Sh::kLaneStep;
+        g.n[h] = max(0, min(count - o, Sh::kGroup));
+        g.x[h] = u32x4{0, 0, 0, 0};
         if (o >= count) continue;
-        const bool full = o + Sh::kGroup <= count;
         bool one;
         if (!many) one = o + Sh::kGroup <= rc.split || o >= rc.split;
         else one = uint32_t(rem + o) / s == uint32_t(rem + o + Sh::kGroup - 1) / s;
-        if (full && one) {
-            // out + o is 16-byte aligned; the source may sit at any element offset.
+        if (g.n[h] == Sh::kGroup && one) {
+            // the source may sit at any element offset
             const int64_t d = rec_delta(rc, o, rem, s);
-            stnt(reinterpret_cast<u32x4*>(out + o),
-                 ld_src<SHORT>(reinterpret_cast<const u32x4_a2*>(src + d + o)));
+            g.x[h] = ld_src<SHORT>(reinterpret_cast<const u32x4_a2*>(src + d + o));
         } else {
             // Crosses a slice boundary or the output's end: element by
             // element, every load issued (clamped to the last element).
@@ -1304,15 +1322,33 @@ __device__ __forceinline__ void copy_rec_tile(const TileRec& rc, const T* src, i
                 const int k = min(o + i, count - 1);
                 x[i] = src[rec_delta(rc, k, rem, s) + k];
             }
-            if (full) {
-                stnt(reinterpret_cast<u32x4*>(out + o), __builtin_bit_cast(u32x4, x));
-            } else {
-#pragma unroll
-                for (int i = 0; i < Sh::kGroup; ++i)
-                    if (o + i < count) out[o + i] = x[i];
-            }
+            g.x[h] = __builtin_bit_cast(u32x4, x);
         }
     }
+    return g;
+}
+
+template <typename T>
+__device__ __forceinline__ void store_rec_tile(const RecGroups<T>& g) {
+    using Sh = GatherShape<T>;
+#pragma unroll
+    for (int h = 0; h < Sh::kGroups; ++h) {
+        T* out = g.out + h * Sh::kStride;  // 16-byte aligned
+        if (g.n[h] == Sh::kGroup) {
+            stnt(reinterpret_cast<u32x4*>(out), g.x[h]);
+        } else if (g.n[h] > 0) {
+            const auto x = __builtin_bit_cast(ElemArray<T, Sh::kGroup>, g.x[h]);
+#pragma unroll
+            for (int i = 0; i < Sh::kGroup; ++i)
+                if (i < g.n[h]) out[i] = x.v[i];
+        }
+    }
+}
+
+// Copy one tile.
+template <typename T, bool SHORT>
+__device__ __forceinline__ void copy_rec_tile(const TileRec& rc, const T* src, int lane) {
+    store_rec_tile(load_rec_tile<T, SHORT>(rc, src, lane));
 }
 
 // Short-piece lists give each XCD runs of kXcdRun consecutive tiles (see
@@ -1410,19 +1446,35 @@ __global__ __launch_bounds__(kWaveLanes) void list_expand_kernel(const ListExpan
     a.recs[b - a.t_begin] = make_rec(out, a.esz, p.shard_off, p.shard_len, p.numel, a.S, kw);
 }
 
+// Tiles per wave of the record form: two for bf16 short-piece lists (one
+// tile is 1 KB read and 1 KB written per wave, too little in flight while
+// the waves of a many-tile list queue for dispatch), else one.
+constexpr int list_rec_tiles(int esz, bool short_pieces) {
+    return esz == 2 && short_pieces ? 2 : 1;
+}
+
 struct ListRecArgs {
     const TileRec* recs;
     const void* src;
     int64_t tiles;  // tiles of the chunk
 };
 
-// Staged form, second kernel: one record per wave.
+// Staged form, second kernel: list_rec_tiles(sizeof(T), SHORT) consecutive
+// records per wave, every tile's loads issued before any tile's stores
+// (records past the chunk's last are clamped to it and not stored).
 template <typename T, bool SHORT>
 __global__ __launch_bounds__(kWaveLanes) void gather_list_recs(const ListRecArgs a) {
-    const int64_t b = list_tile<SHORT>(blockIdx.x, a.tiles);
+    constexpr int NT = list_rec_tiles(int(sizeof(T)), SHORT);
+    const int64_t b = list_tile<SHORT>(blockIdx.x, (a.tiles + NT - 1) / NT);
     if (b < 0) return;
-    const TileRec rc = a.recs[b];
-    copy_rec_tile<T, SHORT>(rc, static_cast<const T*>(a.src), threadIdx.x);
+    const T* src = static_cast<const T*>(a.src);
+    RecGroups<T> g[NT];
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+        g[j] = load_rec_tile<T, SHORT>(a.recs[min(NT * b + j, a.tiles - 1)], src, threadIdx.x);
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+        if (NT * b + j < a.tiles) store_rec_tile(g[j]);
 }
 
 // Resident waves. With every CU full of shard waves, each touching a dozen
@@ -1644,10 +1696,16 @@ hipError_t launch_gather(const GatherLaunch& L, zsp_dtype dtype, hipStream_t str
 
 namespace {
 
-// Workgroups of a list launch over `tiles` tiles.
-int64_t list_blocks(int64_t tiles, bool short_pieces) {
+// Workgroups of a list launch of `waves` waves.
+int64_t list_blocks(int64_t waves, bool short_pieces) {
     const int64_t runs = 8 * kXcdRun;
-    return short_pieces ? (tiles + runs - 1) / runs * runs : tiles;
+    return short_pieces ? (waves + runs - 1) / runs * runs : waves;
+}
+
+// Waves of the record form over `tiles` tiles.
+int64_t rec_waves(int64_t tiles, int esz, bool short_pieces) {
+    const int64_t nt = list_rec_tiles(esz, short_pieces);
+    return (tiles + nt - 1) / nt;
 }
 
 template <typename T>
@@ -1679,7 +1737,7 @@ hipError_t launch_list_t(const ListLaunch& L, int esz, hipStream_t stream) {
         g.recs = L.recs;
         g.src = L.src;
         g.tiles = L.tiles;
-        const int64_t blocks = list_blocks(L.tiles, L.short_pieces);
+        const int64_t blocks = list_blocks(rec_waves(L.tiles, esz, L.short_pieces), L.short_pieces);
         if (blocks > kMaxBlocks) return hipErrorInvalidValue;
         if (L.short_pieces)
             hipLaunchKernelGGL((gather_list_recs<T, true>), dim3(uint32_t(blocks)), block, 0,
@@ -1710,7 +1768,8 @@ hipError_t launch_list_t(const ListLaunch& L, int esz, hipStream_t stream) {
         g.recs = L.recs;
         g.src = L.src;
         g.tiles = t_end - t;
-        const int64_t blocks = list_blocks(t_end - t, L.short_pieces);
+        const int64_t blocks =
+            list_blocks(rec_waves(t_end - t, esz, L.short_pieces), L.short_pieces);
         if (blocks > kMaxBlocks) return hipErrorInvalidValue;
         if (L.short_pieces)
             hipLaunchKernelGGL((gather_list_recs<T, true>), dim3(uint32_t(blocks)), block, 0,
