@@ -201,6 +201,7 @@ class Runner:
                 out = torch.empty(cnt, dtype=bf16, device=device)
                 self.gather_groups.append((first, n, out, cnt * 4))
         self.step_no = 0
+        self.open_event = None  # the end event of the last timed launch
         self.ev = {k: [] for k in STEP_KINDS + ("gather_cold", "gather_list",
                                                  "gather_list_cold", "gather_many_cold")}
 
@@ -208,18 +209,30 @@ class Runner:
         return self.torch.cuda.Event(enable_timing=True)
 
     def _timed(self, kind, fn, record):
-        if record:
-            a, b = self._event(), self._event()
-            a.record()
+        """Run one launch. With `record`, time it from the event that
+        closed the previous timed launch of the same sequence (or a new event
+        when none is open) to an event recorded after it: consecutive
+        launches share one event, so the markers between them add as little
+        as they can to the step being timed."""
+        if not record:
             fn()
-            b.record()
-            self.ev[kind].append((a, b))
-        else:
-            fn()
+            return
+        if self.open_event is None:
+            self.open_event = self._event()
+            self.open_event.record()
+        fn()
+        b = self._event()
+        b.record()
+        self.ev[kind].append((self.open_event, b))
+        self.open_event = b
 
-    def step(self, record=False):
+    def step(self, record=False, start=None):
+        """One step; with `record`, its launches are timed from `start` (an
+        event already recorded) on, and open_event is left at the end of the
+        last one."""
         w, p = self.w, self.plan
         self.step_no += 1
+        self.open_event = start
         hp = dict(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, step=self.step_no)
         if self.stage == 1:
             self._timed("reduce_set", lambda: p.reduce_shard(
@@ -259,6 +272,7 @@ class Runner:
         for _ in range(reps):
             for first, n, out, _b in self.gather_groups:
                 flush()
+                self.open_event = None
                 self._timed("gather_cold", lambda first=first, n=n, out=out:
                             self.plan.gather_range(first, n, out, "work"), True)
 
@@ -280,9 +294,11 @@ class Runner:
             # marshalled once: the timed calls are the library's alone
             self.gmany = binding._list_arrays(ids, outs, torch.bfloat16)
         kind = "gather_list_cold" if flush else "gather_list"
+        self.open_event = None
         for _ in range(reps):
             if flush:
                 flush()
+                self.open_event = None
             self._timed(kind, lambda: self.plan.gather_prepared(self.glist), True)
         if flush:
             ids_c, outs_c, n = self.gmany
@@ -291,6 +307,7 @@ class Runner:
                 h, ids_c, n, binding.SRC_WORK, outs_c, st))
             for _ in range(reps):
                 flush()
+                self.open_event = None
                 self._timed("gather_many_cold", call, True)
 
     def step_bytes(self):
@@ -865,11 +882,9 @@ def time_workload(w, args, device, evict, say):
         if flush:
             evict()
         a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
         a.record()
-        r.step(record=True)
-        b.record()
-        step_events.append((a, b))
+        r.step(record=True, start=a)
+        step_events.append((a, r.open_event))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     event_ms = sum(a.elapsed_time(b) for a, b in step_events) / args.steps
