@@ -1283,9 +1283,9 @@ __device__ __forceinline__ int64_t rec_delta(const TileRec& rc, int k, int rem, 
 // One lane's share of a tile, loaded and not yet stored: its 16-byte groups
 // (8 bf16, or two quads of fp32) and how many elements of each to store.
 // Loading and storing apart lets a wave have several tiles' loads in
-// flight before it stores any; every field of the record is used before
-// the first branch on it, so the record arrives in one scalar load (read
-// field by field around the branches, it took two round trips).
+// flight before it stores any. The compiler reads this form's record in
+// one scalar load; a copy that stored inside its per-group branch had the
+// record's count read first and the rest after the branch, two round trips.
 template <typename T>
 struct RecGroups {
     u32x4 x[GatherShape<T>::kGroups];
