@@ -227,7 +227,9 @@ extern "C" zsp_status zsp_gather_many(zsp_plan* P, const int32_t* ids, int32_t n
     L.coarse = reinterpret_cast<const int32_t*>(d + z.ents);
     L.recs = reinterpret_cast<TileRec*>(d + up);
     L.rec_cap = z.rec_tiles;
-    if ((e = hipMemcpyAsync(s.dev, s.host, up, hipMemcpyHostToDevice, hs)) != hipSuccess)
+    // the staging goes up through a kernel on the call's stream (up is a
+    // multiple of 256 bytes; both buffers are 256-byte aligned)
+    if ((e = launch_upload(s.dev, s.host, up, hs)) != hipSuccess)
         st = set_hip_error(e, "staging copy");
     else
         st = launch_list(L, src, hs);

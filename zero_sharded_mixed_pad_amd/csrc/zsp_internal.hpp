@@ -298,6 +298,9 @@ struct ListLaunch {
 // Launch a list gather (argument form if n_args > 0, else staged); esz is
 // the element size of src and the outputs (2: bf16, 4: fp32).
 hipError_t launch_gather_list(const ListLaunch& L, int esz, hipStream_t stream);
+// Copies `bytes` (a multiple of 16) from pinned host memory `src` to device
+// memory `dst` with a kernel on `stream`; both 16-byte aligned.
+hipError_t launch_upload(void* dst, const void* src, size_t bytes, hipStream_t stream);
 
 // Launch one E-space operation; dtype is the gradient / parameter dtype.
 hipError_t launch_shard_op(const ShardLaunch& L, ShardOp op, zsp_dtype dtype,

@@ -1787,6 +1787,26 @@ hipError_t launch_list_t(const ListLaunch& L, int esz, hipStream_t stream) {
 
 }  // namespace
 
+// Copy of a one-shot list's staging (entries and coarse index) from pinned
+// host memory to the device: a kernel on the call's stream reads the host
+// bytes once over the bus, where a copy-engine transfer made the next kernel
+// wait on another engine (10,000-tensor list call: 86.7 against 97.5 us).
+__global__ __launch_bounds__(256) void upload_kernel(const u32x4* src, u32x4* dst, int64_t n) {
+    for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n;
+         i += int64_t(gridDim.x) * 256)
+        dst[i] = src[i];
+}
+
+hipError_t launch_upload(void* dst, const void* src, size_t bytes, hipStream_t stream) {
+    if (bytes % 16 != 0) return hipErrorInvalidValue;
+    const int64_t n = int64_t(bytes / 16);
+    if (n == 0) return hipSuccess;
+    const int64_t blocks = std::min<int64_t>((n + 255) / 256, 1024);
+    hipLaunchKernelGGL(upload_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, stream,
+                       static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), n);
+    return hipGetLastError();
+}
+
 hipError_t launch_gather_list(const ListLaunch& L, int esz, hipStream_t stream) {
     if (L.tiles <= 0) return hipSuccess;
     if (esz == 2) return launch_list_t<uint16_t>(L, esz, stream);
