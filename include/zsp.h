@@ -266,8 +266,9 @@ zsp_status zsp_gather_range(zsp_plan* plan, int32_t first_param, int32_t n_param
  * overlap one another or the bound state. n = 0 does nothing.
  *   Lists of at most 64 non-empty parameters: one launch, nothing staged.
  *   Longer lists: their entries (16 bytes per parameter plus 4 bytes per
- *   32768 output elements) are copied to the device through one of four
- *   staging slots the plan keeps, then two launches. A slot is allocated
+ *   32768 output elements) go to the device through one of four staging
+ *   slots the plan keeps (a copy kernel reads them from the slot's pinned
+ *   host buffer), then two launches per chunk of records. A slot is allocated
  *   (pinned host and device memory) the first time a list needs more room
  *   than it has -- the only allocation of any gather call -- and is refilled
  *   only after the gathers of its previous use have run: the call waits on
